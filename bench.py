@@ -1,0 +1,247 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--all-configs]
+
+One step = the whole hot path at the headline workload: bf16 causal attention,
+B=1 H=16 Nq=Nk=16384 D=128, scale 1/sqrt(128): the fused forward (O, LSE) followed by
+the backward (dQ, dK, dV from the saved LSE). Inputs are seeded synthetic N(0,1) values
+rounded to bf16, resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout:
+  value        useful TFLOP/s of the step: (fwd + bwd useful FLOPs) / step time, with
+               useful FLOPs counted on visible (i, j) pairs only: fwd 2 (Dqk + Dv) A,
+               bwd 2 (3 Dqk + 2 Dv) A per (b, h), A = N (N + 1) / 2 for causal
+  roofline     for the kernel that takes the most time per step: its algorithmic FLOPs
+               per launch / its average launch duration (HIP events on the launch stream
+               over the timed region), against the bf16 dense MFMA peak
+  cpu_baseline the CPU fp64 oracle on one head of the same workload (fwd + bwd), scaled
+               to TFLOP/s of useful work
+--all-configs additionally prints per-workload timings of the other configurations to
+stderr (not part of the JSON line).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+
+B, H, N, D = 1, 16, 16384, 128
+
+
+def causal_pairs(n: int) -> int:
+    return n * (n + 1) // 2
+
+
+def useful_flops(b, h, a, dqk, dv):
+    fwd = 2.0 * b * h * (dqk + dv) * a
+    bwd = 2.0 * b * h * (3 * dqk + 2 * dv) * a
+    return fwd, bwd
+
+
+def kernel_flops(b, h, a, dqk, dv):
+    """Algorithmic (useful) FLOPs each kernel of the step contributes."""
+    return {
+        "fwd_bf16": 2.0 * b * h * a * (dqk + dv),             # S = Q K^T, O = P V
+        "bwd_dkdv": 2.0 * b * h * a * (2 * dqk + 2 * dv),     # S, dP, dV, dK
+        "bwd_dq": 2.0 * b * h * a * dqk,                      # dQ (S, dP recomputed, not counted)
+    }
+
+
+def gpu_step_timing(steps: int, warmup: int):
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    from block_sparse_attention_fmha_amd import synth
+
+    dev = torch.device("cuda:0")
+    q, k, v, do = synth.attention_inputs(synth.case_seed(2, 0), B, N, N, H, D, D, "bf16", with_dout=True)
+    tq, tk, tv, tdo = (t.to_torch(dev) for t in (q, k, v, do))
+    del q, k, v, do
+    out = torch.empty_like(tq)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    ws = torch.empty(fa.bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
+    mask = fa.Mask("causal")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fmha_fwd(tq, tk, tv, mask=mask, out=out, lse=lse)
+        fa.fmha_bwd(tq, tk, tv, out, lse, tdo, mask=mask, dq=dq, dk=dk, dv=dv, workspace=ws,
+                    stage_events=None if ev is None else ev[1:5])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = {"fwd_bf16": 0.0, "bwd_preprocess": 0.0, "bwd_dkdv": 0.0, "bwd_dq": 0.0}
+    for e in evs:
+        per["fwd_bf16"] += e[0].elapsed_time(e[1])
+        per["bwd_preprocess"] += e[1].elapsed_time(e[2])
+        per["bwd_dkdv"] += e[2].elapsed_time(e[3])
+        per["bwd_dq"] += e[3].elapsed_time(e[4])
+    per = {k: v / steps for k, v in per.items()}
+    return total_ms / steps, per
+
+
+def cpu_baseline():
+    """The CPU fp64 oracle, as it stands, on one head of the workload (fwd + bwd)."""
+    import numpy as np
+    import oracle
+    from block_sparse_attention_fmha_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    q, k, v, do = synth.attention_inputs(synth.case_seed(2, 0), B, N, N, H, D, D, "bf16", with_dout=True)
+    t0 = time.perf_counter()
+    oracle.backward_bh(q.values[0, :, 0], k.values[0, :, 0], v.values[0, :, 0], do.values[0, :, 0], 0, 0,
+                       scale=1.0 / math.sqrt(D), mask=oracle.MaskSpec("causal"))
+    dt = time.perf_counter() - t0
+    f, b = useful_flops(1, 1, causal_pairs(N), D, D)
+    return {"value": round((f + b) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head 0 of {H} (b=0), full N={N} causal fwd+bwd, {dt:.1f} s wall"}
+
+
+def all_configs_report():
+    """Extra timings of the other workloads, to stderr (median of events)."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    from block_sparse_attention_fmha_amd import synth
+    dev = torch.device("cuda:0")
+
+    def timeit(fn, reps=20, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(); fn(); b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def log(**kw):
+        sys.stderr.write(json.dumps(kw) + "\n")
+        sys.stderr.flush()
+
+    # forward grid: N x D x mask x softcap (B=1 H=16)
+    for n in (1024, 4096, 16384):
+        for d in (64, 128):
+            q, k, v = (torch.randn(1, n, 16, d, device=dev).bfloat16() for _ in range(3))
+            for kind in ("none", "causal", "sliding_window"):
+                for cap in (0.0, 30.0):
+                    m = fa.Mask(kind, window=1024)
+                    ms = timeit(lambda: fa.fmha_fwd(q, k, v, mask=m, softcap=cap))
+                    if kind == "none":
+                        a = n * n
+                    elif kind == "causal":
+                        a = causal_pairs(n)
+                    else:
+                        a = sum(min(i, 1024) + 1 for i in range(n))
+                    f = 2.0 * 16 * 2 * d * a
+                    log(workload="fwd_bf16", N=n, D=d, mask=kind, softcap=cap, ms=round(ms, 4),
+                        tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+    # split-KV decode
+    q = torch.randn(8, 1, 32, 128, device=dev).bfloat16()
+    k = torch.randn(8, 32768, 32, 128, device=dev).bfloat16()
+    v = torch.randn(8, 32768, 32, 128, device=dev).bfloat16()
+    for s in (1, 2, 4, 8, 16):
+        ms = timeit(lambda: fa.fmha_fwd_splitkv(q, k, v, s))
+        byts = 2 * k.numel() * 2
+        log(workload="splitkv", splits=s, ms=round(ms, 4), GBs=round(byts / ms / 1e6, 1),
+            frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+    del k, v
+    # fp32 wide head
+    q, k, v = (torch.randn(4, 512, 8, 1024, device=dev) for _ in range(3))
+    ms = timeit(lambda: fa.fmha_fwd(q, k, v))
+    f = 2.0 * 4 * 8 * 2048 * 512 * 512
+    log(workload="fwd_fp32_d1024", ms=round(ms, 4), tflops=round(f / ms / 1e9, 2),
+        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 4))
+
+
+def main():
+    ap = argparse.ArgumentParser(description="attention hot-path benchmark (one MI355X)")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+                         "(heads or key ranges would be sharded across GPUs; not built). Use --gpus 1.\n")
+        sys.exit(2)
+
+    step_ms, per = gpu_step_timing(args.steps, args.warmup)
+    a = causal_pairs(N)
+    f_fwd, f_bwd = useful_flops(B, H, a, D, D)
+    value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    kf = kernel_flops(B, H, a, D, D)
+    dominant = max((k for k in per if k in kf), key=lambda k: per[k])
+    achieved = kf[dominant] / (per[dominant] * 1e-3) / 1e12
+    kernels = {k: {"ms": round(ms, 4)} for k, ms in per.items()}
+    for k in kf:
+        t = kf[k] / (per[k] * 1e-3) / 1e12
+        kernels[k].update(tflops=round(t, 1), frac=round(t / PEAK_BF16_TFLOPS, 4))
+    fwd_tf = f_fwd / (per["fwd_bf16"] * 1e-3) / 1e12
+    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]
+    bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+    line = {
+        "metric": "fwd/bwd TFLOP/s (useful FLOPs) + % of bf16 MFMA peak, causal N=16K D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal attention fwd+bwd, bf16, B=1 H=16 Nq=Nk=16384 D=128",
+                   "batch": B, "heads": H, "seq_len": N, "head_dim": D, "mask": "causal"},
+        "fwd": {"ms": round(per["fwd_bf16"], 4), "tflops": round(fwd_tf, 1),
+                "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 1),
+                "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    if args.all_configs:
+        all_configs_report()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

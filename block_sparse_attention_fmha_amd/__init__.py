@@ -1,0 +1,350 @@
+"""Python binding of libfmha.so: fused masked attention for AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in ``include/fmha.h``. PyTorch provides device memory and
+the current HIP stream. Each function has the name of the C entry point it calls:
+
+    fmha_fwd(q, k, v, ...)                   -> (out, lse)
+    fmha_bwd(q, k, v, out, lse, dout, ...)   -> (dq, dk, dv)
+    fmha_fwd_splitkv(q, k, v, num_splits...) -> (out, lse)
+    build_block_mask(mask, B, Nq, Nk, ...)   -> BlockSparse
+
+Tensors are ``[batch, seq, head, dim]`` with a contiguous head dim (any batch / seq /
+head strides whose byte size is a multiple of 16). If libfmha.so is missing the calls
+raise: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass, field
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfmha.so")
+
+FMHA_OK, FMHA_ERR_INVALID_ARG, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP, FMHA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+FMHA_BF16, FMHA_FP32 = 0, 1
+MASK_KINDS = {"none": 0, "causal": 1, "sliding_window": 2, "block_diagonal": 3, "prefix_lm": 4}
+ENTRY_POINTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_splitkv",
+                "fmha_fwd_splitkv_workspace_size", "build_block_mask", "fmha_status_string",
+                "fmha_abi_version")
+
+
+class FmhaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+# ------------------------------------------------------------------ C structs (fmha.h)
+
+class CMask(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32), ("prefix", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("doc_q", ctypes.c_void_p), ("doc_k", ctypes.c_void_p)]
+
+
+class CBlockSparse(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("n_q_tiles", ctypes.c_int32), ("n_kv_tiles", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("partial_cnt", ctypes.c_void_p), ("partial_idx", ctypes.c_void_p),
+                ("full_cnt", ctypes.c_void_p), ("full_idx", ctypes.c_void_p),
+                ("t_partial_cnt", ctypes.c_void_p), ("t_partial_idx", ctypes.c_void_p),
+                ("t_full_cnt", ctypes.c_void_p), ("t_full_idx", ctypes.c_void_p)]
+
+
+Strides3 = ctypes.c_int64 * 3
+
+
+class CFwdArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nk", ctypes.c_int32), ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("q_stride", Strides3), ("k_stride", Strides3), ("v_stride", Strides3),
+                ("o_stride", Strides3),
+                ("scale", ctypes.c_float), ("softcap", ctypes.c_float), ("bias_slope", ctypes.c_float),
+                ("reserved2", ctypes.c_int32), ("mask", CMask),
+                ("block_sparse", ctypes.POINTER(CBlockSparse))]
+
+
+class CBwdArgs(ctypes.Structure):
+    _fields_ = [("dout", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p),
+                ("dv", ctypes.c_void_p), ("do_stride", Strides3), ("dq_stride", Strides3),
+                ("dk_stride", Strides3), ("dv_stride", Strides3),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stage_events", ctypes.c_void_p)]
+
+
+# ------------------------------------------------------------------ library loading
+
+_LIB = None
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libfmha.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_attention_fmha_amd.build` (no fallback path exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.fmha_fwd.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.c_void_p]
+    lib.fmha_fwd.restype = ctypes.c_int
+    lib.fmha_bwd.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.POINTER(CBwdArgs), ctypes.c_void_p]
+    lib.fmha_bwd.restype = ctypes.c_int
+    lib.fmha_bwd_workspace_size.argtypes = [ctypes.c_int32] * 3
+    lib.fmha_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fmha_fwd_splitkv.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
+    lib.fmha_fwd_splitkv.restype = ctypes.c_int
+    lib.fmha_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int32] * 5
+    lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.build_block_mask.argtypes = [ctypes.POINTER(CMask)] + [ctypes.c_int32] * 6 + [
+        ctypes.POINTER(CBlockSparse), ctypes.c_void_p]
+    lib.build_block_mask.restype = ctypes.c_int
+    lib.fmha_status_string.argtypes = [ctypes.c_int]
+    lib.fmha_status_string.restype = ctypes.c_char_p
+    lib.fmha_abi_version.argtypes = []
+    lib.fmha_abi_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fmha_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != FMHA_OK:
+        raise FmhaError(status, what)
+
+
+# ------------------------------------------------------------------ argument helpers
+
+@dataclass
+class Mask:
+    """Element mask: kind in MASK_KINDS; window W; prefix P; document ids ([B,Nq], [B,Nk]
+    int32 device tensors) for block_diagonal."""
+    kind: str = "none"
+    window: int = 0
+    prefix: int = 0
+    doc_q: object = field(default=None, repr=False)
+    doc_k: object = field(default=None, repr=False)
+
+    def to_c(self) -> CMask:
+        if self.kind not in MASK_KINDS:
+            raise ValueError(f"unknown mask kind {self.kind!r}")
+        m = CMask()
+        m.kind = MASK_KINDS[self.kind]
+        m.window = int(self.window)
+        m.prefix = int(self.prefix)
+        m.reserved = 0
+        if self.kind == "block_diagonal":
+            dq = self.doc_q
+            dk = self.doc_k if self.doc_k is not None else dq
+            for t in (dq, dk):
+                _need_device(t, "doc ids")
+                if str(t.dtype) != "torch.int32" or not t.is_contiguous():
+                    raise ValueError("doc ids must be contiguous int32 device tensors")
+            m.doc_q, m.doc_k = dq.data_ptr(), dk.data_ptr()
+        return m
+
+
+def _need_device(t, what):
+    if t is None or not getattr(t, "is_cuda", False):
+        raise ValueError(f"{what} must be a device tensor")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FMHA_BF16
+    if t.dtype == torch.float32:
+        return FMHA_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _strides(t) -> Strides3:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [batch, seq, head, dim] tensor with a contiguous head dim")
+    return Strides3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+@dataclass
+class BlockSparse:
+    """Block-sparse tile lists on the device (int32), forward and transposed."""
+    tile_m: int
+    tile_n: int
+    n_q_tiles: int
+    n_kv_tiles: int
+    heads: int
+    partial_cnt: object
+    partial_idx: object
+    full_cnt: object
+    full_idx: object
+    t_partial_cnt: object
+    t_partial_idx: object
+    t_full_cnt: object
+    t_full_idx: object
+
+    def to_c(self) -> CBlockSparse:
+        c = CBlockSparse()
+        c.tile_m, c.tile_n = self.tile_m, self.tile_n
+        c.n_q_tiles, c.n_kv_tiles, c.heads, c.reserved = self.n_q_tiles, self.n_kv_tiles, self.heads, 0
+        for name in ("partial_cnt", "partial_idx", "full_cnt", "full_idx", "t_partial_cnt",
+                     "t_partial_idx", "t_full_cnt", "t_full_idx"):
+            t = getattr(self, name)
+            setattr(c, name, t.data_ptr() if t is not None else None)
+        return c
+
+
+def _fwd_args(q, k, v, out, lse, scale, softcap, bias_slope, mask, block_sparse):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse")):
+        _need_device(t, n)
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    B, Nq, H, Dqk = q.shape
+    Nk, Dv = k.shape[1], v.shape[3]
+    if k.shape != (B, Nk, H, Dqk) or v.shape != (B, Nk, H, Dv) or out.shape != (B, Nq, H, Dv):
+        raise ValueError("inconsistent q / k / v / out shapes")
+    if tuple(lse.shape) != (B, H, Nq) or str(lse.dtype) != "torch.float32" or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    a = CFwdArgs()
+    a.B, a.H, a.Nq, a.Nk, a.Dqk, a.Dv = B, H, Nq, Nk, Dqk, Dv
+    a.dtype = _dtype_code(q)
+    a.reserved = a.reserved2 = 0
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
+    a.q_stride, a.k_stride, a.v_stride, a.o_stride = _strides(q), _strides(k), _strides(v), _strides(out)
+    a.scale = float(1.0 / math.sqrt(Dqk) if scale is None else scale)
+    a.softcap = float(softcap or 0.0)
+    a.bias_slope = float(bias_slope or 0.0)
+    a.mask = (mask or Mask()).to_c()
+    keep = None
+    if block_sparse is not None:
+        keep = block_sparse.to_c()
+        a.block_sparse = ctypes.pointer(keep)
+    return a, keep
+
+
+# ------------------------------------------------------------------ entry points
+
+def fmha_fwd(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | None = None,
+             block_sparse: BlockSparse | None = None, out=None, lse=None, stream=None):
+    """Forward: returns (out [B,Nq,H,Dv], lse [B,H,Nq] fp32)."""
+    import torch
+    B, Nq, H, _ = q.shape
+    Dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, Nq, H, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    a, _keep = _fwd_args(q, k, v, out, lse, scale, softcap, bias_slope, mask, block_sparse)
+    _check(load_library().fmha_fwd(ctypes.byref(a), _stream(stream)), "fmha_fwd")
+    return out, lse
+
+
+def fmha_bwd(q, k, v, out, lse, dout, *, scale=None, softcap=0.0, bias_slope=0.0,
+             mask: Mask | None = None, block_sparse: BlockSparse | None = None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None, stage_events=None):
+    """Backward from the saved LSE: returns (dq, dk, dv), bf16, shaped like q, k, v.
+    ``stage_events``: optional 4 torch.cuda.Event objects recorded around the three
+    backward kernels (preprocess, dK/dV, dQ) for per-kernel timing."""
+    import torch
+    lib = load_library()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    B, Nq, H, _ = q.shape
+    need = lib.fmha_bwd_workspace_size(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    for t, n in ((dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace")):
+        _need_device(t, n)
+    if dout.shape != out.shape or dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shapes must match q / k / v / out")
+    a, _keep = _fwd_args(q, k, v, out, lse, scale, softcap, bias_slope, mask, block_sparse)
+    g = CBwdArgs()
+    g.dout, g.dq, g.dk, g.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    g.do_stride, g.dq_stride, g.dk_stride, g.dv_stride = _strides(dout), _strides(dq), _strides(dk), _strides(dv)
+    g.workspace = workspace.data_ptr()
+    g.workspace_bytes = workspace.numel() * workspace.element_size()
+    ev_arr = None
+    if stage_events is not None:
+        if len(stage_events) != 4:
+            raise ValueError("stage_events needs 4 events")
+        ev_arr = (ctypes.c_void_p * 4)(*[_event_handle(e) for e in stage_events])
+        g.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    _check(lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), _stream(stream)), "fmha_bwd")
+    return dq, dk, dv
+
+
+def _event_handle(ev) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use)."""
+    if getattr(ev, "cuda_event", 0) == 0:
+        import torch
+        ev.record(torch.cuda.current_stream())   # materialise the handle
+    return int(ev.cuda_event)
+
+
+def fmha_fwd_splitkv(q, k, v, num_splits: int, *, scale=None, mask: Mask | None = None,
+                     out=None, lse=None, workspace=None, stream=None):
+    """Split-KV forward (partials + LSE-weighted combine): returns (out, lse)."""
+    import torch
+    lib = load_library()
+    B, Nq, H, _ = q.shape
+    Dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, Nq, H, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = lib.fmha_fwd_splitkv_workspace_size(B, H, Nq, Dv, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need_device(workspace, "workspace")
+    a, _keep = _fwd_args(q, k, v, out, lse, scale, 0.0, 0.0, mask, None)
+    _check(lib.fmha_fwd_splitkv(ctypes.byref(a), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+           "fmha_fwd_splitkv")
+    return out, lse
+
+
+def splitkv_workspace_size(B, H, Nq, Dv, num_splits) -> int:
+    return int(load_library().fmha_fwd_splitkv_workspace_size(B, H, Nq, Dv, num_splits))
+
+
+def bwd_workspace_size(B, H, Nq) -> int:
+    return int(load_library().fmha_bwd_workspace_size(B, H, Nq))
+
+
+def build_block_mask(mask: Mask, B: int, Nq: int, Nk: int, tile_m: int, tile_n: int, *,
+                     heads: int = 1, device="cuda", stream=None) -> BlockSparse:
+    """Classify every (tile_m x tile_n) tile of the element mask on the GPU and return
+    the forward and transposed index lists."""
+    import torch
+    nqt, nkt = -(-Nq // tile_m), -(-Nk // tile_n)
+    i32 = dict(dtype=torch.int32, device=device)
+    bs = BlockSparse(tile_m, tile_n, nqt, nkt, heads,
+                     torch.empty((B, heads, nqt), **i32), torch.empty((B, heads, nqt, nkt), **i32),
+                     torch.empty((B, heads, nqt), **i32), torch.empty((B, heads, nqt, nkt), **i32),
+                     torch.empty((B, heads, nkt), **i32), torch.empty((B, heads, nkt, nqt), **i32),
+                     torch.empty((B, heads, nkt), **i32), torch.empty((B, heads, nkt, nqt), **i32))
+    c = bs.to_c()
+    cm = mask.to_c()
+    _check(load_library().build_block_mask(ctypes.byref(cm), B, heads, Nq, Nk, tile_m, tile_n,
+                                           ctypes.byref(c), _stream(stream)), "build_block_mask")
+    return bs

@@ -1,0 +1,232 @@
+// Device-side helpers and kernel parameter blocks shared by the HIP kernels.
+//
+// Everything here is CDNA4 (gfx950) specific: 64-lane wavefronts, the
+// v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2_f32 matrix instructions and the
+// ds_read_b64_tr_b16 transposed LDS read.
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (lane l, g = l / 32):
+//   A (32 x 16, M x K): lane l holds row l % 32, k = 8 g + i for its 8 elements i
+//   B (16 x 32, K x N): lane l holds column l % 32, k = 8 g + i
+//   C (32 x 32):        lane l holds column l % 32, rows 8 (r / 4) + 4 g + r % 4, r = 0..15
+// v_mfma_f32_32x32x2_f32 is the same with one element per lane (k = g).
+//
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives, as its element e
+// (e = 0..3), element i % 4 of the 8 bytes read by lane 4 e + i / 4 of the group. If lane
+// 4 e + c of the group points at row (r0 + e), columns (c0 + 4 c .. c0 + 4 c + 3) of a
+// row-major bf16 tile, lane i receives column c0 + i of rows r0 .. r0 + 3: a transposed
+// 4 x 16 read that yields MFMA operands with the contraction index along the rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskBlockDiag = 3, kMaskPrefix = 4 };
+
+// ---------------------------------------------------------------------------------------
+// Parameter blocks (passed by value as kernel arguments).
+
+struct MaskParams {
+  int kind, window, prefix;
+  const int* doc_q;  // [B, Nq]
+  const int* doc_k;  // [B, Nk]
+};
+
+struct ListParams {  // block-sparse index lists, forward or transposed orientation
+  const int* pcnt;
+  const int* pidx;
+  const int* fcnt;
+  const int* fidx;
+  int heads, tile_rows, tile_cols, n_rows, n_cols;  // rows = the side the grid walks
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs_b, qs_s, qs_h, ks_b, ks_s, ks_h, vs_b, vs_s, vs_h, os_b, os_s, os_h;
+  int B, H, Nq, Nk;
+  int n_tiles;        // tiles of the resident side (query tiles for the forward)
+  int total_work;     // B * H * n_tiles
+  int grid_padded;    // total_work rounded up to a multiple of 8 (XCD remap)
+  int longest_first;  // walk resident tiles from the one with the most keys
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+  float softcap;      // > 0: tanh softcap
+  float bias_log2;    // relative-bias slope * log2(e)
+  MaskParams mask;
+  ListParams lists;
+};
+
+struct BwdParams {
+  AttnParams a;       // q, k, v, o (forward output), lse (forward LSE)
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;        // workspace: D_i = sum_d dO_id O_id, [B, H, Nq] fp32
+  int64_t dos_b, dos_s, dos_h, dqs_b, dqs_s, dqs_h, dks_b, dks_s, dks_h, dvs_b, dvs_s, dvs_h;
+  ListParams tlists;  // transposed block-sparse lists (per key tile) for the dK/dV pass
+  void* const* stage_events;  // optional host array of 4 hipEvent_t (host side only)
+  int n_kv_tiles;     // key tiles for the dK/dV pass
+  int total_work_kv;
+  int grid_padded_kv;
+};
+
+// ---------------------------------------------------------------------------------------
+// Small device helpers.
+
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each with its
+// own L2. Remapping the linear block id so that every XCD receives a contiguous run of
+// work items keeps the key/value stream of one head inside one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int grid_padded) {
+  const int per = grid_padded >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// value of lane (l ^ 32)
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8-byte transposed LDS read (see the layout note at the top of this file).
+__device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(u32x2 lo, u32x2 hi) {
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Is key j visible from query i under the element mask (delta = Nk - Nq)?
+__device__ __forceinline__ bool mask_visible(const MaskParams& m, int b, int i, int j, int nq,
+                                             int nk) {
+  const int d = nk - nq;
+  switch (m.kind) {
+    case kMaskCausal: return j <= i + d;
+    case kMaskWindow: return j <= i + d && j >= i + d - m.window;
+    case kMaskBlockDiag: return m.doc_q[(int64_t)b * nq + i] == m.doc_k[(int64_t)b * nk + j];
+    case kMaskPrefix: return j < m.prefix || j <= i + d;
+    default: return true;
+  }
+}
+
+// Block-sparse list walking with defensive bounds: counts are clamped to [0, n_cols] and
+// an entry outside [0, n_cols) maps to tile n_cols, which lies past the end of the
+// sequence, so it is loaded as zeros and fully masked instead of being dereferenced.
+__device__ __forceinline__ int clamp_count(int c, int n_cols) { return min(max(c, 0), n_cols); }
+__device__ __forceinline__ int list_entry(const int* idx, int e, int n_cols) {
+  const int t = idx[e];
+  return (t >= 0 && t < n_cols) ? t : n_cols;
+}
+
+// Score transform applied to the scaled score x = scale * <q, k> (softcap, then bias).
+// Returns the final score in log2 units.
+template <bool SOFTCAP, bool BIAS>
+__device__ __forceinline__ float score_log2(float raw, const AttnParams& p, int i, int j) {
+  float x = raw * p.scale;
+  if constexpr (SOFTCAP) {
+    // tanh(y) = 1 - 2 / (exp(2 y) + 1), y = x / softcap
+    const float e = fast_exp2(x * (2.0f * kLog2e / p.softcap));
+    x = p.softcap * (1.0f - 2.0f * fast_rcp(e + 1.0f));
+  }
+  float u = x * kLog2e;
+  if constexpr (BIAS) u += p.bias_log2 * (float)abs(i - j);
+  return u;
+}
+
+
+// MFMA row permutation: swapping bits 2 and 3 of the A-operand row index makes the C
+// registers 8 r' + i (i = 0..7) of lane half g hold rows 16 r' + 8 g + i, i.e. 8
+// consecutive rows per lane, which is exactly the K-slot order of the next MFMA's
+// B operand.
+__device__ __forceinline__ int swap_bits23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Row-major bf16 tile in LDS with an XOR swizzle of its 16-byte chunks, so that both
+// access patterns used on the same tile are bank-conflict free without padding:
+//   * 16-byte reads of one chunk column from 16 consecutive rows (MFMA rows), and
+//   * transposed 8-byte reads of 4 consecutive rows x 32 bytes (ds_read_b64_tr_b16).
+// Chunk c of row r is stored at chunk (c & ~(S-1)) | ((c ^ f(r)) & (S-1)), S = 16 when the
+// row has a multiple of 16 chunks (else 8), f(r) = 2 (r mod S/2) + (r / (S/2)) mod 2.
+template <int D>
+struct SwizzledTile {
+  static constexpr int CH = D / 8;
+  static constexpr int S = (CH % 16 == 0) ? 16 : 8;
+  static constexpr int ROW_BYTES = D * 2;
+  __device__ static __forceinline__ int f(int r) {
+    return ((r & (S / 2 - 1)) << 1) | ((r / (S / 2)) & 1);
+  }
+  // byte offset of element `col` (a multiple of 4) of row r
+  __device__ static __forceinline__ int off(int r, int col) {
+    const int c = col >> 3;
+    const int pc = (c & ~(S - 1)) | ((c ^ f(r)) & (S - 1));
+    return r * ROW_BYTES + pc * 16 + (col & 7) * 2;
+  }
+};
+
+// DPP controls (gfx9 encoding) and a sum over groups of 8 or 16 consecutive lanes that
+// stays inside one 16-lane DPP row (no LDS traffic).
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPK == 8 || LPK == 16, "group of 8 or 16 lanes");
+  x += dpp_mov<kDppXor1>(x);
+  x += dpp_mov<kDppXor2>(x);
+  x += dpp_mov<kDppRowHalfMirror>(x);
+  if constexpr (LPK == 16) x += dpp_mov<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4& x, float* f) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(x[e] << 16);
+    f[2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+  }
+}
+
+}  // namespace fmha

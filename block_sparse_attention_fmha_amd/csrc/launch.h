@@ -1,0 +1,37 @@
+// Host-side launchers of the HIP kernels (internal to libfmha.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernel_common.h"
+
+namespace fmha {
+
+// bf16 forward: (Dqk, Dv) in {(64,64), (128,128), (192,128)}. Fills the tiling fields
+// of `p` (n_tiles, total_work, grid_padded) itself.
+hipError_t launch_fwd_bf16(AttnParams p, int dqk, int dv, hipStream_t st);
+int fwd_bf16_block_rows();   // query rows per workgroup (block-sparse tile_m must be a multiple)
+int fwd_bf16_tile_keys();    // keys per tile (block-sparse tile_n must be a multiple)
+
+// fp32 forward, D-split across wavefronts: D in {64, 128, 1024}, Dqk == Dv, analytic masks.
+hipError_t launch_fwd_f32(AttnParams p, int d, hipStream_t st);
+
+// bf16 split-KV forward (partials + combine). `ws` holds the partials.
+size_t splitkv_workspace_bytes(int B, int H, int Nq, int Dv, int splits);
+int splitkv_tile_keys();
+hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, void* ws, hipStream_t st);
+
+// bf16 backward: preprocess, dK/dV pass, dQ pass.
+hipError_t launch_bwd_bf16(BwdParams p, int dqk, int dv, hipStream_t st);
+int bwd_q_block_rows();      // query rows per dQ workgroup / per dK/dV inner step
+int bwd_kv_block_rows();     // key rows per dK/dV workgroup / per dQ inner step
+
+// Block-mask builder: forward lists (per query tile) and transposed lists (per key tile).
+struct BlockMaskOut {
+  int *pcnt, *pidx, *fcnt, *fidx, *tpcnt, *tpidx, *tfcnt, *tfidx;
+};
+hipError_t launch_build_block_mask(const MaskParams& m, int B, int Hm, int Nq, int Nk,
+                                   int tile_m, int tile_n, const BlockMaskOut& out,
+                                   hipStream_t st);
+
+}  // namespace fmha

@@ -26,11 +26,15 @@ def case_seed(config: int, case: int = 0) -> int:
     return BASE_SEED + 1000 * config + case
 
 
-def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to bf16 (round to nearest, ties to even); return the uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+def bf16_bits(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); return the uint16 bits.
+    Works in chunks so that very large tensors need little temporary memory."""
+    flat = np.ascontiguousarray(x, dtype=np.float32).reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for lo in range(0, flat.size, chunk):
+        u = flat[lo:lo + chunk].astype(np.uint64)
+        out[lo:lo + chunk] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return out.reshape(np.shape(x))
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

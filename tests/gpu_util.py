@@ -1,0 +1,97 @@
+"""Shared helpers of the GPU parity tests (not a test module).
+
+The tolerances are the ones the workload specification states:
+  fp32 O / LSE:   max |x - ref| <= 1e-4
+  bf16 O / LSE:   |x - ref| <= 2e-2 + 2e-2 |ref| element-wise (-inf LSE matched exactly)
+  bf16 gradients: ||g - ref||_2 / ||ref||_2 <= 1e-2 per tensor
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from block_sparse_attention_fmha_amd import synth
+
+FP32_ATOL = 1e-4
+BF16_ATOL = 2e-2
+BF16_RTOL = 2e-2
+GRAD_RTOL = 1e-2
+
+
+def announce(msg: str):
+    """Name the case on the real stderr (bypassing capture) before any GPU step, so a
+    run that dies on the GPU still says which case it was running."""
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def device():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible")
+    return torch.device("cuda:0")
+
+
+def to_dev(t: synth.Tensor):
+    return t.to_torch(device())
+
+
+def host(x) -> np.ndarray:
+    import torch
+    if x.dtype == torch.bfloat16:
+        return x.float().cpu().numpy().astype(np.float64)
+    return x.detach().cpu().numpy().astype(np.float64)
+
+
+def check_bf16(name, got, ref, mask=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    ninf_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), ninf_ref), f"{name}: -inf pattern differs"
+    fin = ~ninf_ref
+    err = np.abs(got[fin] - ref[fin])
+    bound = BF16_ATOL + BF16_RTOL * np.abs(ref[fin])
+    assert np.all(np.isfinite(got[fin])), f"{name}: non-finite values"
+    bad = err > bound
+    assert not bad.any(), f"{name}: {bad.sum()} of {bad.size} outside tolerance, worst excess {np.max(err - bound):.3e}"
+
+
+def check_fp32(name, got, ref, mask=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    ninf_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), ninf_ref), f"{name}: -inf pattern differs"
+    fin = ~ninf_ref
+    assert np.all(np.isfinite(got[fin])), f"{name}: non-finite values"
+    err = np.max(np.abs(got[fin] - ref[fin]), initial=0.0)
+    assert err <= FP32_ATOL, f"{name}: max abs error {err:.3e} > {FP32_ATOL}"
+
+
+def check_grad(name, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    rel = num / den if den > 0 else num
+    assert rel <= GRAD_RTOL, f"{name}: norm-relative error {rel:.3e} > {GRAD_RTOL}"
+
+
+def mask_pair(kind, B, Nq, Nk, window=0, prefix=0, doc_seed=None):
+    """(oracle MaskSpec, binding Mask) for the same element mask."""
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    if kind == "block_diagonal":
+        dq = synth.document_ids(doc_seed, B, Nq)
+        dk = dq if Nk == Nq else synth.document_ids(doc_seed + 1, B, Nk)
+        om = oracle.MaskSpec(kind, doc_q=dq, doc_k=dk)
+        gm = fa.Mask(kind, doc_q=torch.from_numpy(dq).to(device()), doc_k=torch.from_numpy(dk).to(device()))
+        return om, gm
+    return oracle.MaskSpec(kind, window=window, prefix=prefix), fa.Mask(kind, window=window, prefix=prefix)

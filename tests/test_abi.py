@@ -1,0 +1,196 @@
+"""The C ABI without a GPU: libfmha.so loads, exports every function include/fmha.h
+declares, the ctypes mirror matches the header's struct layout, and host-side argument
+validation rejects bad requests before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_fmha_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmha.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        from block_sparse_attention_fmha_amd import build
+        build.build()
+    return fa.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == sorted(fa.ENTRY_POINTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.fmha_abi_version() == 1
+    assert fa.status_string(0) == "FMHA_OK"
+    assert fa.status_string(-4) == "FMHA_ERR_WORKSPACE"
+    assert fa.status_string(12345) == "FMHA_ERR_UNKNOWN"
+
+
+def test_struct_layout_matches_header():
+    # offsets the header implies for LP64 (int32 fields, 8-byte pointers / int64)
+    assert ctypes.sizeof(fa.CMask) == 32
+    assert ctypes.sizeof(fa.CBlockSparse) == 24 + 8 * 8
+    assert fa.CFwdArgs.q.offset == 32 and fa.CFwdArgs.q_stride.offset == 72
+    assert fa.CFwdArgs.scale.offset == 168 and fa.CFwdArgs.mask.offset == 184
+    assert fa.CFwdArgs.block_sparse.offset == 216 and ctypes.sizeof(fa.CFwdArgs) == 224
+    assert ctypes.sizeof(fa.CBwdArgs) == 32 + 96 + 24
+
+
+def _args(**kw):
+    a = fa.CFwdArgs()
+    a.B, a.H, a.Nq, a.Nk, a.Dqk, a.Dv, a.dtype = 1, 2, 64, 64, 128, 128, fa.FMHA_BF16
+    fake = 0x100000  # never dereferenced: validation fails first
+    a.q = a.k = a.v = a.o = a.lse = fake
+    for s in (a.q_stride, a.k_stride, a.v_stride, a.o_stride):
+        s[0], s[1], s[2] = 64 * 2 * 128, 2 * 128, 128
+    a.scale = 0.125
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"Dqk": 96, "Dv": 96}, fa.FMHA_ERR_UNSUPPORTED),
+    ({"Dqk": 128, "Dv": 64}, fa.FMHA_ERR_UNSUPPORTED),
+    ({"lse": None}, fa.FMHA_ERR_INVALID_ARG),
+    ({"q": 0x100008}, fa.FMHA_ERR_INVALID_ARG),          # not 16-byte aligned
+    ({"scale": 0.0}, fa.FMHA_ERR_INVALID_ARG),
+    ({"scale": float("nan")}, fa.FMHA_ERR_INVALID_ARG),
+    ({"softcap": -1.0}, fa.FMHA_ERR_INVALID_ARG),
+    ({"dtype": 7}, fa.FMHA_ERR_INVALID_ARG),
+    ({"reserved": 1}, fa.FMHA_ERR_INVALID_ARG),
+    ({"Nq": -1}, fa.FMHA_ERR_INVALID_ARG),
+    ({"dtype": fa.FMHA_FP32, "Dqk": 1024, "Dv": 1024, "softcap": 30.0}, fa.FMHA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    a = _args(**kw)
+    assert lib.fmha_fwd(ctypes.byref(a), None) == status
+
+
+def test_fwd_rejects_misaligned_stride_and_bad_mask(lib):
+    a = _args()
+    a.k_stride[1] = 129  # 258-byte rows
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_INVALID_ARG
+    a = _args()
+    a.mask.kind = 9
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_INVALID_ARG
+    a = _args()
+    a.mask.kind = fa.MASK_KINDS["block_diagonal"]   # doc ids missing
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_INVALID_ARG
+    a = _args()
+    a.mask.kind, a.mask.window = fa.MASK_KINDS["sliding_window"], -3
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_INVALID_ARG
+
+
+def test_null_and_empty_requests(lib):
+    assert lib.fmha_fwd(None, None) == fa.FMHA_ERR_INVALID_ARG
+    a = _args(Nq=0)
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_OK      # nothing to compute, no launch
+    a = _args(B=0)
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_OK
+
+
+def test_block_sparse_tile_constraints(lib):
+    bs = fa.CBlockSparse()
+    bs.tile_m, bs.tile_n, bs.n_q_tiles, bs.n_kv_tiles, bs.heads = 64, 64, 1, 1, 1
+    for name in ("partial_cnt", "partial_idx", "full_cnt", "full_idx"):
+        setattr(bs, name, 0x100000)
+    a = _args()
+    a.block_sparse = ctypes.pointer(bs)
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_UNSUPPORTED   # tile_m not a multiple of 128
+    bs.tile_m, bs.n_q_tiles = 128, 1
+    bs.n_kv_tiles = 5                                                       # inconsistent with Nk / tile_n
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_INVALID_ARG
+
+
+def test_bwd_and_splitkv_workspace_checks(lib):
+    a = _args()
+    g = fa.CBwdArgs()
+    g.dout = g.dq = g.dk = g.dv = 0x100000
+    for s in (g.do_stride, g.dq_stride, g.dk_stride, g.dv_stride):
+        s[0], s[1], s[2] = 64 * 2 * 128, 2 * 128, 128
+    need = lib.fmha_bwd_workspace_size(1, 2, 64)
+    assert need >= 1 * 2 * 64 * 4 and need % 256 == 0
+    g.workspace, g.workspace_bytes = 0x200000, need - 1
+    assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_WORKSPACE
+    assert lib.fmha_bwd(ctypes.byref(a), None, None) == fa.FMHA_ERR_INVALID_ARG
+    need = lib.fmha_fwd_splitkv_workspace_size(1, 2, 64, 128, 4)
+    assert need >= 1 * 2 * 4 * 64 * (128 + 1) * 4
+    assert lib.fmha_fwd_splitkv(ctypes.byref(a), 4, ctypes.c_void_p(0x200000), need - 1, None) == fa.FMHA_ERR_WORKSPACE
+    assert lib.fmha_fwd_splitkv(ctypes.byref(a), 0, ctypes.c_void_p(0x200000), need, None) == fa.FMHA_ERR_INVALID_ARG
+    assert lib.fmha_fwd_splitkv(ctypes.byref(a), 65, ctypes.c_void_p(0x200000), need, None) == fa.FMHA_ERR_INVALID_ARG
+
+
+def test_build_block_mask_argument_checks(lib):
+    m = fa.CMask()
+    out = fa.CBlockSparse()
+    assert lib.build_block_mask(ctypes.byref(m), 1, 1, 128, 128, 64, 64, ctypes.byref(out), None) == fa.FMHA_ERR_INVALID_ARG
+    assert lib.build_block_mask(None, 1, 1, 128, 128, 64, 64, ctypes.byref(out), None) == fa.FMHA_ERR_INVALID_ARG
+    for name in ("partial_cnt", "partial_idx", "full_cnt", "full_idx", "t_partial_cnt", "t_partial_idx",
+                 "t_full_cnt", "t_full_idx"):
+        setattr(out, name, 0x100000)
+    assert lib.build_block_mask(ctypes.byref(m), 1, 1, 128, 128, 0, 64, ctypes.byref(out), None) == fa.FMHA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fa, "_LIB", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.load_library()
+
+
+def test_ctypes_layout_matches_c_compiler(tmp_path):
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fmha.h"\n'
+                   "#define P(s, f) printf(#s \".\" #f \" %zu\\n\", offsetof(s, f))\n"
+                   "int main(void) {\n"
+                   "  P(fmha_fwd_args, q); P(fmha_fwd_args, lse); P(fmha_fwd_args, q_stride);"
+                   "  P(fmha_fwd_args, o_stride); P(fmha_fwd_args, scale); P(fmha_fwd_args, mask);"
+                   "  P(fmha_fwd_args, block_sparse); P(fmha_bwd_args, workspace);"
+                   "  P(fmha_bwd_args, workspace_bytes); P(fmha_block_sparse, partial_cnt);"
+                   "  P(fmha_block_sparse, t_full_idx); P(fmha_mask, doc_k);\n"
+                   '  printf("sizeof.fwd %zu\\nsizeof.bwd %zu\\nsizeof.bs %zu\\nsizeof.mask %zu\\n",'
+                   " sizeof(fmha_fwd_args), sizeof(fmha_bwd_args), sizeof(fmha_block_sparse), sizeof(fmha_mask));\n"
+                   "  return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    want = {
+        "fmha_fwd_args.q": fa.CFwdArgs.q.offset, "fmha_fwd_args.lse": fa.CFwdArgs.lse.offset,
+        "fmha_fwd_args.q_stride": fa.CFwdArgs.q_stride.offset,
+        "fmha_fwd_args.o_stride": fa.CFwdArgs.o_stride.offset,
+        "fmha_fwd_args.scale": fa.CFwdArgs.scale.offset, "fmha_fwd_args.mask": fa.CFwdArgs.mask.offset,
+        "fmha_fwd_args.block_sparse": fa.CFwdArgs.block_sparse.offset,
+        "fmha_bwd_args.workspace": fa.CBwdArgs.workspace.offset,
+        "fmha_bwd_args.workspace_bytes": fa.CBwdArgs.workspace_bytes.offset,
+        "fmha_block_sparse.partial_cnt": fa.CBlockSparse.partial_cnt.offset,
+        "fmha_block_sparse.t_full_idx": fa.CBlockSparse.t_full_idx.offset,
+        "fmha_mask.doc_k": fa.CMask.doc_k.offset,
+        "sizeof.fwd": ctypes.sizeof(fa.CFwdArgs), "sizeof.bwd": ctypes.sizeof(fa.CBwdArgs),
+        "sizeof.bs": ctypes.sizeof(fa.CBlockSparse), "sizeof.mask": ctypes.sizeof(fa.CMask),
+    }
+    assert {k: int(v) for k, v in got.items()} == want

@@ -1,0 +1,146 @@
+"""GPU parity of the forward (bf16 and fp32) against the fp64 oracle.
+
+Small cases compare every output element; the full-size workloads compare sampled
+heads / rows that the oracle computes one by one (the oracle is exact per row, so a
+sampled row is as strict as a full comparison of that row)."""
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_attention_fmha_amd import synth
+from tests.gpu_util import (announce, check_bf16, check_fp32, device, host, mask_pair, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, gmask=None, **kw):
+    import block_sparse_attention_fmha_amd as fa
+    out, lse = fa.fmha_fwd(q, k, v, mask=gmask, **kw)
+    import torch
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _case(seed, B, Nq, Nk, H, Dqk, Dv, dtype, kind="none", window=0, prefix=0, softcap=0.0,
+          slope=0.0, rows=None, heads=None):
+    q, k, v = synth.attention_inputs(seed, B, Nq, Nk, H, Dqk, Dv, dtype)
+    om, gm = mask_pair(kind, B, Nq, Nk, window, prefix, doc_seed=seed)
+    announce(f"fwd {dtype} seed={seed} B={B} Nq={Nq} Nk={Nk} H={H} D={Dqk}/{Dv} mask={kind} "
+             f"W={window} P={prefix} softcap={softcap} bias={slope}")
+    out, lse = run_fwd(to_dev(q), to_dev(k), to_dev(v), gm, softcap=softcap, bias_slope=slope)
+    o_ref, l_ref = oracle.forward(q.values, k.values, v.values, softcap=softcap, bias_slope=slope,
+                                  mask=om, rows=rows, heads=heads)
+    o, l = host(out), host(lse)
+    rsel = slice(None) if rows is None else np.asarray(rows)
+    hsel = slice(None) if heads is None else np.asarray(heads)
+    if dtype == "fp32":
+        check_fp32("O", o[:, rsel][:, :, hsel], o_ref[:, rsel][:, :, hsel])
+        check_fp32("LSE", l[:, hsel][:, :, rsel], l_ref[:, hsel][:, :, rsel])
+    else:
+        check_bf16("O", o[:, rsel][:, :, hsel], o_ref[:, rsel][:, :, hsel])
+        check_bf16("LSE", l[:, hsel][:, :, rsel], l_ref[:, hsel][:, :, rsel])
+
+
+# ------------------------------------------------------------------ small, every element
+
+SMALL = [
+    # (B, Nq, Nk, H, Dqk, Dv, kind, window, prefix, softcap, slope)
+    (2, 256, 256, 3, 128, 128, "none", 0, 0, 0.0, 0.0),
+    (2, 256, 256, 3, 128, 128, "causal", 0, 0, 0.0, 0.0),
+    (1, 300, 300, 2, 128, 128, "causal", 0, 0, 0.0, 0.0),
+    (1, 129, 257, 2, 128, 128, "causal", 0, 0, 0.0, 0.0),
+    (1, 257, 129, 2, 128, 128, "causal", 0, 0, 0.0, 0.0),      # rows with no visible key
+    (1, 513, 769, 2, 128, 128, "sliding_window", 171, 0, 0.0, 0.0),
+    (1, 640, 640, 2, 64, 64, "sliding_window", 100, 0, 30.0, 0.0),
+    (2, 384, 384, 2, 64, 64, "prefix_lm", 0, 100, 0.0, -0.01),
+    (2, 512, 512, 2, 128, 128, "block_diagonal", 0, 0, 0.0, -0.01),
+    (1, 255, 385, 2, 192, 128, "causal", 0, 0, 0.0, 0.0),      # MLA-shaped heads
+    (1, 200, 200, 2, 128, 128, "none", 0, 0, 5.0, -0.05),
+    (1, 1, 1000, 4, 128, 128, "causal", 0, 0, 0.0, 0.0),       # single decode query
+    (1, 1000, 1, 2, 64, 64, "none", 0, 0, 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_fwd_bf16_small(case):
+    B, Nq, Nk, H, Dqk, Dv, kind, W, P, cap, slope = SMALL[case]
+    _case(synth.case_seed(9, case), B, Nq, Nk, H, Dqk, Dv, "bf16", kind, W, P, cap, slope)
+
+
+def test_fwd_bf16_empty_keys_and_queries():
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    dev = device()
+    q = torch.randn(1, 70, 2, 128, device=dev).bfloat16()
+    k = torch.empty(1, 0, 2, 128, device=dev, dtype=torch.bfloat16)
+    announce("fwd bf16 Nk=0")
+    out, lse = run_fwd(q, k, k)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    announce("fwd bf16 Nq=0")
+    q0 = torch.empty(1, 0, 2, 128, device=dev, dtype=torch.bfloat16)
+    kk = torch.randn(1, 5, 2, 128, device=dev).bfloat16()
+    out, lse = run_fwd(q0, kk, kk)
+    assert out.shape == (1, 0, 2, 128)
+
+
+def test_fwd_bf16_strided_bhsd_layout():
+    # BHSD storage passed as BSHD views: only the strides differ
+    q, k, v = synth.attention_inputs(synth.case_seed(9, 50), 2, 200, 200, 3, 128, 128, "bf16")
+    qt, kt, vt = (to_dev(x).permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for x in (q, k, v))
+    assert qt.stride(2) == 200 * 128
+    announce("fwd bf16 strided BHSD B=2 N=200 H=3")
+    out, lse = run_fwd(qt, kt, vt, mask_pair("causal", 2, 200, 200)[1])
+    o_ref, l_ref = oracle.forward(q.values, k.values, v.values, mask=oracle.MaskSpec("causal"))
+    check_bf16("O", host(out), o_ref)
+    check_bf16("LSE", host(lse), l_ref)
+
+
+FP32_SMALL = [
+    (1, 128, 128, 1, 64, "causal"),      # the fp32 parity workload
+    (2, 150, 170, 2, 64, "none"),
+    (1, 200, 200, 2, 128, "sliding_window"),
+    (1, 100, 130, 2, 1024, "causal"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP32_SMALL)))
+def test_fwd_fp32_small(case):
+    B, Nq, Nk, H, D, kind = FP32_SMALL[case]
+    seed = synth.case_seed(1, 0) if case == 0 else synth.case_seed(9, 100 + case)
+    _case(seed, B, Nq, Nk, H, D, D, "fp32", kind, window=50)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _rows_sample(n, seed):
+    rng = np.random.default_rng(seed)
+    pick = np.concatenate([np.arange(min(n, 64)), np.arange(max(0, n - 64), n),
+                           rng.choice(n, size=min(n, 256), replace=False)])
+    return np.unique(pick)
+
+
+CONFIG2 = [(n, d, kind, cap) for n in (1024, 4096, 16384) for d in (64, 128)
+           for kind in ("none", "causal", "sliding_window") for cap in (0.0, 30.0)]
+
+
+@pytest.mark.parametrize("case", range(len(CONFIG2)))
+def test_fwd_bf16_full_size(case):
+    N, D, kind, cap = CONFIG2[case]
+    seed = synth.case_seed(2, case)
+    heads = None if N <= 1024 else [case % 16]
+    rows = _rows_sample(N, seed) if N >= 16384 else None
+    _case(seed, 1, N, N, 16, D, D, "bf16", kind, window=1024, softcap=cap, rows=rows, heads=heads)
+
+
+def test_fwd_fp32_wide_head_full_size():
+    # B=4 H=8 N=512 D=1024, no mask; two (b, h) pairs compared in full
+    seed = synth.case_seed(5, 1)
+    q, k, v = synth.attention_inputs(seed, 4, 512, 512, 8, 1024, 1024, "fp32")
+    announce(f"fwd fp32 wide head seed={seed} B=4 N=512 H=8 D=1024")
+    out, lse = run_fwd(to_dev(q), to_dev(k), to_dev(v))
+    o, l = host(out), host(lse)
+    for b, h in ((0, 0), (3, 5)):
+        o_ref, l_ref = oracle.forward_bh(q.values[b, :, h], k.values[b, :, h], v.values[b, :, h],
+                                         np.arange(512), b, h, 512, 512, scale=1 / 32.0)
+        check_fp32(f"O[{b},{h}]", o[b, :, h], o_ref)
+        check_fp32(f"LSE[{b},{h}]", l[b, h], l_ref)
