@@ -190,11 +190,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3: run --steps hot-path steps, then one plain 512 MiB device copy "
+                         "(counter calibration), and exit without the JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
                          "(heads or key ranges would be sharded across GPUs; not built). Use --gpus 1.\n")
         sys.exit(2)
+
+    if args.profile:
+        import torch
+        step_ms, per = gpu_step_timing(args.steps, args.warmup)
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)      # reads 512 MiB, writes 512 MiB
+        torch.cuda.synchronize()
+        sys.stderr.write(f"profile run: {args.steps} steps, {step_ms:.3f} ms/step; copy 512 MiB done\n")
+        return
 
     step_ms, per = gpu_step_timing(args.steps, args.warmup)
     a = causal_pairs(N)
