@@ -5,7 +5,8 @@
 Every source under csrc/ is compiled by hipcc for gfx950 only, objects go to
 csrc/_build/, and the shared library lands next to this file. Packed-fp32 VALU
 instructions are disabled for device code (-packed-fp32-ops), matching the rule that
-this library never relies on them.
+this library never relies on them. -fno-honor-nans: no kernel relies on NaN semantics
+(infinities are still honoured: masked scores are -inf).
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ ARCH = "gfx950"
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-honor-nans",   # no kernel relies on NaN semantics; lets fmaxf map to v_max3 directly
     "-Wall", "-Wno-unused-result", "-Wno-unused-command-line-argument",
 ]
 

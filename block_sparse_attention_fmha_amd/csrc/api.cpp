@@ -118,7 +118,7 @@ int validate_fwd(const fmha_fwd_args* a) {
   return FMHA_OK;
 }
 
-int validate_lists(const fmha_block_sparse* bs, int B, int H, int Nq, int Nk, bool need_transposed) {
+int validate_lists(const fmha_block_sparse* bs, int B, int H, int Nq, int Nk, int dqk, int dv, bool need_transposed) {
   if (bs->reserved != 0) return FMHA_ERR_INVALID_ARG;
   if (bs->tile_m <= 0 || bs->tile_n <= 0) return FMHA_ERR_INVALID_ARG;
   if (bs->n_q_tiles != ceil_div(Nq, bs->tile_m) || bs->n_kv_tiles != ceil_div(Nk, bs->tile_n))
@@ -126,7 +126,9 @@ int validate_lists(const fmha_block_sparse* bs, int B, int H, int Nq, int Nk, bo
   if (bs->heads != 1 && bs->heads != H) return FMHA_ERR_INVALID_ARG;
   if (!bs->partial_cnt || !bs->partial_idx || !bs->full_cnt || !bs->full_idx) return FMHA_ERR_INVALID_ARG;
   // sparse tiles must be whole multiples of the kernel tiles
-  if (bs->tile_m % fmha::fwd_bf16_block_rows() != 0 || bs->tile_n % fmha::fwd_bf16_tile_keys() != 0)
+  if (bs->tile_m % fmha::fwd_bf16_list_rows() != 0 || bs->tile_n % fmha::fwd_bf16_tile_keys() != 0)
+    return FMHA_ERR_UNSUPPORTED;
+  if (!need_transposed && !fmha::fwd_bf16_lists_fit(dqk, dv, bs->n_kv_tiles, bs->tile_n))
     return FMHA_ERR_UNSUPPORTED;
   if (need_transposed) {
     if (!bs->t_partial_cnt || !bs->t_partial_idx || !bs->t_full_cnt || !bs->t_full_idx)
@@ -227,7 +229,7 @@ int fmha_fwd(const fmha_fwd_args* a, void* stream) {
   if ((int64_t)a->B * a->H * a->Nq == 0) return FMHA_OK;
   if (a->block_sparse) {
     if (a->dtype != FMHA_BF16) return FMHA_ERR_UNSUPPORTED;
-    rc = validate_lists(a->block_sparse, a->B, a->H, a->Nq, a->Nk, false);
+    rc = validate_lists(a->block_sparse, a->B, a->H, a->Nq, a->Nk, a->Dqk, a->Dv, false);
     if (rc != FMHA_OK) return rc;
   }
   rc = check_device();
@@ -265,7 +267,7 @@ int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
   const size_t need = fmha_bwd_workspace_size(a->B, a->H, a->Nq);
   if (g->workspace == nullptr || g->workspace_bytes < need) return FMHA_ERR_WORKSPACE;
   if (a->block_sparse) {
-    rc = validate_lists(a->block_sparse, a->B, a->H, a->Nq, a->Nk, true);
+    rc = validate_lists(a->block_sparse, a->B, a->H, a->Nq, a->Nk, a->Dqk, a->Dv, true);
     if (rc != FMHA_OK) return rc;
   }
   rc = check_device();

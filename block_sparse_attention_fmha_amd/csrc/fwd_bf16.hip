@@ -9,7 +9,7 @@
 // mask only on partial tiles).
 //
 // Mapping onto CDNA4 (our own design, not the pages' CUDA tiling):
-//   * workgroup = 4 wavefronts, 128 query rows (32 per wave); key tiles of 64 rows.
+//   * workgroup = 8 wavefronts (2 per SIMD), 256 query rows (32 per wave), 64-key tiles.
 //   * each wave computes S^T = K Q^T for its 32 queries with v_mfma_f32_32x32x16_bf16:
 //     K rows come from LDS as the A operand, Q stays in VGPRs as the B operand for the
 //     whole pass. In the S^T accumulator every lane owns ONE query row and 16 keys per
@@ -20,9 +20,18 @@
 //     16-key step; those registers, rounded to bf16, are directly the B operand of
 //     O^T += V^T P^T, and the matching V^T operand is read from the row-major V tile
 //     with two ds_read_b64_tr_b16 transposed reads (no transpose pass over V).
-//   * K and V tiles are double-buffered in LDS; the next tile's global loads are issued
-//     before the current tile's MFMAs and written to the other buffer afterwards, so
-//     one barrier per tile suffices.
+//   * ping-pong: the two waves sharing a SIMD (wave w and w + 4) alternate between a
+//     matrix phase (S(j+1) = K(j+1) Q^T and O += V(j) P(j): 32 MFMAs) and a vector phase
+//     (mask, online softmax, P(j+1) in bf16), one phase apart, separated by workgroup
+//     barriers. While one wave feeds the matrix core the other runs its softmax, so the
+//     VALU work hides behind the MFMA work instead of serialising with it.
+//   * K and V tiles live in 3 LDS stages filled by direct global->LDS loads
+//     (global_load_lds_dwordx4, no VGPR staging) issued two phases before first use;
+//     padded row pitches keep the 16-byte K row reads and the transposed V reads free
+//     of bank conflicts.
+//   * the O rescale by exp(m_old - m_new) is skipped for a tile when no row of the wave
+//     raised its running max (a wave-uniform branch), which after the first few tiles
+//     is the common case; the row sum adds exactly the bf16 P fed to the MFMA.
 //   * the work item order is XCD-aware (each XCD gets a contiguous run of heads) and,
 //     for causal-like masks, longest-first over query tiles.
 #include "kernel_common.h"
@@ -31,52 +40,172 @@
 namespace fmha {
 namespace {
 
-constexpr int kBM = 128;   // query rows per workgroup
+constexpr int kBM = 256;   // query rows per workgroup
 constexpr int kBN = 64;    // keys per tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+// LDS stages of (K, V) tiles: tile t is loaded 2 * stages - 4 phases before first use.
+template <int DQK> struct Stages { static constexpr int value = (DQK <= 128) ? 4 : 3; };
 
-// LDS pitches (bytes). K rows are read 16 bytes per lane from 32 different rows: a
-// dword pitch of 4 * odd (mod 64 banks) puts 16 consecutive rows on disjoint banks.
-// V is read with the transposed 8-byte read (4 rows x 32 bytes per 16-lane group): a
-// dword pitch of 16 or 48 (mod 64) puts those 4 row segments on disjoint banks.
-template <int D> struct KPitch { static constexpr int value = D * 2 + 16; };
-template <int D> struct VPitch { static constexpr int value = (D == 64) ? 192 : (D == 128 ? 320 : D * 2 + 64); };
+// LDS row pitches in 16-byte chunks. K rows are read 16 bytes per lane from 16
+// different rows at once: a pitch of 4 * odd dwords (mod 64 banks) puts them on disjoint
+// banks. V is read with the transposed 8-byte read (4 rows x 32 bytes per 16-lane group):
+// a pitch of 16 or 48 dwords (mod 64) puts those 4 row segments on disjoint banks. Every
+// LDS address is then one base register plus immediates.
+template <int D> struct KPitchChunks { static constexpr int value = D / 8 + 1; };
+template <int D> struct VPitchChunks { static constexpr int value = (D == 64) ? 12 : 20; };
 
 template <int DQK, int DV>
 struct FwdSmem {
-  static constexpr int KP = KPitch<DQK>::value;
-  static constexpr int VP = VPitch<DV>::value;
+  static constexpr int KPC = KPitchChunks<DQK>::value;
+  static constexpr int VPC = VPitchChunks<DV>::value;
+  static constexpr int KP = KPC * 16;          // bytes
+  static constexpr int VP = VPC * 16;
   static constexpr int KB = kBN * KP;
   static constexpr int VB = kBN * VP;
   static constexpr int STAGE = KB + VB;
-  static constexpr int BYTES = 2 * STAGE;
+  static constexpr int NST = Stages<DQK>::value;
+  static constexpr int BYTES = NST * STAGE;
 };
 
-// Key-tile sequence of one workgroup: analytic band or block-sparse lists.
+// Key-tile sequence of one workgroup: the analytic band, or (block-sparse) entries in LDS
+// of the form (kernel tile << 4) | class bits, the class of query half hf (rows
+// 128 hf .. 128 hf + 127 of the workgroup) in bits 2 hf, 2 hf + 1: 1 = partial tile (element
+// mask applies), 2 = full tile, 0 = tile not listed for that half (all keys hidden).
 struct TileSeq {
   int count;
-  int t_lo;          // analytic: first tile
-  int sub;           // lists: kernel tiles per sparse column tile
-  int npart;
-  int n_cols;
-  const int* pidx;
-  const int* fidx;
-  __device__ __forceinline__ void at(int it, bool lists, int& n0, bool& partial) const {
-    if (!lists) {
-      n0 = (t_lo + it) * kBN;
-      partial = false;
-      return;
-    }
-    const int e = it / sub, s = it - e * sub;
-    int kt;
-    if (e < npart) { kt = list_entry(pidx, e, n_cols); partial = true; }
-    else { kt = list_entry(fidx, e - npart, n_cols); partial = false; }
-    n0 = kt * sub * kBN + s * kBN;
+  int t_lo;                 // analytic: first tile
+  const uint32_t* ent;      // lists: LDS entries
+  __device__ __forceinline__ int n0(int it, bool lists) const {
+    return lists ? (int)(ent[it] >> 4) * kBN : (t_lo + it) * kBN;
   }
 };
 
+// Merge the block-sparse rows that cover the workgroup's two 128-row halves into one
+// ascending key-tile sequence (sparse tile_m is a multiple of 128, so each half lies in
+// one sparse row). A column listed by both halves is visited once; a column listed as both
+// partial and full for one row counts as full. List entries outside [0, n_cols) and kernel
+// tiles that start at or past Nk are dropped. `cls` needs ceil(n_cols / 4) words and `ent`
+// n_cols * (tile_cols / 64) words of LDS. Returns the sequence length (same in every thread).
+template <int NTHREADS>
+__device__ int build_tile_sequence(const ListParams& L, int b, int h, int q0, int nq, int nk,
+                                   uint32_t* cls, uint32_t* ent, int* total, int tid) {
+  const int ncw = (L.n_cols + 3) >> 2;
+  for (int i = tid; i < ncw; i += NTHREADS) cls[i] = 0u;
+  __syncthreads();
+  const int hm = (L.heads == 1) ? 0 : h;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int qr = q0 + 128 * hf;
+    if (qr >= nq) break;
+    const int64_t row = ((int64_t)b * L.heads + hm) * L.n_rows + qr / L.tile_rows;
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {   // 0: partial list, 1: full list
+      const int cnt = clamp_count((kind ? L.fcnt : L.pcnt)[row], L.n_cols);
+      const int* idx = (kind ? L.fidx : L.pidx) + row * L.n_cols;
+      const uint32_t code = (kind ? 2u : 1u) << (2 * hf);
+      for (int e = tid; e < cnt; e += NTHREADS) {
+        const int c = idx[e];
+        if (c >= 0 && c < L.n_cols) atomicOr(&cls[c >> 2], code << (8 * (c & 3)));
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int sub = L.tile_cols / kBN;
+    const int nkt = (nk + kBN - 1) / kBN;   // kernel tiles holding at least one key
+    int base = 0;
+    for (int c0 = 0; c0 < L.n_cols; c0 += 64) {
+      const int c = c0 + tid;
+      uint32_t v = c < L.n_cols ? (cls[c >> 2] >> (8 * (c & 3))) & 15u : 0u;
+      v = v & ~((v & 10u) >> 1);   // partial and full for the same half: full
+      const uint64_t m = __builtin_amdgcn_ballot_w64(v != 0u);
+      const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (v != 0u) {
+        // the tiles of one column are consecutive slots, so the sequence stays ascending
+        for (int s = 0; s < sub; ++s) {
+          const int kt = c * sub + s;
+          if (kt < nkt) ent[(base + pre) * sub + s] = ((uint32_t)kt << 4) | v;
+        }
+      }
+      base += __builtin_popcountll(m);
+    }
+    if (tid == 0) {
+      // only the last column can hold tiles at or past Nk
+      const int cl = L.n_cols - 1;
+      const bool last_listed = cl >= 0 && ((cls[cl >> 2] >> (8 * (cl & 3))) & 15u) != 0u;
+      *total = base * sub - (last_listed ? L.n_cols * sub - nkt : 0);
+    }
+  }
+  __syncthreads();
+  return *total;
+}
+
+// Max of the 32 S^T entries of a lane as a depth-4 tree of v_max3.
+__device__ __forceinline__ float tree_max32(const f32x16 (&s)[2]) {
+  float a[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int x = 3 * i, y = 3 * i + 1, z = 3 * i + 2;
+    a[i] = fmaxf(fmaxf(s[x >> 4][x & 15], s[y >> 4][y & 15]), s[z >> 4][z & 15]);
+  }
+  a[10] = fmaxf(s[1][14], s[1][15]);
+  const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
+  return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+}
+
+// Visible keys of query row i under the band masks (none, causal, sliding window,
+// prefix-LM) form one interval [lo, hi); block-diagonal is handled separately.
+__device__ __forceinline__ void band_interval(const MaskParams& m, int i, int nq, int nk, int& lo, int& hi) {
+  const int d = nk - nq;
+  lo = 0;
+  hi = nk;
+  if (m.kind == kMaskCausal || m.kind == kMaskWindow) hi = min(nk, i + d + 1);
+  if (m.kind == kMaskWindow) lo = i + d - m.window;
+  if (m.kind == kMaskPrefix) hi = min(nk, max(m.prefix, i + d + 1));
+}
+
+// Set to -inf the S^T entries whose key is hidden from the lane's query row. Register r
+// of block kb holds key kbase + 32 kb + 16 (r / 8) + r % 8 (kbase = tile start + 8 g).
+// `elem` = apply the element mask (else only keys past Nk are hidden); `hide` = hide all.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const MaskParams& m, int b, int qrow, int kbase,
+                                          int nq, int nk, bool elem, bool hide) {
+  if (hide) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = kNegInf;
+    return;
+  }
+  if (elem && m.kind == kMaskBlockDiag) {
+    const int dq = m.doc_q[(int64_t)b * nq + qrow];
+    const int* dk = m.doc_k + (int64_t)b * nk;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kbase + 32 * kb + 16 * (r >> 3) + (r & 7);
+        const bool vis = j < nk && dk[min(j, nk - 1)] == dq;
+        s[kb][r] = vis ? s[kb][r] : kNegInf;
+      }
+    return;
+  }
+  int lo = 0, hi = nk;
+  if (elem) band_interval(m, qrow, nq, nk, lo, hi);
+  // key j visible iff lo <= j < hi, i.e. (unsigned)(j - lo) < (unsigned)(hi - lo)
+  const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
+  const int base = kbase - lo;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const unsigned rel = (unsigned)(base + 32 * kb + 16 * (r >> 3) + (r & 7));
+      s[kb][r] = rel < span ? s[kb][r] : kNegInf;
+    }
+}
+
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
-__global__ __launch_bounds__(kThreads, (DQK <= 128 ? 2 : 1))
+__global__ __launch_bounds__(kThreads, 1)
 void fwd_bf16_kernel(const AttnParams p) {
   using SM = FwdSmem<DQK, DV>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -99,7 +228,8 @@ void fwd_bf16_kernel(const AttnParams p) {
 
   // ---- tile sequence
   TileSeq seq;
-  seq.t_lo = 0; seq.sub = 1; seq.npart = 0; seq.n_cols = 0; seq.pidx = nullptr; seq.fidx = nullptr;
+  seq.t_lo = 0;
+  seq.ent = (const uint32_t*)(smem + SM::BYTES + 16);
   const int mk = p.mask.kind;
   if constexpr (!LISTS) {
     int lo = 0, hi = Nk;
@@ -111,16 +241,9 @@ void fwd_bf16_kernel(const AttnParams p) {
     seq.t_lo = tlo;
     seq.count = max(0, thi - tlo);
   } else {
-    const int qs = q0 / p.lists.tile_rows;
-    const int hm = (p.lists.heads == 1) ? 0 : h;
-    const int row = (b * p.lists.heads + hm) * p.lists.n_rows + qs;
-    seq.n_cols = p.lists.n_cols;
-    seq.npart = clamp_count(p.lists.pcnt[row], p.lists.n_cols);
-    const int nfull = clamp_count(p.lists.fcnt[row], p.lists.n_cols);
-    seq.pidx = p.lists.pidx + (int64_t)row * p.lists.n_cols;
-    seq.fidx = p.lists.fidx + (int64_t)row * p.lists.n_cols;
-    seq.sub = p.lists.tile_cols / kBN;
-    seq.count = (seq.npart + nfull) * seq.sub;
+    uint32_t* ent = (uint32_t*)(smem + SM::BYTES + 16);
+    uint32_t* cls = ent + p.lists.n_cols * (p.lists.tile_cols / kBN);
+    seq.count = build_tile_sequence<kThreads>(p.lists, b, h, q0, Nq, Nk, cls, ent, (int*)(smem + SM::BYTES), tid);
   }
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the whole pass
@@ -132,43 +255,6 @@ void fwd_bf16_kernel(const AttnParams p) {
     else qf[ks] = bf16x8{};
   }
 
-  // ---- global -> register staging of one K/V tile
-  constexpr int KCH = kBN * DQK / 8 / kThreads;  // 16-byte chunks per thread
-  constexpr int VCH = kBN * DV / 8 / kThreads;
-  u32x4 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DQK / 8), col = c - row * (DQK / 8);
-      const int key = n0 + row;
-      kreg[i] = (key < Nk) ? *(const u32x4*)(Kg + (int64_t)key * p.ks_s + col * 8) : u32x4{};
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DV / 8), col = c - row * (DV / 8);
-      const int key = n0 + row;
-      vreg[i] = (key < Nk) ? *(const u32x4*)(Vg + (int64_t)key * p.vs_s + col * 8) : u32x4{};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* Kl = smem + buf * SM::STAGE;
-    char* Vl = Kl + SM::KB;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DQK / 8), col = c - row * (DQK / 8);
-      *(u32x4*)(Kl + row * SM::KP + col * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DV / 8), col = c - row * (DV / 8);
-      *(u32x4*)(Vl + row * SM::VP + col * 16) = vreg[i];
-    }
-  };
-
   // ---- running state
   f32x16 o[DV / 32];
 #pragma unroll
@@ -177,135 +263,154 @@ void fwd_bf16_kernel(const AttnParams p) {
   const float c_eff = (SOFTCAP || BIAS) ? 1.0f : p.scale_log2;
   const int prow = swap_bits23(lq);
   const int qw = q0 + 32 * w;
+  const int trow = 8 * g + ((l & 15) >> 2);
+  const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const int grp = w >> 2;   // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
 
-  if (seq.count > 0) {
-    int n0;
-    bool part;
-    seq.at(0, LISTS, n0, part);
-    load_tile(n0);
-    store_tile(0);
-    __syncthreads();
-  }
+  LdsDma<kBN, DQK, SM::KPC, kThreads> kdma;
+  LdsDma<kBN, DV, SM::VPC, kThreads> vdma;
+  kdma.init(p.ks_s, tid);
+  vdma.init(p.vs_s, tid);
+  zero_lds<kThreads>(smem, SM::BYTES, tid);   // rows past Nk are never loaded: keep them finite
+  auto issue_tile = [&](int t) {
+    const int n0 = seq.n0(t, LISTS);
+    char* st = smem + (t % SM::NST) * SM::STAGE;
+    kdma.issue(Kg, p.ks_s, n0, Nk, st);
+    vdma.issue(Vg, p.vs_s, n0, Nk, st + SM::KB);
+  };
 
-  for (int it = 0; it < seq.count; ++it) {
-    const int buf = it & 1;
-    int n0;
-    bool partial;
-    seq.at(it, LISTS, n0, partial);
-    if (it + 1 < seq.count) {
-      int n1;
-      bool p1;
-      seq.at(it + 1, LISTS, n1, p1);
-      load_tile(n1);
-    }
-    const char* Kl = smem + buf * SM::STAGE;
-    const char* Vl = Kl + SM::KB;
+  f32x16 s[2];
+  bf16x8 pb[2][2];
+  const int T = seq.count;
+  // only the tile holding key Nk - 1 can be ragged, and it is always the last of the sequence
+  const bool last_ragged = T > 0 && seq.n0(T - 1, LISTS) + kBN > Nk;
+  for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_tile(t);
+  wait_all_vmem();   // Q fragments and the first tiles
+  __syncthreads();
 
-    // S^T for the wave's 32 queries x 64 keys (two 32-key blocks)
-    f32x16 s[2];
+  // Phase ph = 0 .. 2T+1. Local phase lp = ph - grp (waves 4-7 run one phase behind).
+  //   lp even: matrix phase  -> S(lp/2) = K Q^T (if < T), O += V(lp/2 - 1) P (if >= 0)
+  //   lp odd:  vector phase  -> softmax of S((lp-1)/2) into P (if < T)
+  // Tile t's stage is busy during phases 2t .. 2t+3. Tile t is issued at phase
+  // 2 (t - NST + 2) (the first NST - 2 tiles before the loop), i.e. 2 NST - 4 phases
+  // before its first use, once the stage's previous tile (t - NST) is done; the wave
+  // then waits for it at the end of phase 2t - 1.
+  for (int ph = 0; ph < 2 * T + 2; ++ph) {
+    if ((ph & 1) == 0 && ph / 2 + SM::NST - 2 < T) issue_tile(ph / 2 + SM::NST - 2);
+    const int lp = ph - grp;
+    if (lp >= 0 && (lp & 1) == 0) {
+      // ------------------------------------------------------------- matrix phase
+      const int ts = lp >> 1;          // tile whose S is computed
+      const int tv = ts - 1;           // tile whose P V is accumulated
+      if (tv >= 0) {
+        const char* Vl = smem + (tv % SM::NST) * SM::STAGE + SM::KB;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const char* krow = Kl + (32 * kb + prow) * SM::KP + 16 * g;
+        for (int db = 0; db < DV / 32; ++db) {
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(krow + 32 * ks);
-        s[kb] = mfma_bf16(a, qf[ks], s[kb]);
-      }
-    }
-
-    // does this (wave, tile) need the element mask?
-    bool need = (n0 + kBN > Nk);
-    if constexpr (LISTS) {
-      need = need || partial;
-    } else {
-      const int last = n0 + kBN - 1;
-      if (mk == kMaskCausal) need = need || (last > qw + delta);
-      else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
-      else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
-      else if (mk == kMaskBlockDiag) need = true;
-    }
-
-    // score transform (softcap / bias) and mask; reg r of block kb holds key
-    // n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of query row qrow.
-    if constexpr (SOFTCAP || BIAS) {
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[kb][r] = score_log2<SOFTCAP, BIAS>(s[kb][r], p, qrow, n0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7));
-    }
-    if (need) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
-          bool vis = key < Nk;
-          if (vis && qrow < Nq && (LISTS ? partial : true)) vis = mask_visible(p.mask, b, qrow, key, Nq, Nk);
-          if (!vis) s[kb][r] = kNegInf;
-        }
-    }
-
-    // online softmax (log2 domain)
-    float mt = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, swap_halves(mt));
-    const float m_new = fmaxf(m_run, mt * c_eff);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float lsum = 0.0f;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
-          lsum += p0 + p1;
-          pk[e] = pack_bf16x2(p0, p1);
-        }
-        pb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
-      }
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-    // O^T += V^T P^T; V^T operand through transposed LDS reads
-    {
-      const int trow = 8 * g + ((l & 15) >> 2);
-      const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const char* base = Vl + (32 * kb + 16 * hh + trow) * SM::VP + (32 * db + tcol) * 2;
-            const u32x2 lo = lds_read_tr(base);
-            const u32x2 hi = lds_read_tr(base + 4 * SM::VP);
-            o[db] = mfma_bf16(join_bf16x8(lo, hi), pb[kb][hh], o[db]);
+            for (int hh = 0; hh < 2; ++hh) {
+              const char* vp = Vl + (32 * kb + 16 * hh + trow) * SM::VP + (32 * db + tcol) * 2;
+              const u32x2 lo = lds_read_tr(vp);
+              const u32x2 hi = lds_read_tr(vp + 4 * SM::VP);
+              o[db] = mfma_bf16(join_bf16x8(lo, hi), pb[kb][hh], o[db]);
+            }
           }
         }
       }
-    }
+      if (ts < T) {
+        // two independent accumulation chains (key blocks) interleaved
+        const char* Kl = smem + (ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < DQK / 16; ++ks) {
+          const bf16x8 a0 = *(const bf16x8*)(Kl + 32 * ks);
+          const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * SM::KP + 32 * ks);
+          s[0] = mfma_bf16(a0, qf[ks], s[0]);
+          s[1] = mfma_bf16(a1, qf[ks], s[1]);
+        }
+      }
+    } else if (lp >= 0 && (lp >> 1) < T) {
+      // ------------------------------------------------------------- vector phase
+      const int ts = lp >> 1;
+      const int n0 = seq.n0(ts, LISTS);
+      bool need = (n0 + kBN > Nk);
+      bool elem = true, hide = false;
+      if constexpr (LISTS) {
+        const uint32_t c = (seq.ent[ts] >> (2 * grp)) & 3u;   // this wave's query half
+        hide = c == 0u;
+        elem = c == 1u;
+        need = need || c != 2u;
+      } else {
+        const int last = n0 + kBN - 1;
+        if (mk == kMaskCausal) need = need || (last > qw + delta);
+        else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
+        else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
+        else if (mk == kMaskBlockDiag) need = true;
+      }
+      // score transform (softcap / bias) and mask; reg r of block kb holds key
+      // n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of query row qrow.
+      if constexpr (SOFTCAP || BIAS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[kb][r] = score_log2<SOFTCAP, BIAS>(s[kb][r], p, qrow, n0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7));
+      }
+      if (need) mask_tile(s, p.mask, b, qrow, n0 + 8 * g, Nq, Nk, elem && qrow < Nq, hide);
 
-    if (it + 1 < seq.count) store_tile(buf ^ 1);
+      // online softmax (log2 domain). The O / l rescale is skipped when no row of the
+      // wave raised its running max. O already holds every P V up to tile ts - 1.
+      // row max as a shallow tree (short dependency chains: this phase has one wave per
+      // SIMD, so latency, not issue rate, bounds it)
+      float mt = tree_max32(s);
+      mt = pair_max(mt) * c_eff;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.0f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+      // four independent partial row sums of exactly the bf16 P fed to the MFMA
+      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
+            pk[e] = pack_bf16x2(p0, p1);
+            ls[e] = add_bf16_pair(pk[e], ls[e]);
+          }
+          pb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
+        }
+      }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    }
+    if (ph & 1) {
+      // tile (ph + 1) / 2 is read from the next phase on; the NST - 3 tiles issued after
+      // it may stay in flight (loads complete in order), provided each issued its full
+      // instruction count: not so for a ragged last tile, where a wave can skip whole
+      // instructions, so that case waits for everything.
+      const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
+      const bool exact = later > 0 && !(last_ragged && (ph + 1) / 2 + later == T - 1);
+      if (exact) kdma.wait_leaving(vdma, later);
+      else wait_lds_dma();
+    }
     __syncthreads();
   }
 
   // ---- epilogue
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   const bool empty = !(l_tot > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (qrow < Nq) {
@@ -325,13 +430,22 @@ void fwd_bf16_kernel(const AttnParams p) {
   }
 }
 
+// LDS bytes beyond the K/V stages for the block-sparse tile sequence (0 without lists).
+int list_bytes(const ListParams& L) {
+  if (L.pcnt == nullptr) return 0;
+  return 16 + 4 * (L.n_cols * (L.tile_cols / kBN) + (L.n_cols + 3) / 4);
+}
+
+template <int DQK, int DV>
+int smem_bytes(const ListParams& L) { return FwdSmem<DQK, DV>::BYTES + list_bytes(L); }
+
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 hipError_t launch_one(const AttnParams& p, hipStream_t st) {
-  using SM = FwdSmem<DQK, DV>;
   auto kern = fwd_bf16_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::BYTES);
+  const int bytes = smem_bytes<DQK, DV>(p.lists);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(p.grid_padded), dim3(kThreads), SM::BYTES, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.grid_padded), dim3(kThreads), bytes, st, p);
   return hipGetLastError();
 }
 
@@ -348,7 +462,22 @@ hipError_t dispatch_mods(const AttnParams& p, bool lists, bool softcap, bool bia
 }  // namespace
 
 int fwd_bf16_block_rows() { return kBM; }
+int fwd_bf16_list_rows() { return kBM / 2; }
 int fwd_bf16_tile_keys() { return kBN; }
+
+bool fwd_bf16_lists_fit(int dqk, int dv, int n_cols, int tile_cols) {
+  ListParams L{};
+  L.pcnt = (const int*)1;   // only the sizes are read
+  L.n_cols = n_cols;
+  L.tile_cols = tile_cols;
+  if ((int64_t)n_cols * (tile_cols / kBN) > (1 << 20)) return false;
+  int bytes = 0;
+  if (dqk == 128 && dv == 128) bytes = smem_bytes<128, 128>(L);
+  else if (dqk == 64 && dv == 64) bytes = smem_bytes<64, 64>(L);
+  else if (dqk == 192 && dv == 128) bytes = smem_bytes<192, 128>(L);
+  else return false;
+  return bytes <= kMaxLdsBytes;
+}
 
 hipError_t launch_fwd_bf16(AttnParams p, int dqk, int dv, hipStream_t st) {
   p.n_tiles = (p.Nq + kBM - 1) / kBM;

@@ -45,6 +45,8 @@ struct MaskParams {
   const int* doc_k;  // [B, Nk]
 };
 
+constexpr int kMaxLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+
 struct ListParams {  // block-sparse index lists, forward or transposed orientation
   const int* pcnt;
   const int* pidx;
@@ -191,13 +193,125 @@ struct SwizzledTile {
   __device__ static __forceinline__ int f(int r) {
     return ((r & (S / 2 - 1)) << 1) | ((r / (S / 2)) & 1);
   }
+  // physical chunk of logical chunk c in row r (an involution for fixed r)
+  __device__ static __forceinline__ int chunk(int r, int c) {
+    return (c & ~(S - 1)) | ((c ^ f(r)) & (S - 1));
+  }
   // byte offset of element `col` (a multiple of 4) of row r
   __device__ static __forceinline__ int off(int r, int col) {
-    const int c = col >> 3;
-    const int pc = (c & ~(S - 1)) | ((c ^ f(r)) & (S - 1));
-    return r * ROW_BYTES + pc * 16 + (col & 7) * 2;
+    return r * ROW_BYTES + chunk(r, col >> 3) * 16 + (col & 7) * 2;
   }
 };
+
+// One direct global->LDS load of 16 bytes per lane: lane i copies gbase + voff (bytes) to
+// LDS bytes lds_block + 16 i. Issued through inline asm on purpose: the compiler would
+// otherwise treat it as a store to every LDS location and wait for it (vmcnt(0)) before
+// the next LDS read, even when that read targets a different tile, which serialises the
+// prefetch with the MFMA phase. Callers order it explicitly instead: wait_lds_dma() and
+// a barrier before the destination tile is read, and never read a tile while its DMA is
+// in flight. gbase and lds_block must be wave-uniform. M0 has no other user in these
+// kernels.
+__device__ __forceinline__ void dma_16b(const char* gbase, uint32_t voff, const char* lds_block) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t laddr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_block;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(gbase), "s"(laddr) : "memory");
+#endif
+}
+
+// Copies rows [row0, row0 + ROWS) of a row-strided bf16 matrix (D columns) into an LDS
+// tile with a padded row pitch of PCH 16-byte chunks (PCH >= D/8), using direct
+// global->LDS loads (global_load_lds_dwordx4). Each wave instruction fills 1 KiB of
+// consecutive LDS, lane i writing bytes 16 i .. 16 i + 15; lanes that fall on a pad slot
+// stay idle. The per-lane global byte offsets (row * row_bytes + chunk * 16) are computed
+// once (init). Since chunk * 16 < row_bytes, "row < rows left" is simply
+// "offset < rows left * row_bytes", so rows at or past `nrows` are skipped with one
+// compare against a scalar and no extra registers; their LDS rows keep older (finite)
+// contents, which callers must mask (zero the tile once before first use). Data is
+// visible to the workgroup after wait_lds_dma() and a barrier. Requires
+// ROWS * row_stride * 2 < 2^31 (checked on the host).
+template <int ROWS, int D, int PCH, int NTHREADS>
+struct LdsDma {
+  static constexpr int CH = D / 8;
+  static constexpr int NW = NTHREADS / 64;
+  static constexpr int NBLK = ROWS * PCH / 64;                 // 1 KiB blocks in the tile
+  static constexpr int NI = (NBLK + NW - 1) / NW;              // blocks per wave (max)
+  static_assert(ROWS * PCH % 64 == 0, "padded tile must be whole 1 KiB blocks");
+  static_assert(PCH >= CH, "pitch shorter than a row");
+  static constexpr uint32_t kIdle = 0xFFFFFFFFu;
+  uint32_t off[NI];
+  int w;
+
+  __device__ __forceinline__ void init(int64_t row_stride, int tid) {
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int blk = j * NW + w;
+      const int L = blk * 64 + lane;
+      const int r = L / PCH, c = L - (L / PCH) * PCH;
+      off[j] = (blk < NBLK && c < CH) ? (uint32_t)(r * (int)(row_stride * 2) + c * 16) : kIdle;
+    }
+  }
+  // number of DMA instructions this wave issues per tile
+  __device__ __forceinline__ int count() const { return (NBLK - w + NW - 1) / NW; }
+  // wait until at most `tiles` tiles' worth of this wave's DMA (of this and `other`)
+  // remain in flight (loads complete in order); `tiles` is 1 or 2
+  template <class Other>
+  __device__ __forceinline__ void wait_leaving(const Other& other, int tiles) const {
+    const int n = tiles * (count() + other.count());
+    switch (n) {
+      case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+      case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+      case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+      case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+  }
+  __device__ __forceinline__ void issue(const __bf16* g, int64_t row_stride, int row0, int nrows,
+                                        char* lds_tile) const {
+    const int left = nrows - row0;
+    const uint32_t lim = (left >= ROWS) ? kIdle : (uint32_t)(left * (int)(row_stride * 2));
+    const char* base = (const char*)(g + (int64_t)row0 * row_stride);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int blk = j * NW + w;
+      if (blk >= NBLK) break;
+      if (off[j] < lim) dma_16b(base, off[j], lds_tile + blk * 1024);
+    }
+  }
+};
+
+// Zero `bytes` (a multiple of 16) of LDS with the whole workgroup; followed by a barrier.
+template <int NTHREADS>
+__device__ __forceinline__ void zero_lds(char* lds, int bytes, int tid) {
+  for (int o = tid * 16; o < bytes; o += NTHREADS * 16) *(u32x4*)(lds + o) = u32x4{};
+  __syncthreads();
+}
+
+// Wait until this wave's direct global->LDS loads have landed (vmcnt = 0). The asm form
+// is invisible to the compiler's wait-count tracking; wait_all_vmem() is the builtin form,
+// which also tells the compiler that every earlier vector-memory load has completed
+// (use it once before a loop, so the loop does not re-wait for loads issued before it).
+__device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Reductions over the two lanes (l, l ^ 32) that share a row, with v_permlane32_swap.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum of two packed bf16 values added to acc (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t packed, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // DPP controls (gfx9 encoding) and a sum over groups of 8 or 16 consecutive lanes that
 // stays inside one 16-lane DPP row (no LDS traffic).

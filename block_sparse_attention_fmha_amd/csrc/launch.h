@@ -10,8 +10,11 @@ namespace fmha {
 // bf16 forward: (Dqk, Dv) in {(64,64), (128,128), (192,128)}. Fills the tiling fields
 // of `p` (n_tiles, total_work, grid_padded) itself.
 hipError_t launch_fwd_bf16(AttnParams p, int dqk, int dv, hipStream_t st);
-int fwd_bf16_block_rows();   // query rows per workgroup (block-sparse tile_m must be a multiple)
+int fwd_bf16_block_rows();   // query rows per workgroup
+int fwd_bf16_list_rows();    // block-sparse tile_m must be a multiple (each half-workgroup reads one sparse row)
 int fwd_bf16_tile_keys();    // keys per tile (block-sparse tile_n must be a multiple)
+// Whether the merged tile sequence of a list row fits the forward kernel's LDS.
+bool fwd_bf16_lists_fit(int dqk, int dv, int n_cols, int tile_cols);
 
 // fp32 forward, D-split across wavefronts: D in {64, 128, 1024}, Dqk == Dv, analytic masks.
 hipError_t launch_fwd_f32(AttnParams p, int d, hipStream_t st);

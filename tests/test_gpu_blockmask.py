@@ -62,31 +62,41 @@ def test_block_sparse_forward_full_size(kind, W, P):
     check_bf16("LSE", l[:, heads][:, :, rows], l_ref[:, heads][:, :, rows])
 
 
-def test_block_sparse_custom_lists_small():
+@pytest.mark.parametrize("N,TM,TN,heads", [(512, 128, 128, 1), (700, 128, 192, 2), (1100, 384, 64, 2),
+                                          (300, 256, 128, 1)])
+def test_block_sparse_custom_lists_small(N, TM, TN, heads):
     # arbitrary lists (not derived from the mask): full tiles ignore the element mask,
-    # partial tiles apply it, unlisted tiles are skipped
+    # partial tiles apply it, unlisted tiles are skipped. Entries are unsorted, some are
+    # repeated, some columns sit in both lists of a row (full wins), and one row is empty
+    # (its queries see nothing: O = 0, LSE = -inf).
     import torch
     import block_sparse_attention_fmha_amd as fa
-    B, N, H, D, T = 1, 512, 2, 128, 128
-    q, k, v = synth.attention_inputs(synth.case_seed(9, 600), B, N, N, H, D, D, "bf16")
-    nt = N // T
-    rng = np.random.default_rng(5)
-    cls = rng.integers(0, 3, size=(nt, nt))   # 0 skip, 1 partial, 2 full
-    lists = {}
-    pc = np.zeros((1, 1, nt), np.int32); pi = np.full((1, 1, nt, nt), -1, np.int32)
-    fc = np.zeros((1, 1, nt), np.int32); fi = np.full((1, 1, nt, nt), -1, np.int32)
-    for r in range(nt):
-        p = np.nonzero(cls[r] == 1)[0]; f = np.nonzero(cls[r] == 2)[0]
-        pc[0, 0, r] = len(p); pi[0, 0, r, :len(p)] = p
-        fc[0, 0, r] = len(f); fi[0, 0, r, :len(f)] = f
+    B, H, D = 1, 2, 128
+    q, k, v = synth.attention_inputs(synth.case_seed(9, 600 + N), B, N, N, H, D, D, "bf16")
+    nqt, nkt = -(-N // TM), -(-N // TN)
+    rng = np.random.default_rng(N + TM + TN)
+    pc = np.zeros((B, heads, nqt), np.int32); pi = np.full((B, heads, nqt, nkt), -1, np.int32)
+    fc = np.zeros((B, heads, nqt), np.int32); fi = np.full((B, heads, nqt, nkt), -1, np.int32)
+    for hh in range(heads):
+        cls = rng.integers(0, 3, size=(nqt, nkt))   # 0 skip, 1 partial, 2 full
+        cls[nqt - 1] = 0 if nqt > 1 else cls[nqt - 1]
+        for r in range(nqt):
+            p = list(rng.permutation(np.nonzero(cls[r] == 1)[0]))
+            f = list(rng.permutation(np.nonzero(cls[r] == 2)[0]))
+            if len(p) > 1 and len(p) < nkt:
+                p.append(p[0])                    # repeated entry
+            if len(f) and len(p) < nkt:
+                p.append(f[-1])                   # also listed as full
+            pc[0, hh, r] = len(p); pi[0, hh, r, :len(p)] = p
+            fc[0, hh, r] = len(f); fi[0, hh, r, :len(f)] = f
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(a).to(dev)
-    bs = fa.BlockSparse(T, T, nt, nt, 1, t(pc), t(pi), t(fc), t(fi), None, None, None, None)
+    bs = fa.BlockSparse(TM, TN, nqt, nkt, heads, t(pc), t(pi), t(fc), t(fi), None, None, None, None)
     om, gm = mask_pair("causal", B, N, N)
-    announce("block-sparse fwd with custom lists N=512")
+    announce(f"block-sparse fwd with custom lists N={N} tiles={TM}x{TN} heads={heads}")
     out, lse = fa.fmha_fwd(to_dev(q), to_dev(k), to_dev(v), mask=gm, block_sparse=bs)
     torch.cuda.synchronize()
-    ref_lists = oracle.BlockLists(T, T, pc, pi, fc, fi, None, None, None, None)
+    ref_lists = oracle.BlockLists(TM, TN, pc, pi, fc, fi, None, None, None, None)
     o_ref, l_ref = oracle.forward(q.values, k.values, v.values, mask=om, lists=ref_lists)
     check_bf16("O", host(out), o_ref)
     check_bf16("LSE", host(lse), l_ref)
