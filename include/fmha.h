@@ -97,10 +97,18 @@ typedef struct {
  *   Backward (transposed) lists, per (b, mask head, key tile):
  *     t_partial_cnt [B, heads, n_kv_tiles], t_partial_idx [B, heads, n_kv_tiles, n_q_tiles]
  *     t_full_cnt    [B, heads, n_kv_tiles], t_full_idx    [B, heads, n_kv_tiles, n_q_tiles]
- *   Index rows hold `cnt` ascending tile indices followed by -1 padding.
+ *   Index rows hold `cnt` tile indices followed by -1 padding (build_block_mask writes
+ *   them ascending; the forward accepts any order).
  * A FULL tile is attended without the element mask, a PARTIAL tile applies the
- * element mask (fmha_mask), an unlisted tile is skipped. Rows and columns past Nq / Nk
- * are always excluded. */
+ * element mask (fmha_mask), an unlisted tile is skipped. Entries outside the tile range
+ * are ignored. The forward treats lists as sets (a repeated entry counts once, a tile in
+ * both lists of a row is FULL); the backward requires each tile at most once per row
+ * over both lists, as build_block_mask writes them. Rows and columns past Nq / Nk are
+ * always excluded.
+ * Kernel granularity (FMHA_ERR_UNSUPPORTED otherwise): forward tile_m % 128 == 0 and
+ * tile_n % 64 == 0, with n_kv_tiles * tile_n / 64 small enough for the merged tile
+ * sequence of a 256-query workgroup to fit in LDS next to the K/V stages (about 3000
+ * 64-key tiles at D = 128); backward tile_m % 128 == 0 and tile_n % 128 == 0. */
 typedef struct {
   int32_t tile_m, tile_n;
   int32_t n_q_tiles, n_kv_tiles;
