@@ -248,7 +248,7 @@ int fmha_fwd(const fmha_fwd_args* a, void* stream) {
 
 size_t fmha_bwd_workspace_size(int32_t B, int32_t H, int32_t Nq) {
   if (B < 0 || H < 0 || Nq < 0) return 0;
-  return align256((size_t)B * H * Nq * sizeof(float));
+  return align256(fmha::bwd_workspace_bytes(B, H, Nq));
 }
 
 int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
@@ -265,7 +265,7 @@ int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
       !strides_ok(g->dv_stride, 2))
     return FMHA_ERR_INVALID_ARG;
   const size_t need = fmha_bwd_workspace_size(a->B, a->H, a->Nq);
-  if (g->workspace == nullptr || g->workspace_bytes < need) return FMHA_ERR_WORKSPACE;
+  if (g->workspace == nullptr || g->workspace_bytes < need || !aligned16(g->workspace)) return FMHA_ERR_WORKSPACE;
   if (a->block_sparse) {
     rc = validate_lists(a->block_sparse, a->B, a->H, a->Nq, a->Nk, a->Dqk, a->Dv, true);
     if (rc != FMHA_OK) return rc;
@@ -281,7 +281,8 @@ int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
   bp.dq = g->dq;
   bp.dk = g->dk;
   bp.dv = g->dv;
-  bp.dsum = static_cast<float*>(g->workspace);
+  bp.ws = static_cast<float*>(g->workspace);
+  if (!fmha::bwd_lists_fit(a->Dqk, a->Dv, bp.a.lists, bp.tlists)) return FMHA_ERR_UNSUPPORTED;
   bp.dos_b = g->do_stride[0]; bp.dos_s = g->do_stride[1]; bp.dos_h = g->do_stride[2];
   bp.dqs_b = g->dq_stride[0]; bp.dqs_s = g->dq_stride[1]; bp.dqs_h = g->dq_stride[2];
   bp.dks_b = g->dk_stride[0]; bp.dks_s = g->dk_stride[1]; bp.dks_h = g->dk_stride[2];

@@ -10,372 +10,381 @@
 //
 // Three kernels, no atomics (every gradient element has one writer and a fixed
 // summation order, so results are bitwise reproducible):
-//   1. preprocess: D = rowsum(dO * O) with DPP row reductions;
-//   2. dK/dV pass: a workgroup owns 128 keys (32 per wave, K and V of those keys held in
-//      VGPRs as MFMA B operands) and walks 64-query tiles of Q / dO staged in LDS;
-//      S = Q K^T and dP = dO V^T come out with ONE KEY PER LANE and 8 consecutive queries
-//      per register group, which is exactly the B operand of dV^T += dO^T P and
-//      dK^T += Q^T dS; dO^T / Q^T operands come from transposed LDS reads;
-//   3. dQ pass: a workgroup owns 128 queries (Q and dO fragments in VGPRs) and walks
-//      64-key tiles of K / V in LDS, mirroring the forward: S^T = K Q^T, dP^T = V dO^T,
-//      dQ^T += K^T dS^T with K^T from transposed LDS reads.
+//   1. preprocess: per 64-query block, lse2 = LSE log2(e) and D = rowsum(dO * O) into the
+//      workspace, padded with (+inf, 0) past Nq so that padded queries drop out of every
+//      product without masks;
+//   2. dK/dV pass: a workgroup owns 128 keys and walks 64-query steps (Q, dO, lse2, D
+//      staged in LDS by direct global->LDS loads). The 8 waves form 4 PAIRS, one per SIMD,
+//      each pair owning 32 keys. The "P wave" holds K of the keys in VGPRs, computes
+//      S = Q K^T, P, and accumulates dV^T += dO^T P; the "dS wave" holds V, computes
+//      dP = dO V^T, dS = P (dP - D) with P handed over through LDS, and accumulates
+//      dK^T += Q^T dS. Each wave needs half the registers of a wave doing all four
+//      products, so two waves fit per SIMD and ping-pong: while one runs its 32 MFMAs of
+//      the step the other runs its exp / dS arithmetic, one phase apart, as in the
+//      forward. S and dP come out with ONE KEY PER LANE and 8 consecutive queries per
+//      register group, which is the B operand of the dV / dK products as is; dO^T / Q^T
+//      come from transposed LDS reads;
+//   3. dQ pass: the forward's structure (256 queries per workgroup, 8 waves ping-ponging
+//      on 64-key tiles in 4 LDS stages): S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with
+//      K^T from transposed LDS reads.
 // The dQ pass recomputes S and dP (7 matrix products instead of 5): that is the price
 // of determinism without atomics.
 //
-// LDS tiles are row-major with the XOR chunk swizzle of SwizzledTile so that the same
-// tile serves 16-byte MFMA row reads and transposed reads without bank conflicts.
+// Tiles read both row-wise (16-byte MFMA rows) and transposed (8-byte reads of 4 rows)
+// use a row pitch of an odd number of 16-byte chunks that is not 0 or +-16 bytes modulo
+// 256: conflict-free row reads and at most 2-way conflicted transposed reads.
 #include "kernel_common.h"
 #include "launch.h"
 
 namespace fmha {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBQ = 64;      // queries per dK/dV step
-constexpr int kBK = 128;     // keys per dK/dV workgroup
-constexpr int kQM = 128;     // queries per dQ workgroup
+constexpr int kThreads = 512;
+constexpr int kKB = 128;     // keys per dK/dV workgroup: 4 wave pairs x 32 keys
+constexpr int kQS = 64;      // queries per dK/dV step
+constexpr int kQM = 256;     // queries per dQ workgroup: 8 waves x 32
 constexpr int kKN = 64;      // keys per dQ step
+constexpr int kPreThreads = 256;
+
+// Row pitch in 16-byte chunks of a tile read row-wise and transposed.
+template <int D> struct DualPitch;
+template <> struct DualPitch<64> { static constexpr int value = 9; };
+template <> struct DualPitch<128> { static constexpr int value = 19; };
+template <> struct DualPitch<192> { static constexpr int value = 25; };
+// Row pitch of a tile read row-wise only (odd chunk count: conflict-free 16-byte reads).
+template <int D> struct RowPitch { static constexpr int value = D / 8 + 1; };
 
 // ------------------------------------------------------------------------------- preprocess
 template <int DV>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kPreThreads)
 void bwd_preprocess_kernel(const BwdParams bp) {
   constexpr int LPK = DV / 8;
-  constexpr int ROWS = kThreads / LPK;
+  constexpr int ROWS = kPreThreads / LPK;
   const AttnParams& p = bp.a;
+  const int npad = bp.n_qblk * 64;
   const int64_t r = (int64_t)blockIdx.x * ROWS + threadIdx.x / LPK;
   const int dl = threadIdx.x % LPK;
-  const int64_t total = (int64_t)p.B * p.H * p.Nq;
+  const int64_t total = (int64_t)p.B * p.H * npad;
   const bool in = r < total;
-  float x = 0.0f;
-  int b = 0, h = 0, i = 0;
+  float x = 0.0f, lse2 = __builtin_huge_valf();
+  int64_t bh = 0;
+  int i = 0;
   if (in) {
-    i = (int)(r % p.Nq);
-    const int64_t bh = r / p.Nq;
-    h = (int)(bh % p.H);
-    b = (int)(bh / p.H);
-    const __bf16* Og = (const __bf16*)p.o + b * p.os_b + h * p.os_h + (int64_t)i * p.os_s + 8 * dl;
-    const __bf16* Dg = (const __bf16*)bp.dout + b * bp.dos_b + h * bp.dos_h + (int64_t)i * bp.dos_s + 8 * dl;
-    float of[8], df[8];
-    bf16x8_to_f32(*(const u32x4*)Og, of);
-    bf16x8_to_f32(*(const u32x4*)Dg, df);
+    i = (int)(r % npad);
+    bh = r / npad;
+    if (i < p.Nq) {
+      const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+      const __bf16* Og = (const __bf16*)p.o + b * p.os_b + h * p.os_h + (int64_t)i * p.os_s + 8 * dl;
+      const __bf16* Dg = (const __bf16*)bp.dout + b * bp.dos_b + h * bp.dos_h + (int64_t)i * bp.dos_s + 8 * dl;
+      float of[8], df[8];
+      bf16x8_to_f32(*(const u32x4*)Og, of);
+      bf16x8_to_f32(*(const u32x4*)Dg, df);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x = __builtin_fmaf(of[e], df[e], x);
+      for (int e = 0; e < 8; ++e) x = __builtin_fmaf(of[e], df[e], x);
+      const float ls = p.lse[bh * p.Nq + i];
+      lse2 = (ls == kNegInf) ? __builtin_huge_valf() : ls * kLog2e;
+    }
   }
   x = group_sum<LPK>(x);
-  if (in && dl == 0) bp.dsum[r] = x;
-}
-
-// Log2-domain probability of the recomputed score, its softcap derivative factor, and
-// the mask. `raw` is <q, k>; lse2 = LSE * log2(e) (+inf for empty / out-of-range rows).
-template <bool SOFTCAP, bool BIAS>
-__device__ __forceinline__ float recompute_p(float raw, const AttnParams& p, int i, int j, float lse2,
-                                             float& dcap) {
-  if constexpr (SOFTCAP || BIAS) {
-    float x = raw * p.scale;
-    dcap = 1.0f;
-    if constexpr (SOFTCAP) {
-      const float e = fast_exp2(x * (2.0f * kLog2e / p.softcap));
-      const float th = 1.0f - 2.0f * fast_rcp(e + 1.0f);
-      x = p.softcap * th;
-      dcap = 1.0f - th * th;
-    }
-    float u = x * kLog2e;
-    if constexpr (BIAS) u += p.bias_log2 * (float)abs(i - j);
-    return fast_exp2(u - lse2);
-  } else {
-    dcap = 1.0f;
-    return fast_exp2(__builtin_fmaf(raw, p.scale_log2, -lse2));
+  if (in && dl == 0) {
+    float* blk = bp.ws + (bh * bp.n_qblk + i / 64) * 128;
+    blk[i % 64] = lse2;
+    blk[64 + i % 64] = x;
   }
 }
 
 // ------------------------------------------------------------------------------- dK / dV
 template <int DQK, int DV>
 struct DkdvSmem {
-  static constexpr int QB = kBQ * DQK * 2;
-  static constexpr int OB = kBQ * DV * 2;
-  static constexpr int STAGE = QB + OB + 2 * kBQ * 4;   // Q, dO, lse2, D
-  static constexpr int BYTES = 2 * STAGE;
+  static constexpr int QPC = DualPitch<DQK>::value, OPC = DualPitch<DV>::value;
+  static constexpr int QP = QPC * 16, OP = OPC * 16;   // bytes
+  static constexpr int QB = kQS * QP, OB = kQS * OP;
+  static constexpr int LB = 1024;                      // lse2[64], D[64], 512 bytes unused
+  static constexpr int STAGE = QB + OB + LB;
+  static constexpr int XB = 4 * 64 * 64;               // P hand-over: 4 pairs x 64 lanes x 64 B
+  static constexpr int NST = (4 * STAGE + XB <= 148 * 1024) ? 4 : 3;
+  static constexpr int BYTES = NST * STAGE + XB;
 };
+
+// One matrix phase of a dK/dV wave. First acc^T += T^T bop for the previous step (T = dO
+// for the P wave, Q for the dS wave, read transposed; DA = its width), then
+// s = R bf^T for the current step (R = Q for the P wave, dO for the dS wave, rows in the
+// permuted order; DR = its width). Either half may be absent.
+template <int DR, int DA, int RP, int TP, int NBF, int NACC>
+__device__ __forceinline__ void dkdv_matrix(const char* Tl, const char* Rl, bool do_acc, bool do_s,
+                                            f32x16 (&acc)[NACC], const bf16x8 (&bop)[2][2], f32x16 (&s)[2],
+                                            const bf16x8 (&bf)[NBF], int trow, int tcol, int prow, int g) {
+  if (do_acc) {
+#pragma unroll
+    for (int db = 0; db < DA / 32; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const char* tp = Tl + (32 * kb + 16 * hh + trow) * TP + (32 * db + tcol) * 2;
+          const u32x2 lo = lds_read_tr(tp);
+          const u32x2 hi = lds_read_tr(tp + 4 * TP);
+          acc[db] = mfma_bf16(join_bf16x8(lo, hi), bop[kb][hh], acc[db]);
+        }
+  }
+  if (do_s) {
+    const char* rp = Rl + prow * RP + 16 * g;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < DR / 16; ++ks) {
+      const bf16x8 a0 = *(const bf16x8*)(rp + 32 * ks);
+      const bf16x8 a1 = *(const bf16x8*)(rp + 32 * RP + 32 * ks);
+      s[0] = mfma_bf16(a0, bf[ks], s[0]);
+      s[1] = mfma_bf16(a1, bf[ks], s[1]);
+    }
+  }
+}
 
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
 void bwd_dkdv_kernel(const BwdParams bp) {
   using SM = DkdvSmem<DQK, DV>;
-  using TQ = SwizzledTile<DQK>;
-  using TO = SwizzledTile<DV>;
+  constexpr int DM = DQK > DV ? DQK : DV;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnParams& p = bp.a;
 
   const int bid = xcd_remap(blockIdx.x, bp.grid_padded_kv);
   if (bid >= bp.total_work_kv) return;
   const int bh = bid / bp.n_kv_tiles;
-  const int kt = bid - bh * bp.n_kv_tiles;
-  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int k0 = kt * kBK;
+  const int kt = bid - bh * bp.n_kv_tiles;   // ascending: under causal masks the first key
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;   // tiles see the most queries
+  const int k0 = kt * kKB;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 5, lq = l & 31;
+  const int role = w >> 2;     // 0: P wave (K; S, P, dV), 1: dS wave (V; dP, dS, dK)
+  const int pair = w & 3;      // waves w and w + 4 share a SIMD and the same 32 keys
   const int Nq = p.Nq, Nk = p.Nk, delta = Nk - Nq;
-  const int kw = k0 + 32 * w;
+  const int kw = k0 + 32 * pair;
   const int key = kw + lq;
 
   const __bf16* Qg = (const __bf16*)p.q + b * p.qs_b + h * p.qs_h;
   const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + h * p.ks_h;
   const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + h * p.vs_h;
   const __bf16* DOg = (const __bf16*)bp.dout + b * bp.dos_b + h * bp.dos_h;
-  const float* LSEg = p.lse + ((int64_t)b * p.H + h) * Nq;
-  const float* Dg = bp.dsum + ((int64_t)b * p.H + h) * Nq;
+  const char* WSg = (const char*)(bp.ws + (int64_t)bh * bp.n_qblk * 128);
 
   // ---- query-step sequence
+  TileSeq<kQS> seq;
+  seq.t_lo = 0;
+  seq.ent = (const uint32_t*)(smem + SM::BYTES + 16);
   const int mk = p.mask.kind;
-  int count, s_lo = 0, sub = 1, npart = 0, ncols = 0;
-  const int* pidx = nullptr;
-  const int* fidx = nullptr;
   if constexpr (!LISTS) {
     int lo = 0, hi = Nq;
     if (mk == kMaskCausal || mk == kMaskWindow) lo = max(0, k0 - delta);
     if (mk == kMaskPrefix) lo = (k0 < p.mask.prefix) ? 0 : max(0, k0 - delta);
-    if (mk == kMaskWindow) hi = min(Nq, k0 + kBK - 1 - delta + p.mask.window + 1);
+    if (mk == kMaskWindow) hi = min(Nq, k0 + kKB - 1 - delta + p.mask.window + 1);
     lo = min(lo, Nq);
-    s_lo = lo / kBQ;
-    count = max(0, (hi + kBQ - 1) / kBQ - s_lo);
+    seq.t_lo = lo / kQS;
+    seq.count = max(0, (hi + kQS - 1) / kQS - seq.t_lo);
   } else {
-    const int ks = k0 / p.lists.tile_rows;
-    const int hm = (p.lists.heads == 1) ? 0 : h;
-    const int row = (b * p.lists.heads + hm) * p.lists.n_rows + ks;
-    ncols = p.lists.n_cols;
-    npart = clamp_count(p.lists.pcnt[row], ncols);
-    const int nfull = clamp_count(p.lists.fcnt[row], ncols);
-    pidx = p.lists.pidx + (int64_t)row * ncols;
-    fidx = p.lists.fidx + (int64_t)row * ncols;
-    sub = p.lists.tile_cols / kBQ;
-    count = (npart + nfull) * sub;
+    const ListParams& L = p.lists;   // transposed lists: rows = key tiles
+    const int64_t row = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h)) * L.n_rows + k0 / L.tile_rows;
+    seq.count = build_tile_sequence<kThreads, kQS>(L, row, -1, Nq, smem + SM::BYTES, tid);
   }
-  auto step_at = [&](int it, int& i0, bool& partial) {
-    if constexpr (!LISTS) {
-      i0 = (s_lo + it) * kBQ;
-      partial = false;
-    } else {
-      const int e = it / sub, s = it - e * sub;
-      int qt;
-      if (e < npart) { qt = list_entry(pidx, e, ncols); partial = true; }
-      else { qt = list_entry(fidx, e - npart, ncols); partial = false; }
-      i0 = qt * sub * kBQ + s * kBQ;
-    }
-  };
 
-  // ---- K and V of this lane's key as B operands (k-slot = head dim)
-  bf16x8 kf[DQK / 16], vf[DV / 16];
+  // ---- B operand of this wave's S (K) or dP (V): the lane's key, k-slot = head dim
+  bf16x8 bf[DM / 16];
+  {
+    const __bf16* src = role ? Vg : Kg;
+    const int64_t st = role ? p.vs_s : p.ks_s;
+    const int dr = role ? DV : DQK;
 #pragma unroll
-  for (int ks = 0; ks < DQK / 16; ++ks)
-    kf[ks] = (key < Nk) ? *(const bf16x8*)(Kg + (int64_t)key * p.ks_s + 16 * ks + 8 * g) : bf16x8{};
-#pragma unroll
-  for (int ks = 0; ks < DV / 16; ++ks)
-    vf[ks] = (key < Nk) ? *(const bf16x8*)(Vg + (int64_t)key * p.vs_s + 16 * ks + 8 * g) : bf16x8{};
+    for (int ks = 0; ks < DM / 16; ++ks)
+      bf[ks] = (16 * ks < dr && key < Nk) ? *(const bf16x8*)(src + (int64_t)key * st + 16 * ks + 8 * g) : bf16x8{};
+  }
 
-  // ---- staging of one Q / dO tile (+ lse2, D)
-  constexpr int QCH = kBQ * DQK / 8 / kThreads;
-  constexpr int OCH = kBQ * DV / 8 / kThreads;
-  u32x4 qreg[QCH], oreg[OCH];
-  float lreg = 0.0f, dreg = 0.0f;
-  auto load_step = [&](int i0) {
+  f32x16 acc[DM / 32];
 #pragma unroll
-    for (int c2 = 0; c2 < QCH; ++c2) {
-      const int c = tid + kThreads * c2;
-      const int row = c / (DQK / 8), col = c - row * (DQK / 8);
-      const int i = i0 + row;
-      qreg[c2] = (i < Nq) ? *(const u32x4*)(Qg + (int64_t)i * p.qs_s + col * 8) : u32x4{};
-    }
-#pragma unroll
-    for (int c2 = 0; c2 < OCH; ++c2) {
-      const int c = tid + kThreads * c2;
-      const int row = c / (DV / 8), col = c - row * (DV / 8);
-      const int i = i0 + row;
-      oreg[c2] = (i < Nq) ? *(const u32x4*)(DOg + (int64_t)i * bp.dos_s + col * 8) : u32x4{};
-    }
-    if (tid < kBQ) {
-      const int i = i0 + tid;
-      const float ls = (i < Nq) ? LSEg[i] : kNegInf;
-      lreg = (ls == kNegInf) ? __builtin_huge_valf() : ls * kLog2e;
-      dreg = (i < Nq) ? Dg[i] : 0.0f;
-    }
-  };
-  auto store_step = [&](int buf) {
-    char* Ql = smem + buf * SM::STAGE;
-    char* Ol = Ql + SM::QB;
-    float* Ll = (float*)(Ol + SM::OB);
-#pragma unroll
-    for (int c2 = 0; c2 < QCH; ++c2) {
-      const int c = tid + kThreads * c2;
-      const int row = c / (DQK / 8), col = c - row * (DQK / 8);
-      *(u32x4*)(Ql + TQ::off(row, col * 8)) = qreg[c2];
-    }
-#pragma unroll
-    for (int c2 = 0; c2 < OCH; ++c2) {
-      const int c = tid + kThreads * c2;
-      const int row = c / (DV / 8), col = c - row * (DV / 8);
-      *(u32x4*)(Ol + TO::off(row, col * 8)) = oreg[c2];
-    }
-    if (tid < kBQ) {
-      Ll[tid] = lreg;
-      Ll[kBQ + tid] = dreg;
-    }
-  };
-
-  f32x16 dk[DQK / 32], dv[DV / 32];
-#pragma unroll
-  for (int i = 0; i < DQK / 32; ++i) dk[i] = f32x16{};
-#pragma unroll
-  for (int i = 0; i < DV / 32; ++i) dv[i] = f32x16{};
+  for (int i = 0; i < DM / 32; ++i) acc[i] = f32x16{};
+  f32x16 s[2];
+  bf16x8 bop[2][2];
   const int prow = swap_bits23(lq);
   const int trow = 8 * g + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  u32x4* xch = (u32x4*)(smem + SM::NST * SM::STAGE + pair * 4096) + l;   // + 64 i
 
-  if (count > 0) {
-    int i0;
-    bool part;
-    step_at(0, i0, part);
-    load_step(i0);
-    store_step(0);
-    __syncthreads();
-  }
+  // visible queries of the lane's key under the band masks: qlo <= i <= qhi
+  int qlo = 0, qhi = 0x3fffffff;
+  if (mk == kMaskCausal || mk == kMaskWindow || (mk == kMaskPrefix && key >= p.mask.prefix)) qlo = key - delta;
+  if (mk == kMaskWindow) qhi = key - delta + p.mask.window;
 
-  for (int it = 0; it < count; ++it) {
-    const int buf = it & 1;
-    int i0;
-    bool partial;
-    step_at(it, i0, partial);
-    if (it + 1 < count) {
-      int i1;
-      bool p1;
-      step_at(it + 1, i1, p1);
-      load_step(i1);
-    }
-    const char* Ql = smem + buf * SM::STAGE;
-    const char* Ol = Ql + SM::QB;
-    const float* Ll = (const float*)(Ol + SM::OB);
+  LdsDma<kQS, DQK, SM::QPC, kThreads> qdma;
+  LdsDma<kQS, DV, SM::OPC, kThreads> odma;
+  qdma.init(p.qs_s, tid);
+  odma.init(bp.dos_s, tid);
+  constexpr int ld_wave = 7;   // a wave with the fewest tile blocks issues the lse2 / D load
+  const int per_step = qdma.count() + odma.count() + (w == ld_wave ? 1 : 0);
+  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // rows past Nq are never loaded: keep them finite
+  auto issue_step = [&](int t) {
+    const int i0 = seq.start(t, LISTS);
+    char* st = smem + (t % SM::NST) * SM::STAGE;
+    qdma.issue(Qg, p.qs_s, i0, Nq, st);
+    odma.issue(DOg, bp.dos_s, i0, Nq, st + SM::QB);
+    if (w == ld_wave) dma_16b(WSg, (uint32_t)(i0 / 64) * 512u + 16u * l, st + SM::QB + SM::OB);
+  };
 
-    bool need;
-    if constexpr (LISTS) {
-      need = partial;
-    } else {
-      const int kl = kw + 31;
-      need = false;
-      if (mk == kMaskCausal) need = kl > i0 + delta;
-      else if (mk == kMaskWindow) need = (kl > i0 + delta) || (kw < i0 + kBQ - 1 + delta - p.mask.window);
-      else if (mk == kMaskPrefix) need = (kl >= p.mask.prefix) && (kl > i0 + delta);
-      else if (mk == kMaskBlockDiag) need = true;
-    }
+  const int T = seq.count;
+  const bool last_ragged = T > 0 && seq.start(T - 1, LISTS) + kQS > Nq;
+  for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_step(t);
+  wait_all_vmem();
+  __syncthreads();
 
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      // S = Q K^T: rows = queries (permuted), columns = this lane's key
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(Ql + TQ::off(32 * sb + prow, 16 * ks + 8 * g));
-        s = mfma_bf16(a, kf[ks], s);
+  // Phase ph = 0 .. 2T+1, local phase lp = ph - role (the dS waves run one phase behind).
+  //   lp even: matrix phase: acc += T(lp/2 - 1)^T bop, s = R(lp/2) bf^T
+  //   lp odd:  vector phase of step (lp-1)/2: P wave: P (into bop and the hand-over
+  //            buffer); dS wave: dS from the handed-over P (into bop)
+  // The P wave writes the hand-over buffer at phase 2t+1 and the dS wave reads it at
+  // phase 2t+2; the next write comes at 2t+3. Stage t is read during phases 2t .. 2t+3.
+  for (int ph = 0; ph < 2 * T + 2; ++ph) {
+    if ((ph & 1) == 0 && ph / 2 + SM::NST - 2 < T) issue_step(ph / 2 + SM::NST - 2);
+    const int lp = ph - role;
+    if (lp >= 0 && (lp & 1) == 0) {
+      // ------------------------------------------------------------- matrix phase
+      const int ts = lp >> 1, tv = ts - 1;
+      const char* Sv = smem + ((tv < 0 ? 0 : tv) % SM::NST) * SM::STAGE;
+      const char* Ss = smem + (ts % SM::NST) * SM::STAGE;
+      if constexpr (DQK == DV) {
+        const char* Tl = Sv + (role ? 0 : SM::QB);
+        const char* Rl = Ss + (role ? SM::QB : 0);
+        dkdv_matrix<DQK, DQK, SM::QP, SM::QP>(Tl, Rl, tv >= 0, ts < T, acc, bop, s, bf, trow, tcol, prow, g);
+      } else {
+        if (role == 0)
+          dkdv_matrix<DQK, DV, SM::QP, SM::OP>(Sv + SM::QB, Ss, tv >= 0, ts < T, acc, bop, s, bf, trow, tcol, prow, g);
+        else
+          dkdv_matrix<DV, DQK, SM::OP, SM::QP>(Sv, Ss + SM::QB, tv >= 0, ts < T, acc, bop, s, bf, trow, tcol, prow, g);
       }
-      f32x16 dp = f32x16{};
+    } else if (lp >= 0 && (lp >> 1) < T) {
+      // ------------------------------------------------------------- vector phase
+      const int ts = lp >> 1;
+      const int i0 = seq.start(ts, LISTS);
+      const float* LD = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB);
+      // register r of block kb holds query i0 + 32 kb + 16 (r / 8) + 8 g + r % 8
+      if (role == 0) {
+        bool need;
+        if constexpr (LISTS) {
+          need = seq.cls(ts, 0, true) != 2u;
+        } else {
+          need = false;
+          if (mk == kMaskCausal) need = kw + 31 > i0 + delta;
+          else if (mk == kMaskWindow) need = (kw + 31 > i0 + delta) || (kw < i0 + kQS - 1 + delta - p.mask.window);
+          else if (mk == kMaskPrefix) need = (kw + 31 >= p.mask.prefix) && (kw + 31 > i0 + delta);
+          else if (mk == kMaskBlockDiag) need = true;
+        }
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(Ol + TO::off(32 * sb + prow, 16 * ks + 8 * g));
-        dp = mfma_bf16(a, vf[ks], dp);
-      }
-      // reg r <-> query i0 + 32 sb + 16 (r/8) + 8 g + r % 8
-      bf16x8 pb[2], dsb[2];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int qi = 32 * sb + 16 * hh + 8 * g;
-        const f32x4 la = *(const f32x4*)(Ll + qi), lb = *(const f32x4*)(Ll + qi + 4);
-        const f32x4 da = *(const f32x4*)(Ll + kBQ + qi), db4 = *(const f32x4*)(Ll + kBQ + qi + 4);
-        u32x4 pk, dk4;
+          for (int hh = 0; hh < 2; ++hh) {
+            const int qi = 32 * kb + 16 * hh + 8 * g;
+            const f32x4 la = *(const f32x4*)(LD + qi), lb = *(const f32x4*)(LD + qi + 4);
+            u32x4 pk, pc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv[2], dsv[2];
+            for (int e = 0; e < 4; ++e) {
+              float pv[2], pd[2];
 #pragma unroll
-          for (int z = 0; z < 2; ++z) {
-            const int r = 8 * hh + 2 * e + z;
-            const int ee = 2 * e + z;
-            const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
-            const float dd = ee < 4 ? da[ee] : db4[ee - 4];
-            const int qidx = i0 + qi + ee;
-            float dcap;
-            float pr = recompute_p<SOFTCAP, BIAS>(s[r], p, qidx, key, lse2, dcap);
-            if (need && qidx < Nq && !mask_visible(p.mask, b, qidx, key, Nq, Nk)) pr = 0.0f;
-            pv[z] = pr;
-            dsv[z] = pr * (dp[r] - dd) * dcap;
+              for (int z = 0; z < 2; ++z) {
+                const int ee = 2 * e + z, r = 8 * hh + ee;
+                const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
+                const int qidx = i0 + qi + ee;
+                float dcap = 1.0f, u;
+                if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
+                else u = s[kb][r] * p.scale_log2;
+                if (need) {
+                  bool vis;
+                  if (mk == kMaskBlockDiag) vis = qidx >= Nq || key >= Nk || mask_visible(p.mask, b, qidx, key, Nq, Nk);
+                  else vis = qidx >= qlo && qidx <= qhi;
+                  if (!vis) u = kNegInf;
+                }
+                pv[z] = fast_exp2(u - lse2);
+                pd[z] = pv[z] * dcap;
+              }
+              pk[e] = pack_bf16x2(pv[0], pv[1]);
+              pc[e] = SOFTCAP ? pack_bf16x2(pd[0], pd[1]) : pk[e];
+            }
+            bop[kb][hh] = __builtin_bit_cast(bf16x8, pk);
+            xch[64 * (2 * kb + hh)] = pc;
           }
-          pk[e] = pack_bf16x2(pv[0], pv[1]);
-          dk4[e] = pack_bf16x2(dsv[0], dsv[1]);
-        }
-        pb[hh] = __builtin_bit_cast(bf16x8, pk);
-        dsb[hh] = __builtin_bit_cast(bf16x8, dk4);
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (transposed reads of the row-major tiles)
+      } else {
+        const float* Dl = LD + 64;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = 32 * sb + 16 * hh + trow;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db) {
-          const u32x2 lo = lds_read_tr(Ol + TO::off(r0, 32 * db + tcol));
-          const u32x2 hi = lds_read_tr(Ol + TO::off(r0 + 4, 32 * db + tcol));
-          dv[db] = mfma_bf16(join_bf16x8(lo, hi), pb[hh], dv[db]);
-        }
+          for (int hh = 0; hh < 2; ++hh) {
+            const int qi = 32 * kb + 16 * hh + 8 * g;
+            const f32x4 da = *(const f32x4*)(Dl + qi), db4 = *(const f32x4*)(Dl + qi + 4);
+            const u32x4 pc = xch[64 * (2 * kb + hh)];
+            u32x4 dk4;
 #pragma unroll
-        for (int db = 0; db < DQK / 32; ++db) {
-          const u32x2 lo = lds_read_tr(Ql + TQ::off(r0, 32 * db + tcol));
-          const u32x2 hi = lds_read_tr(Ql + TQ::off(r0 + 4, 32 * db + tcol));
-          dk[db] = mfma_bf16(join_bf16x8(lo, hi), dsb[hh], dk[db]);
-        }
+            for (int e = 0; e < 4; ++e) {
+              float pf[2];
+              bf16x2_to_f32(pc[e], pf);
+              float dsv[2];
+#pragma unroll
+              for (int z = 0; z < 2; ++z) {
+                const int ee = 2 * e + z, r = 8 * hh + ee;
+                const float dd = ee < 4 ? da[ee] : db4[ee - 4];
+                dsv[z] = pf[z] * (s[kb][r] - dd);
+              }
+              dk4[e] = pack_bf16x2(dsv[0], dsv[1]);
+            }
+            bop[kb][hh] = __builtin_bit_cast(bf16x8, dk4);
+          }
       }
     }
-
-    if (it + 1 < count) store_step(buf ^ 1);
+    if (ph & 1) {
+      // step (ph + 1) / 2 is read from the next phase on; the NST - 3 steps issued after
+      // it may stay in flight, unless a ragged last step made some waves skip loads
+      const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
+      const bool exact = later > 0 && !(last_ragged && (ph + 1) / 2 + later == T - 1);
+      if (exact) wait_vmcnt_at_most(later * per_step);
+      else wait_lds_dma();
+    }
     __syncthreads();
   }
 
   // ---- epilogue: lane = key, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
   if (key < Nk) {
-    __bf16* dKg = (__bf16*)bp.dk + b * bp.dks_b + h * bp.dks_h + (int64_t)key * bp.dks_s;
-    __bf16* dVg = (__bf16*)bp.dv + b * bp.dvs_b + h * bp.dvs_h + (int64_t)key * bp.dvs_s;
+    const bool isk = role != 0;
+    __bf16* dst = isk ? (__bf16*)bp.dk + b * bp.dks_b + h * bp.dks_h + (int64_t)key * bp.dks_s
+                      : (__bf16*)bp.dv + b * bp.dvs_b + h * bp.dvs_h + (int64_t)key * bp.dvs_s;
+    const float sc = isk ? p.scale : 1.0f;
+    const int dw = isk ? DQK : DV;
 #pragma unroll
-    for (int db = 0; db < DQK / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x2 v;
-        v[0] = pack_bf16x2(dk[db][4 * jj] * p.scale, dk[db][4 * jj + 1] * p.scale);
-        v[1] = pack_bf16x2(dk[db][4 * jj + 2] * p.scale, dk[db][4 * jj + 3] * p.scale);
-        *(u32x2*)(dKg + 32 * db + 8 * jj + 4 * g) = v;
-      }
-#pragma unroll
-    for (int db = 0; db < DV / 32; ++db)
+    for (int db = 0; db < DM / 32; ++db) {
+      if (32 * db >= dw) break;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         u32x2 v;
-        v[0] = pack_bf16x2(dv[db][4 * jj], dv[db][4 * jj + 1]);
-        v[1] = pack_bf16x2(dv[db][4 * jj + 2], dv[db][4 * jj + 3]);
-        *(u32x2*)(dVg + 32 * db + 8 * jj + 4 * g) = v;
+        v[0] = pack_bf16x2(acc[db][4 * jj] * sc, acc[db][4 * jj + 1] * sc);
+        v[1] = pack_bf16x2(acc[db][4 * jj + 2] * sc, acc[db][4 * jj + 3] * sc);
+        *(u32x2*)(dst + 32 * db + 8 * jj + 4 * g) = v;
       }
+    }
   }
 }
 
 // ------------------------------------------------------------------------------- dQ
 template <int DQK, int DV>
 struct DqSmem {
-  static constexpr int KB = kKN * DQK * 2;
-  static constexpr int VB = kKN * DV * 2;
+  static constexpr int KPC = DualPitch<DQK>::value, VPC = RowPitch<DV>::value;
+  static constexpr int KP = KPC * 16, VP = VPC * 16;
+  static constexpr int KB = kKN * KP, VB = kKN * VP;
   static constexpr int STAGE = KB + VB;
-  static constexpr int BYTES = 2 * STAGE;
+  static constexpr int NST = (4 * STAGE <= 148 * 1024) ? 4 : 3;
+  static constexpr int BYTES = NST * STAGE;
 };
 
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
 void bwd_dq_kernel(const BwdParams bp) {
   using SM = DqSmem<DQK, DV>;
-  using TK = SwizzledTile<DQK>;
-  using TV = SwizzledTile<DV>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnParams& p = bp.a;
 
@@ -388,7 +397,9 @@ void bwd_dq_kernel(const BwdParams bp) {
   const int q0 = qt * kQM;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 5, lq = l & 31;
+  const int grp = w >> 2;   // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   const int Nq = p.Nq, Nk = p.Nk, delta = Nk - Nq;
   const int qw = q0 + 32 * w;
   const int qrow = qw + lq;
@@ -399,44 +410,27 @@ void bwd_dq_kernel(const BwdParams bp) {
   const __bf16* DOg = (const __bf16*)bp.dout + b * bp.dos_b + h * bp.dos_h;
 
   // ---- key-tile sequence (same bands / lists as the forward)
+  TileSeq<kKN> seq;
+  seq.t_lo = 0;
+  seq.ent = (const uint32_t*)(smem + SM::BYTES + 16);
   const int mk = p.mask.kind;
-  int count, t_lo = 0, sub = 1, npart = 0, ncols = 0;
-  const int* pidx = nullptr;
-  const int* fidx = nullptr;
   if constexpr (!LISTS) {
     int lo = 0, hi = Nk;
     if (mk == kMaskCausal || mk == kMaskWindow) hi = min(Nk, q0 + kQM + delta);
     if (mk == kMaskPrefix) hi = min(Nk, max(p.mask.prefix, q0 + kQM + delta));
     if (mk == kMaskWindow) lo = max(0, q0 + delta - p.mask.window);
     hi = max(hi, 0);
-    t_lo = lo / kKN;
-    count = max(0, (hi + kKN - 1) / kKN - t_lo);
+    seq.t_lo = lo / kKN;
+    seq.count = max(0, (hi + kKN - 1) / kKN - seq.t_lo);
   } else {
-    const int qs = q0 / p.lists.tile_rows;
-    const int hm = (p.lists.heads == 1) ? 0 : h;
-    const int row = (b * p.lists.heads + hm) * p.lists.n_rows + qs;
-    ncols = p.lists.n_cols;
-    npart = clamp_count(p.lists.pcnt[row], ncols);
-    const int nfull = clamp_count(p.lists.fcnt[row], ncols);
-    pidx = p.lists.pidx + (int64_t)row * ncols;
-    fidx = p.lists.fidx + (int64_t)row * ncols;
-    sub = p.lists.tile_cols / kKN;
-    count = (npart + nfull) * sub;
+    const ListParams& L = p.lists;
+    const int64_t rbase = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h)) * L.n_rows;
+    const int64_t r0 = rbase + q0 / L.tile_rows;
+    const int64_t r1 = (q0 + kQM / 2 < Nq) ? rbase + (q0 + kQM / 2) / L.tile_rows : -1;
+    seq.count = build_tile_sequence<kThreads, kKN>(L, r0, r1, Nk, smem + SM::BYTES, tid);
   }
-  auto tile_at = [&](int it, int& n0, bool& partial) {
-    if constexpr (!LISTS) {
-      n0 = (t_lo + it) * kKN;
-      partial = false;
-    } else {
-      const int e = it / sub, s = it - e * sub;
-      int kt2;
-      if (e < npart) { kt2 = list_entry(pidx, e, ncols); partial = true; }
-      else { kt2 = list_entry(fidx, e - npart, ncols); partial = false; }
-      n0 = kt2 * sub * kKN + s * kKN;
-    }
-  };
 
-  // ---- Q and dO rows of this lane's query as B operands
+  // ---- Q and dO rows of this lane's query as B operands; lse2 and D of the row
   bf16x8 qf[DQK / 16], of[DV / 16];
 #pragma unroll
   for (int ks = 0; ks < DQK / 16; ++ks)
@@ -446,46 +440,10 @@ void bwd_dq_kernel(const BwdParams bp) {
     of[ks] = (qrow < Nq) ? *(const bf16x8*)(DOg + (int64_t)qrow * bp.dos_s + 16 * ks + 8 * g) : bf16x8{};
   float lse2 = __builtin_huge_valf(), ddv = 0.0f;
   if (qrow < Nq) {
-    const float ls = p.lse[((int64_t)b * p.H + h) * Nq + qrow];
-    lse2 = (ls == kNegInf) ? __builtin_huge_valf() : ls * kLog2e;
-    ddv = bp.dsum[((int64_t)b * p.H + h) * Nq + qrow];
+    const float* blk = bp.ws + ((int64_t)bh * bp.n_qblk + qrow / 64) * 128;
+    lse2 = blk[qrow % 64];
+    ddv = blk[64 + qrow % 64];
   }
-
-  constexpr int KCH = kKN * DQK / 8 / kThreads;
-  constexpr int VCH = kKN * DV / 8 / kThreads;
-  u32x4 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DQK / 8), col = c - row * (DQK / 8);
-      const int kk = n0 + row;
-      kreg[i] = (kk < Nk) ? *(const u32x4*)(Kg + (int64_t)kk * p.ks_s + col * 8) : u32x4{};
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DV / 8), col = c - row * (DV / 8);
-      const int kk = n0 + row;
-      vreg[i] = (kk < Nk) ? *(const u32x4*)(Vg + (int64_t)kk * p.vs_s + col * 8) : u32x4{};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* Kl = smem + buf * SM::STAGE;
-    char* Vl = Kl + SM::KB;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DQK / 8), col = c - row * (DQK / 8);
-      *(u32x4*)(Kl + TK::off(row, col * 8)) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (DV / 8), col = c - row * (DV / 8);
-      *(u32x4*)(Vl + TV::off(row, col * 8)) = vreg[i];
-    }
-  };
 
   f32x16 dq[DQK / 32];
 #pragma unroll
@@ -493,97 +451,135 @@ void bwd_dq_kernel(const BwdParams bp) {
   const int prow = swap_bits23(lq);
   const int trow = 8 * g + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const float c_eff = (SOFTCAP || BIAS) ? 1.0f : p.scale_log2;
 
-  if (count > 0) {
-    int n0;
-    bool part;
-    tile_at(0, n0, part);
-    load_tile(n0);
-    store_tile(0);
-    __syncthreads();
-  }
+  LdsDma<kKN, DQK, SM::KPC, kThreads> kdma;
+  LdsDma<kKN, DV, SM::VPC, kThreads> vdma;
+  kdma.init(p.ks_s, tid);
+  vdma.init(p.vs_s, tid);
+  zero_lds<kThreads>(smem, SM::BYTES, tid);   // rows past Nk are never loaded: keep them finite
+  auto issue_tile = [&](int t) {
+    const int n0 = seq.start(t, LISTS);
+    char* st = smem + (t % SM::NST) * SM::STAGE;
+    kdma.issue(Kg, p.ks_s, n0, Nk, st);
+    vdma.issue(Vg, p.vs_s, n0, Nk, st + SM::KB);
+  };
 
-  for (int it = 0; it < count; ++it) {
-    const int buf = it & 1;
-    int n0;
-    bool partial;
-    tile_at(it, n0, partial);
-    if (it + 1 < count) {
-      int n1;
-      bool p1;
-      tile_at(it + 1, n1, p1);
-      load_tile(n1);
-    }
-    const char* Kl = smem + buf * SM::STAGE;
-    const char* Vl = Kl + SM::KB;
+  f32x16 s[2], dp[2];
+  bf16x8 dsb[2][2];
+  const int T = seq.count;
+  const bool last_ragged = T > 0 && seq.start(T - 1, LISTS) + kKN > Nk;
+  for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_tile(t);
+  wait_all_vmem();
+  __syncthreads();
 
-    bool need = (n0 + kKN > Nk);
-    if constexpr (LISTS) {
-      need = need || partial;
-    } else {
-      const int last = n0 + kKN - 1;
-      if (mk == kMaskCausal) need = need || (last > qw + delta);
-      else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
-      else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
-      else if (mk == kMaskBlockDiag) need = true;
-    }
-
-    bf16x8 dsb[2][2];
+  // Phase ph = 0 .. 2T+1, local phase lp = ph - grp, as in the forward:
+  //   lp even: matrix phase: dQ^T += K(lp/2 - 1)^T dS^T, S^T, dP^T of tile lp/2
+  //   lp odd:  vector phase: P and dS of tile (lp-1)/2
+  for (int ph = 0; ph < 2 * T + 2; ++ph) {
+    if ((ph & 1) == 0 && ph / 2 + SM::NST - 2 < T) issue_tile(ph / 2 + SM::NST - 2);
+    const int lp = ph - grp;
+    if (lp >= 0 && (lp & 1) == 0) {
+      // ------------------------------------------------------------- matrix phase
+      const int ts = lp >> 1, tv = ts - 1;
+      if (tv >= 0) {
+        const char* Kl = smem + (tv % SM::NST) * SM::STAGE;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+        for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(Kl + TK::off(32 * kb + prow, 16 * ks + 8 * g));
-        s = mfma_bf16(a, qf[ks], s);
-      }
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(Vl + TV::off(32 * kb + prow, 16 * ks + 8 * g));
-        dp = mfma_bf16(a, of[ks], dp);
-      }
-      // reg r <-> key n0 + 32 kb + 16 (r/8) + 8 g + r % 8, query qrow
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float dsv[2];
-#pragma unroll
-          for (int z = 0; z < 2; ++z) {
-            const int r = 8 * hh + 2 * e + z;
-            const int kk = n0 + 32 * kb + 16 * hh + 8 * g + 2 * e + z;
-            float dcap;
-            float pr = recompute_p<SOFTCAP, BIAS>(s[r], p, qrow, kk, lse2, dcap);
-            if (need) {
-              bool vis = kk < Nk;
-              if (vis && qrow < Nq && (LISTS ? partial : true)) vis = mask_visible(p.mask, b, qrow, kk, Nq, Nk);
-              if (!vis) pr = 0.0f;
+            for (int hh = 0; hh < 2; ++hh) {
+              const char* kp = Kl + (32 * kb + 16 * hh + trow) * SM::KP + (32 * db + tcol) * 2;
+              const u32x2 lo = lds_read_tr(kp);
+              const u32x2 hi = lds_read_tr(kp + 4 * SM::KP);
+              dq[db] = mfma_bf16(join_bf16x8(lo, hi), dsb[kb][hh], dq[db]);
             }
-            dsv[z] = pr * (dp[r] - ddv) * dcap;
-          }
-          pk[e] = pack_bf16x2(dsv[0], dsv[1]);
-        }
-        dsb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
       }
-    }
-    // dQ^T += K^T dS^T
+      if (ts < T) {
+        const char* Kl = smem + (ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g;
+        const char* Vl = smem + (ts % SM::NST) * SM::STAGE + SM::KB + prow * SM::VP + 16 * g;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        dp[0] = f32x16{};
+        dp[1] = f32x16{};
 #pragma unroll
-    for (int db = 0; db < DQK / 32; ++db)
+        for (int ks = 0; ks < DQK / 16; ++ks) {
+          const bf16x8 a0 = *(const bf16x8*)(Kl + 32 * ks);
+          const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * SM::KP + 32 * ks);
+          s[0] = mfma_bf16(a0, qf[ks], s[0]);
+          s[1] = mfma_bf16(a1, qf[ks], s[1]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < DV / 16; ++ks) {
+          const bf16x8 a0 = *(const bf16x8*)(Vl + 32 * ks);
+          const bf16x8 a1 = *(const bf16x8*)(Vl + 32 * SM::VP + 32 * ks);
+          dp[0] = mfma_bf16(a0, of[ks], dp[0]);
+          dp[1] = mfma_bf16(a1, of[ks], dp[1]);
+        }
+      }
+    } else if (lp >= 0 && (lp >> 1) < T) {
+      // ------------------------------------------------------------- vector phase
+      const int ts = lp >> 1;
+      const int n0 = seq.start(ts, LISTS);
+      bool need = (n0 + kKN > Nk);
+      bool elem = true, hide = false;
+      if constexpr (LISTS) {
+        const uint32_t c = seq.cls(ts, grp, true);
+        hide = c == 0u;
+        elem = c == 1u;
+        need = need || c != 2u;
+      } else {
+        const int last = n0 + kKN - 1;
+        if (mk == kMaskCausal) need = need || (last > qw + delta);
+        else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
+        else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
+        else if (mk == kMaskBlockDiag) need = true;
+      }
+      // reg r of block kb holds key n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of row qrow
+      f32x16 dcap[2];
+      if constexpr (SOFTCAP || BIAS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float dc;
+            s[kb][r] = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qrow, n0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7), dc);
+            if constexpr (SOFTCAP) dcap[kb][r] = dc;
+          }
+      }
+      if (need) mask_tile(s, p.mask, b, qrow, n0 + 8 * g, Nq, Nk, elem && qrow < Nq, hide);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int r0 = 32 * kb + 16 * hh + trow;
-          const u32x2 lo = lds_read_tr(Kl + TK::off(r0, 32 * db + tcol));
-          const u32x2 hi = lds_read_tr(Kl + TK::off(r0 + 4, 32 * db + tcol));
-          dq[db] = mfma_bf16(join_bf16x8(lo, hi), dsb[kb][hh], dq[db]);
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float dsv[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const int r = 8 * hh + 2 * e + z;
+              const float pr = fast_exp2(__builtin_fmaf(s[kb][r], c_eff, -lse2));
+              float d = pr * (dp[kb][r] - ddv);
+              if constexpr (SOFTCAP) d *= dcap[kb][r];
+              dsv[z] = d;
+            }
+            pk[e] = pack_bf16x2(dsv[0], dsv[1]);
+          }
+          dsb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
         }
-
-    if (it + 1 < count) store_tile(buf ^ 1);
+    }
+    if (ph & 1) {
+      const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
+      const bool exact = later > 0 && !(last_ragged && (ph + 1) / 2 + later == T - 1);
+      if (exact) kdma.wait_leaving(vdma, later);
+      else wait_lds_dma();
+    }
     __syncthreads();
   }
 
+  // ---- epilogue: lane = query, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
   if (qrow < Nq) {
     __bf16* dQg = (__bf16*)bp.dq + b * bp.dqs_b + h * bp.dqs_h + (int64_t)qrow * bp.dqs_s;
 #pragma unroll
@@ -603,29 +599,31 @@ hipError_t record_stage(const BwdParams& bp, int i, hipStream_t st) {
   return hipEventRecord(static_cast<hipEvent_t>(bp.stage_events[i]), st);
 }
 
+int list_bytes(const ListParams& L, int unit) { return L.pcnt == nullptr ? 0 : tile_sequence_bytes(L, unit); }
+
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
-hipError_t launch_passes(const BwdParams& bp, const ListParams& tlists, hipStream_t st) {
+hipError_t launch_passes(const BwdParams& bp, hipStream_t st) {
   {
     hipError_t e0 = record_stage(bp, 1, st);
     if (e0 != hipSuccess) return e0;
     BwdParams kv = bp;
-    kv.a.lists = tlists;
+    kv.a.lists = bp.tlists;
     auto kern = bwd_dkdv_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
-    constexpr int smem_bytes = DkdvSmem<DQK, DV>::BYTES;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem_bytes);
+    const int bytes = DkdvSmem<DQK, DV>::BYTES + list_bytes(kv.a.lists, kQS);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(bp.grid_padded_kv), dim3(kThreads), smem_bytes, st, kv);
+    hipLaunchKernelGGL(kern, dim3(bp.grid_padded_kv), dim3(kThreads), bytes, st, kv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     auto kern = bwd_dq_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
-    constexpr int smem_bytes = DqSmem<DQK, DV>::BYTES;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem_bytes);
+    const int bytes = DqSmem<DQK, DV>::BYTES + list_bytes(bp.a.lists, kKN);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     e = record_stage(bp, 2, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(bp.a.grid_padded), dim3(kThreads), smem_bytes, st, bp);
+    hipLaunchKernelGGL(kern, dim3(bp.a.grid_padded), dim3(kThreads), bytes, st, bp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return record_stage(bp, 3, st);
@@ -633,19 +631,39 @@ hipError_t launch_passes(const BwdParams& bp, const ListParams& tlists, hipStrea
 }
 
 template <int DQK, int DV>
-hipError_t dispatch(const BwdParams& bp, const ListParams& tl, bool lists, bool softcap, bool bias, hipStream_t st) {
+hipError_t dispatch(const BwdParams& bp, bool lists, bool softcap, bool bias, hipStream_t st) {
   if (lists) {
-    if (softcap) return bias ? launch_passes<DQK, DV, true, true, true>(bp, tl, st) : launch_passes<DQK, DV, true, true, false>(bp, tl, st);
-    return bias ? launch_passes<DQK, DV, true, false, true>(bp, tl, st) : launch_passes<DQK, DV, true, false, false>(bp, tl, st);
+    if (softcap) return bias ? launch_passes<DQK, DV, true, true, true>(bp, st) : launch_passes<DQK, DV, true, true, false>(bp, st);
+    return bias ? launch_passes<DQK, DV, true, false, true>(bp, st) : launch_passes<DQK, DV, true, false, false>(bp, st);
   }
-  if (softcap) return bias ? launch_passes<DQK, DV, false, true, true>(bp, tl, st) : launch_passes<DQK, DV, false, true, false>(bp, tl, st);
-  return bias ? launch_passes<DQK, DV, false, false, true>(bp, tl, st) : launch_passes<DQK, DV, false, false, false>(bp, tl, st);
+  if (softcap) return bias ? launch_passes<DQK, DV, false, true, true>(bp, st) : launch_passes<DQK, DV, false, true, false>(bp, st);
+  return bias ? launch_passes<DQK, DV, false, false, true>(bp, st) : launch_passes<DQK, DV, false, false, false>(bp, st);
+}
+
+template <int DQK, int DV>
+bool lists_fit_dims(const ListParams& fwd, const ListParams& tr) {
+  return DkdvSmem<DQK, DV>::BYTES + list_bytes(tr, kQS) <= kMaxLdsBytes &&
+         DqSmem<DQK, DV>::BYTES + list_bytes(fwd, kKN) <= kMaxLdsBytes;
 }
 
 }  // namespace
 
-int bwd_q_block_rows() { return kQM; }
-int bwd_kv_block_rows() { return kBK; }
+int bwd_q_block_rows() { return kQM / 2; }
+int bwd_kv_block_rows() { return kKB; }
+
+size_t bwd_workspace_bytes(int B, int H, int Nq) {
+  const size_t nqb = (size_t)((Nq + 63) / 64);
+  return (size_t)B * H * nqb * 128 * sizeof(float) + 512;
+}
+
+bool bwd_lists_fit(int dqk, int dv, const ListParams& fwd, const ListParams& tr) {
+  if ((int64_t)fwd.n_cols * (fwd.tile_cols / kKN) > (1 << 20) || (int64_t)tr.n_cols * (tr.tile_cols / kQS) > (1 << 20))
+    return false;
+  if (dqk == 128 && dv == 128) return lists_fit_dims<128, 128>(fwd, tr);
+  if (dqk == 64 && dv == 64) return lists_fit_dims<64, 64>(fwd, tr);
+  if (dqk == 192 && dv == 128) return lists_fit_dims<192, 128>(fwd, tr);
+  return false;
+}
 
 // bp.a.lists holds the forward lists (per query tile, walked by the dQ pass) and
 // bp.tlists the transposed lists (per key tile, walked by the dK/dV pass).
@@ -654,19 +672,20 @@ hipError_t launch_bwd_bf16(BwdParams bp, int dqk, int dv, hipStream_t st) {
   p.n_tiles = (p.Nq + kQM - 1) / kQM;
   p.total_work = p.B * p.H * p.n_tiles;
   p.grid_padded = (p.total_work + 7) / 8 * 8;
-  bp.n_kv_tiles = (p.Nk + kBK - 1) / kBK;
+  bp.n_kv_tiles = (p.Nk + kKB - 1) / kKB;
   bp.total_work_kv = p.B * p.H * bp.n_kv_tiles;
   bp.grid_padded_kv = (bp.total_work_kv + 7) / 8 * 8;
+  bp.n_qblk = (p.Nq + 63) / 64;
 
   {
     hipError_t e0 = record_stage(bp, 0, st);
     if (e0 != hipSuccess) return e0;
     const int lpk = dv / 8;
-    const int64_t rows = (int64_t)p.B * p.H * p.Nq;
-    const int rows_per_blk = kThreads / lpk;
+    const int64_t rows = (int64_t)p.B * p.H * bp.n_qblk * 64;
+    const int rows_per_blk = kPreThreads / lpk;
     const unsigned nblk = (unsigned)((rows + rows_per_blk - 1) / rows_per_blk);
-    if (dv == 128) hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(nblk), dim3(kThreads), 0, st, bp);
-    else if (dv == 64) hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(nblk), dim3(kThreads), 0, st, bp);
+    if (dv == 128) hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(nblk), dim3(kPreThreads), 0, st, bp);
+    else if (dv == 64) hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(nblk), dim3(kPreThreads), 0, st, bp);
     else return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -674,10 +693,9 @@ hipError_t launch_bwd_bf16(BwdParams bp, int dqk, int dv, hipStream_t st) {
   const bool lists = p.lists.pcnt != nullptr;
   const bool softcap = p.softcap > 0.0f;
   const bool bias = p.bias_log2 != 0.0f;
-  const ListParams tl = bp.tlists;
-  if (dqk == 128 && dv == 128) return dispatch<128, 128>(bp, tl, lists, softcap, bias, st);
-  if (dqk == 64 && dv == 64) return dispatch<64, 64>(bp, tl, lists, softcap, bias, st);
-  if (dqk == 192 && dv == 128) return dispatch<192, 128>(bp, tl, lists, softcap, bias, st);
+  if (dqk == 128 && dv == 128) return dispatch<128, 128>(bp, lists, softcap, bias, st);
+  if (dqk == 64 && dv == 64) return dispatch<64, 64>(bp, lists, softcap, bias, st);
+  if (dqk == 192 && dv == 128) return dispatch<192, 128>(bp, lists, softcap, bias, st);
   return hipErrorInvalidValue;
 }
 

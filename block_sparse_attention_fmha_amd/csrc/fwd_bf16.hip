@@ -67,79 +67,6 @@ struct FwdSmem {
   static constexpr int BYTES = NST * STAGE;
 };
 
-// Key-tile sequence of one workgroup: the analytic band, or (block-sparse) entries in LDS
-// of the form (kernel tile << 4) | class bits, the class of query half hf (rows
-// 128 hf .. 128 hf + 127 of the workgroup) in bits 2 hf, 2 hf + 1: 1 = partial tile (element
-// mask applies), 2 = full tile, 0 = tile not listed for that half (all keys hidden).
-struct TileSeq {
-  int count;
-  int t_lo;                 // analytic: first tile
-  const uint32_t* ent;      // lists: LDS entries
-  __device__ __forceinline__ int n0(int it, bool lists) const {
-    return lists ? (int)(ent[it] >> 4) * kBN : (t_lo + it) * kBN;
-  }
-};
-
-// Merge the block-sparse rows that cover the workgroup's two 128-row halves into one
-// ascending key-tile sequence (sparse tile_m is a multiple of 128, so each half lies in
-// one sparse row). A column listed by both halves is visited once; a column listed as both
-// partial and full for one row counts as full. List entries outside [0, n_cols) and kernel
-// tiles that start at or past Nk are dropped. `cls` needs ceil(n_cols / 4) words and `ent`
-// n_cols * (tile_cols / 64) words of LDS. Returns the sequence length (same in every thread).
-template <int NTHREADS>
-__device__ int build_tile_sequence(const ListParams& L, int b, int h, int q0, int nq, int nk,
-                                   uint32_t* cls, uint32_t* ent, int* total, int tid) {
-  const int ncw = (L.n_cols + 3) >> 2;
-  for (int i = tid; i < ncw; i += NTHREADS) cls[i] = 0u;
-  __syncthreads();
-  const int hm = (L.heads == 1) ? 0 : h;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int qr = q0 + 128 * hf;
-    if (qr >= nq) break;
-    const int64_t row = ((int64_t)b * L.heads + hm) * L.n_rows + qr / L.tile_rows;
-#pragma unroll
-    for (int kind = 0; kind < 2; ++kind) {   // 0: partial list, 1: full list
-      const int cnt = clamp_count((kind ? L.fcnt : L.pcnt)[row], L.n_cols);
-      const int* idx = (kind ? L.fidx : L.pidx) + row * L.n_cols;
-      const uint32_t code = (kind ? 2u : 1u) << (2 * hf);
-      for (int e = tid; e < cnt; e += NTHREADS) {
-        const int c = idx[e];
-        if (c >= 0 && c < L.n_cols) atomicOr(&cls[c >> 2], code << (8 * (c & 3)));
-      }
-    }
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int sub = L.tile_cols / kBN;
-    const int nkt = (nk + kBN - 1) / kBN;   // kernel tiles holding at least one key
-    int base = 0;
-    for (int c0 = 0; c0 < L.n_cols; c0 += 64) {
-      const int c = c0 + tid;
-      uint32_t v = c < L.n_cols ? (cls[c >> 2] >> (8 * (c & 3))) & 15u : 0u;
-      v = v & ~((v & 10u) >> 1);   // partial and full for the same half: full
-      const uint64_t m = __builtin_amdgcn_ballot_w64(v != 0u);
-      const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if (v != 0u) {
-        // the tiles of one column are consecutive slots, so the sequence stays ascending
-        for (int s = 0; s < sub; ++s) {
-          const int kt = c * sub + s;
-          if (kt < nkt) ent[(base + pre) * sub + s] = ((uint32_t)kt << 4) | v;
-        }
-      }
-      base += __builtin_popcountll(m);
-    }
-    if (tid == 0) {
-      // only the last column can hold tiles at or past Nk
-      const int cl = L.n_cols - 1;
-      const bool last_listed = cl >= 0 && ((cls[cl >> 2] >> (8 * (cl & 3))) & 15u) != 0u;
-      *total = base * sub - (last_listed ? L.n_cols * sub - nkt : 0);
-    }
-  }
-  __syncthreads();
-  return *total;
-}
-
 // Max of the 32 S^T entries of a lane as a depth-4 tree of v_max3.
 __device__ __forceinline__ float tree_max32(const f32x16 (&s)[2]) {
   float a[11];
@@ -152,56 +79,6 @@ __device__ __forceinline__ float tree_max32(const f32x16 (&s)[2]) {
   const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
   const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
   return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
-}
-
-// Visible keys of query row i under the band masks (none, causal, sliding window,
-// prefix-LM) form one interval [lo, hi); block-diagonal is handled separately.
-__device__ __forceinline__ void band_interval(const MaskParams& m, int i, int nq, int nk, int& lo, int& hi) {
-  const int d = nk - nq;
-  lo = 0;
-  hi = nk;
-  if (m.kind == kMaskCausal || m.kind == kMaskWindow) hi = min(nk, i + d + 1);
-  if (m.kind == kMaskWindow) lo = i + d - m.window;
-  if (m.kind == kMaskPrefix) hi = min(nk, max(m.prefix, i + d + 1));
-}
-
-// Set to -inf the S^T entries whose key is hidden from the lane's query row. Register r
-// of block kb holds key kbase + 32 kb + 16 (r / 8) + r % 8 (kbase = tile start + 8 g).
-// `elem` = apply the element mask (else only keys past Nk are hidden); `hide` = hide all.
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const MaskParams& m, int b, int qrow, int kbase,
-                                          int nq, int nk, bool elem, bool hide) {
-  if (hide) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = kNegInf;
-    return;
-  }
-  if (elem && m.kind == kMaskBlockDiag) {
-    const int dq = m.doc_q[(int64_t)b * nq + qrow];
-    const int* dk = m.doc_k + (int64_t)b * nk;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kbase + 32 * kb + 16 * (r >> 3) + (r & 7);
-        const bool vis = j < nk && dk[min(j, nk - 1)] == dq;
-        s[kb][r] = vis ? s[kb][r] : kNegInf;
-      }
-    return;
-  }
-  int lo = 0, hi = nk;
-  if (elem) band_interval(m, qrow, nq, nk, lo, hi);
-  // key j visible iff lo <= j < hi, i.e. (unsigned)(j - lo) < (unsigned)(hi - lo)
-  const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
-  const int base = kbase - lo;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const unsigned rel = (unsigned)(base + 32 * kb + 16 * (r >> 3) + (r & 7));
-      s[kb][r] = rel < span ? s[kb][r] : kNegInf;
-    }
 }
 
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
@@ -227,7 +104,7 @@ void fwd_bf16_kernel(const AttnParams p) {
   const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + h * p.vs_h;
 
   // ---- tile sequence
-  TileSeq seq;
+  TileSeq<kBN> seq;
   seq.t_lo = 0;
   seq.ent = (const uint32_t*)(smem + SM::BYTES + 16);
   const int mk = p.mask.kind;
@@ -241,9 +118,12 @@ void fwd_bf16_kernel(const AttnParams p) {
     seq.t_lo = tlo;
     seq.count = max(0, thi - tlo);
   } else {
-    uint32_t* ent = (uint32_t*)(smem + SM::BYTES + 16);
-    uint32_t* cls = ent + p.lists.n_cols * (p.lists.tile_cols / kBN);
-    seq.count = build_tile_sequence<kThreads>(p.lists, b, h, q0, Nq, Nk, cls, ent, (int*)(smem + SM::BYTES), tid);
+    // the two 128-row halves of the workgroup each lie in one sparse row
+    const ListParams& L = p.lists;
+    const int64_t rbase = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h)) * L.n_rows;
+    const int64_t r0 = rbase + q0 / L.tile_rows;
+    const int64_t r1 = (q0 + kBM / 2 < Nq) ? rbase + (q0 + kBM / 2) / L.tile_rows : -1;
+    seq.count = build_tile_sequence<kThreads, kBN>(L, r0, r1, Nk, smem + SM::BYTES, tid);
   }
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the whole pass
@@ -273,7 +153,7 @@ void fwd_bf16_kernel(const AttnParams p) {
   vdma.init(p.vs_s, tid);
   zero_lds<kThreads>(smem, SM::BYTES, tid);   // rows past Nk are never loaded: keep them finite
   auto issue_tile = [&](int t) {
-    const int n0 = seq.n0(t, LISTS);
+    const int n0 = seq.start(t, LISTS);
     char* st = smem + (t % SM::NST) * SM::STAGE;
     kdma.issue(Kg, p.ks_s, n0, Nk, st);
     vdma.issue(Vg, p.vs_s, n0, Nk, st + SM::KB);
@@ -283,7 +163,7 @@ void fwd_bf16_kernel(const AttnParams p) {
   bf16x8 pb[2][2];
   const int T = seq.count;
   // only the tile holding key Nk - 1 can be ragged, and it is always the last of the sequence
-  const bool last_ragged = T > 0 && seq.n0(T - 1, LISTS) + kBN > Nk;
+  const bool last_ragged = T > 0 && seq.start(T - 1, LISTS) + kBN > Nk;
   for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_tile(t);
   wait_all_vmem();   // Q fragments and the first tiles
   __syncthreads();
@@ -334,11 +214,11 @@ void fwd_bf16_kernel(const AttnParams p) {
     } else if (lp >= 0 && (lp >> 1) < T) {
       // ------------------------------------------------------------- vector phase
       const int ts = lp >> 1;
-      const int n0 = seq.n0(ts, LISTS);
+      const int n0 = seq.start(ts, LISTS);
       bool need = (n0 + kBN > Nk);
       bool elem = true, hide = false;
       if constexpr (LISTS) {
-        const uint32_t c = (seq.ent[ts] >> (2 * grp)) & 3u;   // this wave's query half
+        const uint32_t c = seq.cls(ts, grp, true);   // this wave's query half
         hide = c == 0u;
         elem = c == 1u;
         need = need || c != 2u;
@@ -431,10 +311,7 @@ void fwd_bf16_kernel(const AttnParams p) {
 }
 
 // LDS bytes beyond the K/V stages for the block-sparse tile sequence (0 without lists).
-int list_bytes(const ListParams& L) {
-  if (L.pcnt == nullptr) return 0;
-  return 16 + 4 * (L.n_cols * (L.tile_cols / kBN) + (L.n_cols + 3) / 4);
-}
+int list_bytes(const ListParams& L) { return L.pcnt == nullptr ? 0 : tile_sequence_bytes(L, kBN); }
 
 template <int DQK, int DV>
 int smem_bytes(const ListParams& L) { return FwdSmem<DQK, DV>::BYTES + list_bytes(L); }

@@ -81,7 +81,10 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;        // workspace: D_i = sum_d dO_id O_id, [B, H, Nq] fp32
+  float* ws;          // workspace: per (b, h) and 64-query block, 64 x lse2 then 64 x D
+                      // (lse2 = LSE log2(e), +inf for empty rows and rows past Nq;
+                      // D_i = sum_d dO_id O_id, 0 past Nq), plus 512 bytes of tail padding
+  int n_qblk;         // 64-query blocks per (b, h): ceil(Nq / 64)
   int64_t dos_b, dos_s, dos_h, dqs_b, dqs_s, dqs_h, dks_b, dks_s, dks_h, dvs_b, dvs_s, dvs_h;
   ListParams tlists;  // transposed block-sparse lists (per key tile) for the dK/dV pass
   void* const* stage_events;  // optional host array of 4 hipEvent_t (host side only)
@@ -156,20 +159,29 @@ __device__ __forceinline__ int list_entry(const int* idx, int e, int n_cols) {
 }
 
 // Score transform applied to the scaled score x = scale * <q, k> (softcap, then bias).
-// Returns the final score in log2 units.
+// Returns the final score in log2 units; `dcap` receives d(softcap(x))/dx = 1 - tanh^2
+// (1 without softcap), the factor the backward applies to dS.
 template <bool SOFTCAP, bool BIAS>
-__device__ __forceinline__ float score_log2(float raw, const AttnParams& p, int i, int j) {
+__device__ __forceinline__ float score_log2_d(float raw, const AttnParams& p, int i, int j, float& dcap) {
   float x = raw * p.scale;
+  dcap = 1.0f;
   if constexpr (SOFTCAP) {
     // tanh(y) = 1 - 2 / (exp(2 y) + 1), y = x / softcap
     const float e = fast_exp2(x * (2.0f * kLog2e / p.softcap));
-    x = p.softcap * (1.0f - 2.0f * fast_rcp(e + 1.0f));
+    const float th = 1.0f - 2.0f * fast_rcp(e + 1.0f);
+    x = p.softcap * th;
+    dcap = 1.0f - th * th;
   }
   float u = x * kLog2e;
   if constexpr (BIAS) u += p.bias_log2 * (float)abs(i - j);
   return u;
 }
 
+template <bool SOFTCAP, bool BIAS>
+__device__ __forceinline__ float score_log2(float raw, const AttnParams& p, int i, int j) {
+  float dcap;
+  return score_log2_d<SOFTCAP, BIAS>(raw, p, i, j, dcap);
+}
 
 // MFMA row permutation: swapping bits 2 and 3 of the A-operand row index makes the C
 // registers 8 r' + i (i = 0..7) of lane half g hold rows 16 r' + 8 g + i, i.e. 8
@@ -178,30 +190,6 @@ __device__ __forceinline__ float score_log2(float raw, const AttnParams& p, int 
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-
-// Row-major bf16 tile in LDS with an XOR swizzle of its 16-byte chunks, so that both
-// access patterns used on the same tile are bank-conflict free without padding:
-//   * 16-byte reads of one chunk column from 16 consecutive rows (MFMA rows), and
-//   * transposed 8-byte reads of 4 consecutive rows x 32 bytes (ds_read_b64_tr_b16).
-// Chunk c of row r is stored at chunk (c & ~(S-1)) | ((c ^ f(r)) & (S-1)), S = 16 when the
-// row has a multiple of 16 chunks (else 8), f(r) = 2 (r mod S/2) + (r / (S/2)) mod 2.
-template <int D>
-struct SwizzledTile {
-  static constexpr int CH = D / 8;
-  static constexpr int S = (CH % 16 == 0) ? 16 : 8;
-  static constexpr int ROW_BYTES = D * 2;
-  __device__ static __forceinline__ int f(int r) {
-    return ((r & (S / 2 - 1)) << 1) | ((r / (S / 2)) & 1);
-  }
-  // physical chunk of logical chunk c in row r (an involution for fixed r)
-  __device__ static __forceinline__ int chunk(int r, int c) {
-    return (c & ~(S - 1)) | ((c ^ f(r)) & (S - 1));
-  }
-  // byte offset of element `col` (a multiple of 4) of row r
-  __device__ static __forceinline__ int off(int r, int col) {
-    return r * ROW_BYTES + chunk(r, col >> 3) * 16 + (col & 7) * 2;
-  }
-};
 
 // One direct global->LDS load of 16 bytes per lane: lane i copies gbase + voff (bytes) to
 // LDS bytes lds_block + 16 i. Issued through inline asm on purpose: the compiler would
@@ -217,6 +205,22 @@ __device__ __forceinline__ void dma_16b(const char* gbase, uint32_t voff, const 
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(gbase), "s"(laddr) : "memory");
 #endif
+}
+
+// s_waitcnt vmcnt(n) for a run-time n (wave-uniform); n above 15 waits for 15, which is
+// stricter and therefore still correct.
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+  switch (n) {
+#define FMHA_VMCNT_CASE(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    FMHA_VMCNT_CASE(1) FMHA_VMCNT_CASE(2) FMHA_VMCNT_CASE(3) FMHA_VMCNT_CASE(4) FMHA_VMCNT_CASE(5)
+    FMHA_VMCNT_CASE(6) FMHA_VMCNT_CASE(7) FMHA_VMCNT_CASE(8) FMHA_VMCNT_CASE(9) FMHA_VMCNT_CASE(10)
+    FMHA_VMCNT_CASE(11) FMHA_VMCNT_CASE(12) FMHA_VMCNT_CASE(13) FMHA_VMCNT_CASE(14)
+#undef FMHA_VMCNT_CASE
+    default:
+      if (n >= 15) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      break;
+  }
 }
 
 // Copies rows [row0, row0 + ROWS) of a row-strided bf16 matrix (D columns) into an LDS
@@ -256,18 +260,10 @@ struct LdsDma {
   // number of DMA instructions this wave issues per tile
   __device__ __forceinline__ int count() const { return (NBLK - w + NW - 1) / NW; }
   // wait until at most `tiles` tiles' worth of this wave's DMA (of this and `other`)
-  // remain in flight (loads complete in order); `tiles` is 1 or 2
+  // remain in flight (loads complete in order)
   template <class Other>
   __device__ __forceinline__ void wait_leaving(const Other& other, int tiles) const {
-    const int n = tiles * (count() + other.count());
-    switch (n) {
-      case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-      case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-      case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-      case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-      case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
+    wait_vmcnt_at_most(tiles * (count() + other.count()));
   }
   __device__ __forceinline__ void issue(const __bf16* g, int64_t row_stride, int row0, int nrows,
                                         char* lds_tile) const {
@@ -335,6 +331,11 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+__device__ __forceinline__ void bf16x2_to_f32(uint32_t x, float* f) {
+  f[0] = __uint_as_float(x << 16);
+  f[1] = __uint_as_float(x & 0xFFFF0000u);
+}
+
 __device__ __forceinline__ void bf16x8_to_f32(const u32x4& x, float* f) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -342,5 +343,147 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4& x, float* f) {
     f[2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
   }
 }
+
+// Visible keys of query row i under the band masks (none, causal, sliding window,
+// prefix-LM) form one interval [lo, hi); block-diagonal is handled separately.
+__device__ __forceinline__ void band_interval(const MaskParams& m, int i, int nq, int nk, int& lo, int& hi) {
+  const int d = nk - nq;
+  lo = 0;
+  hi = nk;
+  if (m.kind == kMaskCausal || m.kind == kMaskWindow) hi = min(nk, i + d + 1);
+  if (m.kind == kMaskWindow) lo = i + d - m.window;
+  if (m.kind == kMaskPrefix) hi = min(nk, max(m.prefix, i + d + 1));
+}
+
+// Set to -inf the entries of a 32-query x 64-key S^T tile (lane = query row, the layout of
+// S^T = K Q^T with permuted K rows) whose key is hidden from the lane's query row.
+// Register r of block kb holds key kbase + 32 kb + 16 (r / 8) + r % 8 (kbase = tile start
+// + 8 g).
+// `elem` = apply the element mask (else only keys past Nk are hidden); `hide` = hide all.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const MaskParams& m, int b, int qrow, int kbase,
+                                          int nq, int nk, bool elem, bool hide) {
+  if (hide) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = kNegInf;
+    return;
+  }
+  if (elem && m.kind == kMaskBlockDiag) {
+    const int dq = m.doc_q[(int64_t)b * nq + qrow];
+    const int* dk = m.doc_k + (int64_t)b * nk;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kbase + 32 * kb + 16 * (r >> 3) + (r & 7);
+        const bool vis = j < nk && dk[min(j, nk - 1)] == dq;
+        s[kb][r] = vis ? s[kb][r] : kNegInf;
+      }
+    return;
+  }
+  int lo = 0, hi = nk;
+  if (elem) band_interval(m, qrow, nq, nk, lo, hi);
+  // key j visible iff lo <= j < hi, i.e. (unsigned)(j - lo) < (unsigned)(hi - lo)
+  const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
+  const int base = kbase - lo;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const unsigned rel = (unsigned)(base + 32 * kb + 16 * (r >> 3) + (r & 7));
+      s[kb][r] = rel < span ? s[kb][r] : kNegInf;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Block-sparse tile sequences.
+//
+// A workgroup walks the tiles of one or two sparse rows (its "halves": the forward and
+// dQ passes cover 256 query rows = two 128-row halves, the dK/dV pass one row of keys).
+// The listed columns of those rows are merged into one ascending sequence of UNIT-wide
+// kernel tiles in LDS. Entry = (kernel tile << 4) | class bits, the class of half hf in
+// bits 2 hf, 2 hf + 1: 1 = partial (element mask applies), 2 = full, 0 = not listed for
+// that half (all of its elements hidden). Lists are sets: a repeated entry counts once, a
+// column listed both partial and full is full, entries outside [0, n_cols) are dropped,
+// and so are kernel tiles at or past n_elems (the column side's length).
+
+// LDS bytes of a merged sequence: count word (16 bytes), entries, class words.
+__host__ __device__ inline int tile_sequence_bytes(const ListParams& L, int unit) {
+  return 16 + 4 * (L.n_cols * (L.tile_cols / unit) + (L.n_cols + 3) / 4);
+}
+
+// row0 / row1: flattened index into the [B, heads, n_rows] count arrays of each half, or
+// -1 for an absent half. `lds` points at tile_sequence_bytes(L, UNIT) bytes. Contains
+// barriers: every thread of the workgroup must call it. Returns the sequence length.
+template <int NTHREADS, int UNIT>
+__device__ int build_tile_sequence(const ListParams& L, int64_t row0, int64_t row1, int n_elems, char* lds,
+                                   int tid) {
+  int* total = (int*)lds;
+  uint32_t* ent = (uint32_t*)(lds + 16);
+  const int sub = L.tile_cols / UNIT;
+  uint32_t* cls = ent + L.n_cols * sub;
+  const int ncw = (L.n_cols + 3) >> 2;
+  for (int i = tid; i < ncw; i += NTHREADS) cls[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int64_t row = hf ? row1 : row0;
+    if (row < 0) continue;
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {   // 0: partial list, 1: full list
+      const int cnt = clamp_count((kind ? L.fcnt : L.pcnt)[row], L.n_cols);
+      const int* idx = (kind ? L.fidx : L.pidx) + row * L.n_cols;
+      const uint32_t code = (kind ? 2u : 1u) << (2 * hf);
+      for (int e = tid; e < cnt; e += NTHREADS) {
+        const int c = idx[e];
+        if (c >= 0 && c < L.n_cols) atomicOr(&cls[c >> 2], code << (8 * (c & 3)));
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int nkt = (n_elems + UNIT - 1) / UNIT;   // kernel tiles holding at least one element
+    int base = 0;
+    for (int c0 = 0; c0 < L.n_cols; c0 += 64) {
+      const int c = c0 + tid;
+      uint32_t v = c < L.n_cols ? (cls[c >> 2] >> (8 * (c & 3))) & 15u : 0u;
+      v = v & ~((v & 10u) >> 1);   // partial and full for the same half: full
+      const uint64_t m = __builtin_amdgcn_ballot_w64(v != 0u);
+      const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (v != 0u) {
+        // the kernel tiles of one column are consecutive slots: the sequence stays ascending
+        for (int s = 0; s < sub; ++s) {
+          const int kt = c * sub + s;
+          if (kt < nkt) ent[(base + pre) * sub + s] = ((uint32_t)kt << 4) | v;
+        }
+      }
+      base += __builtin_popcountll(m);
+    }
+    if (tid == 0) {
+      // only the last column can hold kernel tiles at or past n_elems
+      const int cl = L.n_cols - 1;
+      const bool last_listed = cl >= 0 && ((cls[cl >> 2] >> (8 * (cl & 3))) & 15u) != 0u;
+      *total = base * sub - (last_listed ? L.n_cols * sub - nkt : 0);
+    }
+  }
+  __syncthreads();
+  return *total;
+}
+
+// Key / query tile walk of one workgroup: an analytic run of tiles, or a merged sequence.
+template <int UNIT>
+struct TileSeq {
+  int count;
+  int t_lo;               // analytic: first tile
+  const uint32_t* ent;    // lists: LDS entries
+  __device__ __forceinline__ int start(int it, bool lists) const {
+    return lists ? (int)(ent[it] >> 4) * UNIT : (t_lo + it) * UNIT;
+  }
+  // class bits (2) of half hf; analytic walks report "full" (masking is decided by range)
+  __device__ __forceinline__ uint32_t cls(int it, int hf, bool lists) const {
+    return lists ? (ent[it] >> (2 * hf)) & 3u : 2u;
+  }
+};
 
 }  // namespace fmha

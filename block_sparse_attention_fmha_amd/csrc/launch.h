@@ -26,8 +26,11 @@ hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, void* ws, hipStre
 
 // bf16 backward: preprocess, dK/dV pass, dQ pass.
 hipError_t launch_bwd_bf16(BwdParams p, int dqk, int dv, hipStream_t st);
-int bwd_q_block_rows();      // query rows per dQ workgroup / per dK/dV inner step
-int bwd_kv_block_rows();     // key rows per dK/dV workgroup / per dQ inner step
+int bwd_q_block_rows();      // block-sparse tile_m must be a multiple (one sparse row per dQ half-workgroup)
+int bwd_kv_block_rows();     // block-sparse tile_n must be a multiple (one sparse row per dK/dV workgroup)
+size_t bwd_workspace_bytes(int B, int H, int Nq);
+// Whether the merged tile sequences of both list orientations fit the kernels' LDS.
+bool bwd_lists_fit(int dqk, int dv, const ListParams& fwd, const ListParams& tr);
 
 // Block-mask builder: forward lists (per query tile) and transposed lists (per key tile).
 struct BlockMaskOut {
