@@ -24,9 +24,11 @@
 //      forward. S and dP come out with ONE KEY PER LANE and 8 consecutive queries per
 //      register group, which is the B operand of the dV / dK products as is; dO^T / Q^T
 //      come from transposed LDS reads;
-//   3. dQ pass: the forward's structure (256 queries per workgroup, 8 waves ping-ponging
-//      on 64-key tiles in 4 LDS stages): S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with
-//      K^T from transposed LDS reads.
+//   3. dQ pass: a workgroup owns 128 queries and walks 64-key tiles of K / V (direct
+//      global->LDS loads, 3-4 stages), again in wave pairs sharing 32 queries: the "S wave"
+//      holds Q, computes S^T = K Q^T and P and hands P over; the "dQ wave" holds dO,
+//      computes dP^T = V dO^T and dS, and accumulates dQ^T += K^T dS^T (K^T from
+//      transposed LDS reads). Lane = query in both, as in the forward.
 // The dQ pass recomputes S and dP (7 matrix products instead of 5): that is the price
 // of determinism without atomics.
 //
@@ -42,7 +44,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kKB = 128;     // keys per dK/dV workgroup: 4 wave pairs x 32 keys
 constexpr int kQS = 64;      // queries per dK/dV step
-constexpr int kQM = 256;     // queries per dQ workgroup: 8 waves x 32
+constexpr int kQM = 128;     // queries per dQ workgroup: 4 wave pairs x 32
 constexpr int kKN = 64;      // keys per dQ step
 constexpr int kPreThreads = 256;
 
@@ -256,10 +258,40 @@ void bwd_dkdv_kernel(const BwdParams bp) {
         const char* Rl = Ss + (role ? SM::QB : 0);
         dkdv_matrix<DQK, DQK, SM::QP, SM::QP>(Tl, Rl, tv >= 0, ts < T, acc, bop, s, bf, trow, tcol, prow, g);
       } else {
-        if (role == 0)
-          dkdv_matrix<DQK, DV, SM::QP, SM::OP>(Sv + SM::QB, Ss, tv >= 0, ts < T, acc, bop, s, bf, trow, tcol, prow, g);
-        else
-          dkdv_matrix<DV, DQK, SM::OP, SM::QP>(Sv, Ss + SM::QB, tv >= 0, ts < T, acc, bop, s, bf, trow, tcol, prow, g);
+        // one code path for both roles (two inlined variants would not fit the registers):
+        // wave-uniform widths and pitches, loops bounded by the wider head
+        const char* Tl = role ? Sv : Sv + SM::QB;
+        const char* Rl = role ? Ss + SM::QB : Ss;
+        const int tp = role ? SM::QP : SM::OP, rp = role ? SM::OP : SM::QP;
+        const int na = (role ? DQK : DV) / 32, nr = (role ? DV : DQK) / 16;
+        if (tv >= 0) {
+#pragma unroll
+          for (int db = 0; db < DM / 32; ++db) {
+            if (db >= na) break;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const char* tq = Tl + (32 * kb + 16 * hh + trow) * tp + (32 * db + tcol) * 2;
+                const u32x2 lo = lds_read_tr(tq);
+                const u32x2 hi = lds_read_tr(tq + 4 * tp);
+                acc[db] = mfma_bf16(join_bf16x8(lo, hi), bop[kb][hh], acc[db]);
+              }
+          }
+        }
+        if (ts < T) {
+          const char* rq = Rl + prow * rp + 16 * g;
+          s[0] = f32x16{};
+          s[1] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < DM / 16; ++ks) {
+            if (ks >= nr) break;
+            const bf16x8 a0 = *(const bf16x8*)(rq + 32 * ks);
+            const bf16x8 a1 = *(const bf16x8*)(rq + 32 * rp + 32 * ks);
+            s[0] = mfma_bf16(a0, bf[ks], s[0]);
+            s[1] = mfma_bf16(a1, bf[ks], s[1]);
+          }
+        }
       }
     } else if (lp >= 0 && (lp >> 1) < T) {
       // ------------------------------------------------------------- vector phase
@@ -371,20 +403,23 @@ void bwd_dkdv_kernel(const BwdParams bp) {
 }
 
 // ------------------------------------------------------------------------------- dQ
-template <int DQK, int DV>
+template <int DQK, int DV, bool LISTS>
 struct DqSmem {
   static constexpr int KPC = DualPitch<DQK>::value, VPC = RowPitch<DV>::value;
   static constexpr int KP = KPC * 16, VP = VPC * 16;
   static constexpr int KB = kKN * KP, VB = kKN * VP;
   static constexpr int STAGE = KB + VB;
-  static constexpr int NST = (4 * STAGE <= 148 * 1024) ? 4 : 3;
-  static constexpr int BYTES = NST * STAGE;
+  static constexpr int XB = 4 * 64 * 64;               // P hand-over: 4 pairs x 64 lanes x 64 B
+  // 4 stages when they fit next to the hand-over buffer (and the list sequence)
+  static constexpr int NST = (4 * STAGE + XB <= (LISTS ? 148 : 160) * 1024) ? 4 : 3;
+  static constexpr int BYTES = NST * STAGE + XB;
 };
 
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
 void bwd_dq_kernel(const BwdParams bp) {
-  using SM = DqSmem<DQK, DV>;
+  using SM = DqSmem<DQK, DV, LISTS>;
+  constexpr int DM = DQK > DV ? DQK : DV;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnParams& p = bp.a;
 
@@ -399,9 +434,10 @@ void bwd_dq_kernel(const BwdParams bp) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 5, lq = l & 31;
-  const int grp = w >> 2;   // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
+  const int role = w >> 2;     // 0: S wave (Q; S^T, P), 1: dQ wave (dO; dP^T, dS, dQ^T)
+  const int pair = w & 3;      // waves w and w + 4 share a SIMD and the same 32 queries
   const int Nq = p.Nq, Nk = p.Nk, delta = Nk - Nq;
-  const int qw = q0 + 32 * w;
+  const int qw = q0 + 32 * pair;
   const int qrow = qw + lq;
 
   const __bf16* Qg = (const __bf16*)p.q + b * p.qs_b + h * p.qs_h;
@@ -423,27 +459,24 @@ void bwd_dq_kernel(const BwdParams bp) {
     seq.t_lo = lo / kKN;
     seq.count = max(0, (hi + kKN - 1) / kKN - seq.t_lo);
   } else {
-    const ListParams& L = p.lists;
-    const int64_t rbase = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h)) * L.n_rows;
-    const int64_t r0 = rbase + q0 / L.tile_rows;
-    const int64_t r1 = (q0 + kQM / 2 < Nq) ? rbase + (q0 + kQM / 2) / L.tile_rows : -1;
-    seq.count = build_tile_sequence<kThreads, kKN>(L, r0, r1, Nk, smem + SM::BYTES, tid);
+    const ListParams& L = p.lists;   // the workgroup's 128 queries lie in one sparse row
+    const int64_t row = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h)) * L.n_rows + q0 / L.tile_rows;
+    seq.count = build_tile_sequence<kThreads, kKN>(L, row, -1, Nk, smem + SM::BYTES, tid);
   }
 
-  // ---- Q and dO rows of this lane's query as B operands; lse2 and D of the row
-  bf16x8 qf[DQK / 16], of[DV / 16];
+  // ---- B operand of this wave's S^T (Q) or dP^T (dO): the lane's query, k-slot = head dim
+  bf16x8 bf[DM / 16];
+  {
+    const __bf16* src = role ? DOg : Qg;
+    const int64_t st = role ? bp.dos_s : p.qs_s;
+    const int dr = role ? DV : DQK;
 #pragma unroll
-  for (int ks = 0; ks < DQK / 16; ++ks)
-    qf[ks] = (qrow < Nq) ? *(const bf16x8*)(Qg + (int64_t)qrow * p.qs_s + 16 * ks + 8 * g) : bf16x8{};
-#pragma unroll
-  for (int ks = 0; ks < DV / 16; ++ks)
-    of[ks] = (qrow < Nq) ? *(const bf16x8*)(DOg + (int64_t)qrow * bp.dos_s + 16 * ks + 8 * g) : bf16x8{};
-  float lse2 = __builtin_huge_valf(), ddv = 0.0f;
-  if (qrow < Nq) {
-    const float* blk = bp.ws + ((int64_t)bh * bp.n_qblk + qrow / 64) * 128;
-    lse2 = blk[qrow % 64];
-    ddv = blk[64 + qrow % 64];
+    for (int ks = 0; ks < DM / 16; ++ks)
+      bf[ks] = (16 * ks < dr && qrow < Nq) ? *(const bf16x8*)(src + (int64_t)qrow * st + 16 * ks + 8 * g) : bf16x8{};
   }
+  // lse2 (S wave) or D (dQ wave) of the lane's query
+  float rowv = role ? 0.0f : __builtin_huge_valf();
+  if (qrow < Nq) rowv = bp.ws[((int64_t)bh * bp.n_qblk + qrow / 64) * 128 + (role ? 64 : 0) + qrow % 64];
 
   f32x16 dq[DQK / 32];
 #pragma unroll
@@ -452,12 +485,13 @@ void bwd_dq_kernel(const BwdParams bp) {
   const int trow = 8 * g + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
   const float c_eff = (SOFTCAP || BIAS) ? 1.0f : p.scale_log2;
+  u32x4* xch = (u32x4*)(smem + SM::NST * SM::STAGE + pair * 4096) + l;   // + 64 i
 
   LdsDma<kKN, DQK, SM::KPC, kThreads> kdma;
   LdsDma<kKN, DV, SM::VPC, kThreads> vdma;
   kdma.init(p.ks_s, tid);
   vdma.init(p.vs_s, tid);
-  zero_lds<kThreads>(smem, SM::BYTES, tid);   // rows past Nk are never loaded: keep them finite
+  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // rows past Nk are never loaded: keep them finite
   auto issue_tile = [&](int t) {
     const int n0 = seq.start(t, LISTS);
     char* st = smem + (t % SM::NST) * SM::STAGE;
@@ -465,7 +499,7 @@ void bwd_dq_kernel(const BwdParams bp) {
     vdma.issue(Vg, p.vs_s, n0, Nk, st + SM::KB);
   };
 
-  f32x16 s[2], dp[2];
+  f32x16 s[2];
   bf16x8 dsb[2][2];
   const int T = seq.count;
   const bool last_ragged = T > 0 && seq.start(T - 1, LISTS) + kKN > Nk;
@@ -473,16 +507,19 @@ void bwd_dq_kernel(const BwdParams bp) {
   wait_all_vmem();
   __syncthreads();
 
-  // Phase ph = 0 .. 2T+1, local phase lp = ph - grp, as in the forward:
-  //   lp even: matrix phase: dQ^T += K(lp/2 - 1)^T dS^T, S^T, dP^T of tile lp/2
-  //   lp odd:  vector phase: P and dS of tile (lp-1)/2
+  // Phase ph = 0 .. 2T+1, local phase lp = ph - role (the dQ waves run one phase behind).
+  //   S wave:  lp even: S^T of tile lp/2;                 lp odd: P of tile (lp-1)/2 -> hand-over
+  //   dQ wave: lp even: dQ^T += K^T dS^T of tile lp/2 - 1, dP^T of tile lp/2;
+  //            lp odd:  dS of tile (lp-1)/2 from the handed-over P
+  // The hand-over buffer is written at phase 2t+1 and read at 2t+2; tile t's stage is read
+  // during phases 2t .. 2t+3.
   for (int ph = 0; ph < 2 * T + 2; ++ph) {
     if ((ph & 1) == 0 && ph / 2 + SM::NST - 2 < T) issue_tile(ph / 2 + SM::NST - 2);
-    const int lp = ph - grp;
+    const int lp = ph - role;
     if (lp >= 0 && (lp & 1) == 0) {
       // ------------------------------------------------------------- matrix phase
       const int ts = lp >> 1, tv = ts - 1;
-      if (tv >= 0) {
+      if (role != 0 && tv >= 0) {
         const char* Kl = smem + (tv % SM::NST) * SM::STAGE;
 #pragma unroll
         for (int db = 0; db < DQK / 32; ++db)
@@ -497,78 +534,96 @@ void bwd_dq_kernel(const BwdParams bp) {
             }
       }
       if (ts < T) {
-        const char* Kl = smem + (ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g;
-        const char* Vl = smem + (ts % SM::NST) * SM::STAGE + SM::KB + prow * SM::VP + 16 * g;
+        // S wave: A = K rows, width DQK; dQ wave: A = V rows, width DV
+        const char* st = smem + (ts % SM::NST) * SM::STAGE;
+        const char* ap = role ? st + SM::KB + prow * SM::VP + 16 * g : st + prow * SM::KP + 16 * g;
+        const int pitch = role ? SM::VP : SM::KP;
+        const int dr = role ? DV : DQK;
         s[0] = f32x16{};
         s[1] = f32x16{};
-        dp[0] = f32x16{};
-        dp[1] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < DQK / 16; ++ks) {
-          const bf16x8 a0 = *(const bf16x8*)(Kl + 32 * ks);
-          const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * SM::KP + 32 * ks);
-          s[0] = mfma_bf16(a0, qf[ks], s[0]);
-          s[1] = mfma_bf16(a1, qf[ks], s[1]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < DV / 16; ++ks) {
-          const bf16x8 a0 = *(const bf16x8*)(Vl + 32 * ks);
-          const bf16x8 a1 = *(const bf16x8*)(Vl + 32 * SM::VP + 32 * ks);
-          dp[0] = mfma_bf16(a0, of[ks], dp[0]);
-          dp[1] = mfma_bf16(a1, of[ks], dp[1]);
+        for (int ks = 0; ks < DM / 16; ++ks) {
+          if (16 * ks >= dr) break;
+          const bf16x8 a0 = *(const bf16x8*)(ap + 32 * ks);
+          const bf16x8 a1 = *(const bf16x8*)(ap + 32 * pitch + 32 * ks);
+          s[0] = mfma_bf16(a0, bf[ks], s[0]);
+          s[1] = mfma_bf16(a1, bf[ks], s[1]);
         }
       }
     } else if (lp >= 0 && (lp >> 1) < T) {
       // ------------------------------------------------------------- vector phase
       const int ts = lp >> 1;
-      const int n0 = seq.start(ts, LISTS);
-      bool need = (n0 + kKN > Nk);
-      bool elem = true, hide = false;
-      if constexpr (LISTS) {
-        const uint32_t c = seq.cls(ts, grp, true);
-        hide = c == 0u;
-        elem = c == 1u;
-        need = need || c != 2u;
-      } else {
-        const int last = n0 + kKN - 1;
-        if (mk == kMaskCausal) need = need || (last > qw + delta);
-        else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
-        else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
-        else if (mk == kMaskBlockDiag) need = true;
-      }
-      // reg r of block kb holds key n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of row qrow
-      f32x16 dcap[2];
-      if constexpr (SOFTCAP || BIAS) {
+      if (role == 0) {
+        const int n0 = seq.start(ts, LISTS);
+        bool need = (n0 + kKN > Nk);
+        bool elem = true, hide = false;
+        if constexpr (LISTS) {
+          const uint32_t c = seq.cls(ts, 0, true);
+          hide = c == 0u;
+          elem = c == 1u;
+          need = need || c != 2u;
+        } else {
+          const int last = n0 + kKN - 1;
+          if (mk == kMaskCausal) need = need || (last > qw + delta);
+          else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
+          else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
+          else if (mk == kMaskBlockDiag) need = true;
+        }
+        // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents)
+        int lo = 0, hi = Nk, dqd = 0;
+        const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
+        const bool bd = need && !hide && elem && qrow < Nq && mk == kMaskBlockDiag;
+        if (need) {
+          if (hide) hi = 0;
+          else if (elem && qrow < Nq && mk != kMaskBlockDiag) band_interval(p.mask, qrow, Nq, Nk, lo, hi);
+          hi = min(hi, Nk);
+          if (bd) dqd = p.mask.doc_q[(int64_t)b * Nq + qrow];
+        }
+        const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
+        // reg r of block kb holds key n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of row qrow
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float dc;
-            s[kb][r] = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qrow, n0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7), dc);
-            if constexpr (SOFTCAP) dcap[kb][r] = dc;
+          for (int hh = 0; hh < 2; ++hh) {
+            u32x4 pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float pv[2];
+#pragma unroll
+              for (int z = 0; z < 2; ++z) {
+                const int r = 8 * hh + 2 * e + z;
+                const int j = n0 + 32 * kb + 16 * hh + 8 * g + 2 * e + z;
+                float dcap = 1.0f, u = s[kb][r];
+                if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
+                if (need) {
+                  bool vis = (unsigned)(j - lo) < span;
+                  if (bd) vis = vis && dkd[min(j, Nk - 1)] == dqd;
+                  if (!vis) u = kNegInf;
+                }
+                pv[z] = fast_exp2(__builtin_fmaf(u, c_eff, -rowv));
+                if constexpr (SOFTCAP) pv[z] *= dcap;
+              }
+              pk[e] = pack_bf16x2(pv[0], pv[1]);
+            }
+            xch[64 * (2 * kb + hh)] = pk;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 pc = xch[64 * (2 * kb + hh)];
+            u32x4 dk4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float pf[2];
+              bf16x2_to_f32(pc[e], pf);
+              const int r = 8 * hh + 2 * e;
+              dk4[e] = pack_bf16x2(pf[0] * (s[kb][r] - rowv), pf[1] * (s[kb][r + 1] - rowv));
+            }
+            dsb[kb][hh] = __builtin_bit_cast(bf16x8, dk4);
           }
       }
-      if (need) mask_tile(s, p.mask, b, qrow, n0 + 8 * g, Nq, Nk, elem && qrow < Nq, hide);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float dsv[2];
-#pragma unroll
-            for (int z = 0; z < 2; ++z) {
-              const int r = 8 * hh + 2 * e + z;
-              const float pr = fast_exp2(__builtin_fmaf(s[kb][r], c_eff, -lse2));
-              float d = pr * (dp[kb][r] - ddv);
-              if constexpr (SOFTCAP) d *= dcap[kb][r];
-              dsv[z] = d;
-            }
-            pk[e] = pack_bf16x2(dsv[0], dsv[1]);
-          }
-          dsb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
-        }
     }
     if (ph & 1) {
       const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
@@ -579,8 +634,8 @@ void bwd_dq_kernel(const BwdParams bp) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane = query, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
-  if (qrow < Nq) {
+  // ---- epilogue (dQ wave): lane = query, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
+  if (role != 0 && qrow < Nq) {
     __bf16* dQg = (__bf16*)bp.dq + b * bp.dqs_b + h * bp.dqs_h + (int64_t)qrow * bp.dqs_s;
 #pragma unroll
     for (int db = 0; db < DQK / 32; ++db)
@@ -618,7 +673,7 @@ hipError_t launch_passes(const BwdParams& bp, hipStream_t st) {
   }
   {
     auto kern = bwd_dq_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
-    const int bytes = DqSmem<DQK, DV>::BYTES + list_bytes(bp.a.lists, kKN);
+    const int bytes = DqSmem<DQK, DV, LISTS>::BYTES + list_bytes(bp.a.lists, kKN);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     e = record_stage(bp, 2, st);
@@ -643,12 +698,12 @@ hipError_t dispatch(const BwdParams& bp, bool lists, bool softcap, bool bias, hi
 template <int DQK, int DV>
 bool lists_fit_dims(const ListParams& fwd, const ListParams& tr) {
   return DkdvSmem<DQK, DV>::BYTES + list_bytes(tr, kQS) <= kMaxLdsBytes &&
-         DqSmem<DQK, DV>::BYTES + list_bytes(fwd, kKN) <= kMaxLdsBytes;
+         DqSmem<DQK, DV, true>::BYTES + list_bytes(fwd, kKN) <= kMaxLdsBytes;
 }
 
 }  // namespace
 
-int bwd_q_block_rows() { return kQM / 2; }
+int bwd_q_block_rows() { return kQM; }
 int bwd_kv_block_rows() { return kKB; }
 
 size_t bwd_workspace_bytes(int B, int H, int Nq) {
