@@ -224,7 +224,7 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   odma.init(bp.dos_s, tid);
   constexpr int ld_wave = 7;   // a wave with the fewest tile blocks issues the lse2 / D load
   const int per_step = qdma.count() + odma.count() + (w == ld_wave ? 1 : 0);
-  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // rows past Nq are never loaded: keep them finite
+  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // defensive: every slot is loaded before it is read
   auto issue_step = [&](int t) {
     const int i0 = seq.start(t, LISTS);
     char* st = smem + (t % SM::NST) * SM::STAGE;
@@ -234,7 +234,6 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   };
 
   const int T = seq.count;
-  const bool last_ragged = T > 0 && seq.start(T - 1, LISTS) + kQS > Nq;
   for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_step(t);
   wait_all_vmem();
   __syncthreads();
@@ -372,9 +371,9 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     }
     if (ph & 1) {
       // step (ph + 1) / 2 is read from the next phase on; the NST - 3 steps issued after
-      // it may stay in flight, unless a ragged last step made some waves skip loads
+      // it may stay in flight (loads complete in order)
       const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
-      const bool exact = later > 0 && !(last_ragged && (ph + 1) / 2 + later == T - 1);
+      const bool exact = later > 0;
       if (exact) wait_vmcnt_at_most(later * per_step);
       else wait_lds_dma();
     }
@@ -491,7 +490,7 @@ void bwd_dq_kernel(const BwdParams bp) {
   LdsDma<kKN, DV, SM::VPC, kThreads> vdma;
   kdma.init(p.ks_s, tid);
   vdma.init(p.vs_s, tid);
-  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // rows past Nk are never loaded: keep them finite
+  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // defensive: every slot is loaded before it is read
   auto issue_tile = [&](int t) {
     const int n0 = seq.start(t, LISTS);
     char* st = smem + (t % SM::NST) * SM::STAGE;
@@ -502,7 +501,6 @@ void bwd_dq_kernel(const BwdParams bp) {
   f32x16 s[2];
   bf16x8 dsb[2][2];
   const int T = seq.count;
-  const bool last_ragged = T > 0 && seq.start(T - 1, LISTS) + kKN > Nk;
   for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_tile(t);
   wait_all_vmem();
   __syncthreads();
@@ -627,7 +625,7 @@ void bwd_dq_kernel(const BwdParams bp) {
     }
     if (ph & 1) {
       const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
-      const bool exact = later > 0 && !(last_ragged && (ph + 1) / 2 + later == T - 1);
+      const bool exact = later > 0;
       if (exact) kdma.wait_leaving(vdma, later);
       else wait_lds_dma();
     }

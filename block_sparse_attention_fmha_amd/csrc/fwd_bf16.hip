@@ -151,7 +151,7 @@ void fwd_bf16_kernel(const AttnParams p) {
   LdsDma<kBN, DV, SM::VPC, kThreads> vdma;
   kdma.init(p.ks_s, tid);
   vdma.init(p.vs_s, tid);
-  zero_lds<kThreads>(smem, SM::BYTES, tid);   // rows past Nk are never loaded: keep them finite
+  zero_lds<kThreads>(smem, SM::BYTES, tid);   // defensive: every slot is loaded before it is read
   auto issue_tile = [&](int t) {
     const int n0 = seq.start(t, LISTS);
     char* st = smem + (t % SM::NST) * SM::STAGE;
@@ -162,8 +162,6 @@ void fwd_bf16_kernel(const AttnParams p) {
   f32x16 s[2];
   bf16x8 pb[2][2];
   const int T = seq.count;
-  // only the tile holding key Nk - 1 can be ragged, and it is always the last of the sequence
-  const bool last_ragged = T > 0 && seq.start(T - 1, LISTS) + kBN > Nk;
   for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_tile(t);
   wait_all_vmem();   // Q fragments and the first tiles
   __syncthreads();
@@ -278,11 +276,10 @@ void fwd_bf16_kernel(const AttnParams p) {
     }
     if (ph & 1) {
       // tile (ph + 1) / 2 is read from the next phase on; the NST - 3 tiles issued after
-      // it may stay in flight (loads complete in order), provided each issued its full
-      // instruction count: not so for a ragged last tile, where a wave can skip whole
-      // instructions, so that case waits for everything.
+      // it may stay in flight (loads complete in order; every tile costs each wave the
+      // same number of load instructions)
       const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
-      const bool exact = later > 0 && !(last_ragged && (ph + 1) / 2 + later == T - 1);
+      const bool exact = later > 0;
       if (exact) kdma.wait_leaving(vdma, later);
       else wait_lds_dma();
     }

@@ -201,9 +201,17 @@ __device__ __forceinline__ int swap_bits23(int m) {
 // kernels.
 __device__ __forceinline__ void dma_16b(const char* gbase, uint32_t voff, const char* lds_block) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t laddr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_block;
+  // both bases are wave-uniform by contract; readfirstlane makes that visible to the
+  // compiler where it cannot prove it (free when the value already sits in an SGPR)
+  // (the flat address of an LDS location holds its LDS offset in the low 32 bits)
+  const uint32_t laddr = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_block);
+  const uint64_t ga = (uint64_t)(uintptr_t)gbase;
+  // readfirstlane returns int: go through uint32_t so the low word is zero-extended
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
+  const uint64_t gu = ((uint64_t)ghi << 32) | (uint64_t)glo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(gbase), "s"(laddr) : "memory");
+               :: "v"(voff), "s"((const char*)(uintptr_t)gu), "s"(laddr) : "memory");
 #endif
 }
 
@@ -226,14 +234,16 @@ __device__ __forceinline__ void wait_vmcnt_at_most(int n) {
 // Copies rows [row0, row0 + ROWS) of a row-strided bf16 matrix (D columns) into an LDS
 // tile with a padded row pitch of PCH 16-byte chunks (PCH >= D/8), using direct
 // global->LDS loads (global_load_lds_dwordx4). Each wave instruction fills 1 KiB of
-// consecutive LDS, lane i writing bytes 16 i .. 16 i + 15; lanes that fall on a pad slot
-// stay idle. The per-lane global byte offsets (row * row_bytes + chunk * 16) are computed
-// once (init). Since chunk * 16 < row_bytes, "row < rows left" is simply
-// "offset < rows left * row_bytes", so rows at or past `nrows` are skipped with one
-// compare against a scalar and no extra registers; their LDS rows keep older (finite)
-// contents, which callers must mask (zero the tile once before first use). Data is
-// visible to the workgroup after wait_lds_dma() and a barrier. Requires
-// ROWS * row_stride * 2 < 2^31 (checked on the host).
+// consecutive LDS, lane i writing bytes 16 i .. 16 i + 15. The per-lane global byte
+// offsets (row * row_bytes + chunk * 16) are computed once (init). Every lane of every
+// instruction loads, without branches: a lane on a pad slot, or on a row at or past
+// `nrows` (a ragged last tile), loads offset 0 instead (row row0, which always exists),
+// so its LDS slot receives finite data that callers never use unmasked (pad columns are
+// never read; rows past the end are masked or multiplied by zero probabilities). Since
+// chunk * 16 < row_bytes, "row < rows left" is "offset < rows left * row_bytes". Each
+// tile therefore costs every wave exactly count() instructions, which keeps partial
+// vmcnt waits exact. Data is visible to the workgroup after the wave's wait and a
+// barrier. Requires ROWS * row_stride * 2 < 2^31 (checked on the host).
 template <int ROWS, int D, int PCH, int NTHREADS>
 struct LdsDma {
   static constexpr int CH = D / 8;
@@ -242,7 +252,6 @@ struct LdsDma {
   static constexpr int NI = (NBLK + NW - 1) / NW;              // blocks per wave (max)
   static_assert(ROWS * PCH % 64 == 0, "padded tile must be whole 1 KiB blocks");
   static_assert(PCH >= CH, "pitch shorter than a row");
-  static constexpr uint32_t kIdle = 0xFFFFFFFFu;
   uint32_t off[NI];
   int w;
 
@@ -254,7 +263,7 @@ struct LdsDma {
       const int blk = j * NW + w;
       const int L = blk * 64 + lane;
       const int r = L / PCH, c = L - (L / PCH) * PCH;
-      off[j] = (blk < NBLK && c < CH) ? (uint32_t)(r * (int)(row_stride * 2) + c * 16) : kIdle;
+      off[j] = (blk < NBLK && c < CH) ? (uint32_t)(r * (int)(row_stride * 2) + c * 16) : 0u;
     }
   }
   // number of DMA instructions this wave issues per tile
@@ -267,14 +276,29 @@ struct LdsDma {
   }
   __device__ __forceinline__ void issue(const __bf16* g, int64_t row_stride, int row0, int nrows,
                                         char* lds_tile) const {
+    issue_part<0, 1>(g, row_stride, row0, nrows, lds_tile);
+  }
+  // The instructions j with j % NPART == PART only: lets a caller spread one tile's loads
+  // over several points of its code (issue every PART once per tile).
+  template <int PART, int NPART>
+  __device__ __forceinline__ void issue_part(const __bf16* g, int64_t row_stride, int row0, int nrows,
+                                             char* lds_tile) const {
     const int left = nrows - row0;
-    const uint32_t lim = (left >= ROWS) ? kIdle : (uint32_t)(left * (int)(row_stride * 2));
     const char* base = (const char*)(g + (int64_t)row0 * row_stride);
+    const int cnt = __builtin_amdgcn_readfirstlane(count());   // scalar: blocks of this wave
+    if (left >= ROWS) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int blk = j * NW + w;
-      if (blk >= NBLK) break;
-      if (off[j] < lim) dma_16b(base, off[j], lds_tile + blk * 1024);
+      for (int j = PART; j < NI; j += NPART) {
+        if (j >= cnt) break;
+        dma_16b(base, off[j], lds_tile + (j * NW + w) * 1024);
+      }
+    } else {
+      const uint32_t lim = (uint32_t)(left * (int)(row_stride * 2));
+#pragma unroll
+      for (int j = PART; j < NI; j += NPART) {
+        if (j >= cnt) break;
+        dma_16b(base, off[j] < lim ? off[j] : 0u, lds_tile + (j * NW + w) * 1024);
+      }
     }
   }
 };
