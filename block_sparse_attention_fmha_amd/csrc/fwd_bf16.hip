@@ -29,9 +29,11 @@
 //     (global_load_lds_dwordx4, no VGPR staging) issued two phases before first use;
 //     padded row pitches keep the 16-byte K row reads and the transposed V reads free
 //     of bank conflicts.
-//   * the O rescale by exp(m_old - m_new) is skipped for a tile when no row of the wave
-//     raised its running max (a wave-uniform branch), which after the first few tiles
-//     is the common case; the row sum adds exactly the bf16 P fed to the MFMA.
+//   * the running max is updated lazily: the O / l rescale by exp(m_old - m_new) runs
+//     (a wave-uniform branch) only when some row's tile max exceeds the running max by
+//     more than 2^8 in probability; otherwise the stale max stays, every p is at most
+//     256 (exact in bf16 and fp32 sums), and O and l remain consistently scaled. The
+//     row sum adds exactly the bf16 P fed to the MFMA.
 //   * the work item order is XCD-aware (each XCD gets a contiguous run of heads) and,
 //     for causal-like masks, longest-first over query tiles.
 #include "kernel_common.h"
@@ -43,6 +45,7 @@ namespace {
 constexpr int kBM = 256;   // query rows per workgroup
 constexpr int kBN = 64;    // keys per tile
 constexpr int kThreads = 512;
+constexpr float kRescaleLog2 = 8.0f;   // stale-max tolerance of the online softmax (log2 units)
 // LDS stages of (K, V) tiles: tile t is loaded 2 * stages - 4 phases before first use.
 template <int DQK> struct Stages { static constexpr int value = (DQK <= 128) ? 4 : 3; };
 
@@ -244,7 +247,10 @@ void fwd_bf16_kernel(const AttnParams p) {
       // SIMD, so latency, not issue rate, bounds it)
       float mt = tree_max32(s);
       mt = pair_max(mt) * c_eff;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run)) {
+      // lazy rescale: keep a stale running max until some row's max exceeds it by more
+      // than kRescaleLog2, so p = exp2(s - m) <= 2^kRescaleLog2 and the rescale runs only
+      // on large jumps (usually just the first tile); O and l always share the same m
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2)) {
         const float m_new = fmaxf(m_run, mt);
         const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.0f : m_new));
         l_run *= alpha;
