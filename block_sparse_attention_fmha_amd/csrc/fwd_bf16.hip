@@ -32,8 +32,8 @@
 //   * the running max is updated lazily: the O / l rescale by exp(m_old - m_new) runs
 //     (a wave-uniform branch) only when some row's tile max exceeds the running max by
 //     more than 2^8 in probability; otherwise the stale max stays, every p is at most
-//     256 (exact in bf16 and fp32 sums), and O and l remain consistently scaled. The
-//     row sum adds exactly the bf16 P fed to the MFMA.
+//     256, and O and l remain consistently scaled. The row sum adds the fp32
+//     probabilities whose bf16 roundings feed the MFMA.
 //   * the work item order is XCD-aware (each XCD gets a contiguous run of heads) and,
 //     for causal-like masks, longest-first over query tiles.
 #include "kernel_common.h"
@@ -261,7 +261,8 @@ void fwd_bf16_kernel(const AttnParams p) {
         m_run = m_new;
       }
       const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
-      // four independent partial row sums of exactly the bf16 P fed to the MFMA
+      // four independent partial row sums of the fp32 probabilities (plain adds: the packed
+      // bf16 dot product would stall the partner wave's MFMAs, as it shares their pipe)
       float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -273,7 +274,7 @@ void fwd_bf16_kernel(const AttnParams p) {
             const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
             const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
             pk[e] = pack_bf16x2(p0, p1);
-            ls[e] = add_bf16_pair(pk[e], ls[e]);
+            ls[e] += p0 + p1;
           }
           pb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
         }

@@ -322,12 +322,6 @@ __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-// Sum of two packed bf16 values added to acc (v_dot2c_f32_bf16 against (1, 1)).
-__device__ __forceinline__ float add_bf16_pair(uint32_t packed, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
-}
-
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
