@@ -13,7 +13,9 @@ Prints ONE JSON line on stdout:
                bwd 2 (3 Dqk + 2 Dv) A per (b, h), A = N (N + 1) / 2 for causal
   roofline     for the kernel that takes the most time per step: its algorithmic FLOPs
                per launch / its average launch duration (HIP events on the launch stream
-               over the timed region), against the bf16 dense MFMA peak
+               over the timed region), against the bf16 dense MFMA peak; "traffic" is its
+               HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+               summary, or null when the kernel sources changed since it was taken
   cpu_baseline the CPU fp64 oracle on one head of the same workload (fwd + bwd), scaled
                to TFLOP/s of useful work
 --all-configs additionally prints per-workload timings of the other configurations to
@@ -37,6 +39,42 @@ PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 
 B, H, N, D = 1, 16, 16384, 128
+
+PROFILE_HBM = os.path.join(ROOT, "profiles", "fwd_bwd_causal_b1h16n16384d128_hbm_counters.md")
+PROFILE_NAMES = {"fwd_bf16": "fwd_bf16_kernel<128, 128, false, false, false>",
+                 "bwd_dkdv": "bwd_dkdv_kernel<128, 128, false, false, false>",
+                 "bwd_dq": "bwd_dq_kernel<128, 128, false, false, false>"}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources and the build script (their code and flags)."""
+    import hashlib
+    pkg = os.path.join(ROOT, "block_sparse_attention_fmha_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
+    h = hashlib.sha256()
+    for f in files + ["../build.py"]:
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when that summary was taken with different kernel sources (or is missing)."""
+    try:
+        text = open(PROFILE_HBM).read()
+    except OSError:
+        return None
+    tag = "Kernel sources sha256: "
+    if tag not in text or text.split(tag, 1)[1].split()[0].strip("`") != kernel_source_hash():
+        return None
+    name = PROFILE_NAMES.get(kernel)
+    for row in text.splitlines():
+        if name and row.startswith(f"| `{name}`"):
+            return int(round(float(row.strip("|").split("|")[-1]) * 2**20))
+    return None
 
 
 def causal_pairs(n: int) -> int:
@@ -247,7 +285,7 @@ def main():
         "kernels": kernels,
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(dominant)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
