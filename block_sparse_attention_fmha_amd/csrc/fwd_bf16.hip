@@ -22,8 +22,8 @@
 //     with two ds_read_b64_tr_b16 transposed reads (no transpose pass over V).
 //   * ping-pong: the two waves sharing a SIMD (wave w and w + 4) alternate between a
 //     matrix phase (S(j+1) = K(j+1) Q^T and O += V(j) P(j): 32 MFMAs) and a vector phase
-//     (mask, online softmax, P(j+1) in bf16), one phase apart, separated by workgroup
-//     barriers. While one wave feeds the matrix core the other runs its softmax, so the
+//     (mask, online softmax, P(j+1) in bf16), one phase apart, with a workgroup barrier
+//     once per tile (two phases). While one wave feeds the matrix core the other runs its softmax, so the
 //     VALU work hides behind the MFMA work instead of serialising with it.
 //   * K and V tiles live in 3 LDS stages filled by direct global->LDS loads
 //     (global_load_lds_dwordx4, no VGPR staging) issued two phases before first use;
@@ -289,8 +289,11 @@ void fwd_bf16_kernel(const AttnParams p) {
       const bool exact = later > 0;
       if (exact) kdma.wait_leaving(vdma, later);
       else wait_lds_dma();
+      // Once per tile: tile (ph + 1) / 2 is visible to all waves and every wave is done
+      // with the stage that the next phase refills. Within a tile the partner waves need
+      // no barrier (their state is private and no stage changes), so they alternate freely.
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---- epilogue
