@@ -103,8 +103,12 @@ struct DkdvSmem {
   static constexpr int QB = kQS * QP, OB = kQS * OP;
   static constexpr int LB = 1024;                      // lse2[64], D[64], 512 bytes unused
   static constexpr int STAGE = QB + OB + LB;
-  static constexpr int XB = 4 * 64 * 64;               // P hand-over: 4 pairs x 64 lanes x 64 B
-  static constexpr int NST = (4 * STAGE + XB <= 148 * 1024) ? 4 : 3;
+  static constexpr int XB1 = 4 * 64 * 64;              // P hand-over: 4 pairs x 64 lanes x 64 B
+  static constexpr int NST = (4 * STAGE + XB1 <= 148 * 1024) ? 4 : 3;
+  // Double-buffered hand-over where it fits: then the workgroup needs a barrier only
+  // once per step (two phases) instead of after every phase.
+  static constexpr bool DBLX = NST * STAGE + 2 * XB1 <= 152 * 1024;
+  static constexpr int XB = DBLX ? 2 * XB1 : XB1;
   static constexpr int BYTES = NST * STAGE + XB;
 };
 
@@ -211,7 +215,9 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   const int prow = swap_bits23(lq);
   const int trow = 8 * g + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
-  u32x4* xch = (u32x4*)(smem + SM::NST * SM::STAGE + pair * 4096) + l;   // + 64 i
+  // hand-over slot of the pair, lane-major (+ 64 i per 16-byte piece); when double-
+  // buffered, the buffer of step t (t & 1) sits 1024 pieces further
+  u32x4* xch = (u32x4*)(smem + SM::NST * SM::STAGE + pair * 4096) + l;
 
   // visible queries of the lane's key under the band masks: qlo <= i <= qhi
   int qlo = 0, qhi = 0x3fffffff;
@@ -340,7 +346,7 @@ void bwd_dkdv_kernel(const BwdParams bp) {
               pc[e] = SOFTCAP ? pack_bf16x2(pd[0], pd[1]) : pk[e];
             }
             bop[kb][hh] = __builtin_bit_cast(bf16x8, pk);
-            xch[64 * (2 * kb + hh)] = pc;
+            xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pc;
           }
       } else {
         const float* Dl = LD + 64;
@@ -350,7 +356,7 @@ void bwd_dkdv_kernel(const BwdParams bp) {
           for (int hh = 0; hh < 2; ++hh) {
             const int qi = 32 * kb + 16 * hh + 8 * g;
             const f32x4 da = *(const f32x4*)(Dl + qi), db4 = *(const f32x4*)(Dl + qi + 4);
-            const u32x4 pc = xch[64 * (2 * kb + hh)];
+            const u32x4 pc = xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)];
             u32x4 dk4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -377,7 +383,10 @@ void bwd_dkdv_kernel(const BwdParams bp) {
       if (exact) wait_vmcnt_at_most(later * per_step);
       else wait_lds_dma();
     }
-    __syncthreads();
+    // Stages are refilled only at even phases and the hand-over of step t is written at
+    // phase 2t + 1 and read at 2t + 2, so with a double-buffered hand-over the odd-phase
+    // barrier alone orders every LDS reuse; otherwise barrier after every phase.
+    if (!SM::DBLX || (ph & 1)) __syncthreads();
   }
 
   // ---- epilogue: lane = key, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
@@ -408,8 +417,13 @@ struct DqSmem {
   static constexpr int KP = KPC * 16, VP = VPC * 16;
   static constexpr int KB = kKN * KP, VB = kKN * VP;
   static constexpr int STAGE = KB + VB;
-  static constexpr int XB = 4 * 64 * 64;               // P hand-over: 4 pairs x 64 lanes x 64 B
-  // 4 stages when they fit next to the hand-over buffer (and the list sequence)
+  static constexpr int XB1 = 4 * 64 * 64;              // P hand-over: 4 pairs x 64 lanes x 64 B
+  // Double-buffered hand-over (barrier once per tile), and as many stages as then fit:
+  // the S and dQ waves have unequal phases (16 vs 32 MFMAs), so a barrier after every
+  // phase costs more than the fourth stage gains (measured: 1.95 vs 2.25 ms at the
+  // causal 16K D = 128 shape).
+  static constexpr bool DBLX = true;
+  static constexpr int XB = 2 * XB1;
   static constexpr int NST = (4 * STAGE + XB <= (LISTS ? 148 : 160) * 1024) ? 4 : 3;
   static constexpr int BYTES = NST * STAGE + XB;
 };
@@ -603,14 +617,14 @@ void bwd_dq_kernel(const BwdParams bp) {
               }
               pk[e] = pack_bf16x2(pv[0], pv[1]);
             }
-            xch[64 * (2 * kb + hh)] = pk;
+            xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pk;
           }
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 pc = xch[64 * (2 * kb + hh)];
+            const u32x4 pc = xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)];
             u32x4 dk4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -629,7 +643,7 @@ void bwd_dq_kernel(const BwdParams bp) {
       if (exact) kdma.wait_leaving(vdma, later);
       else wait_lds_dma();
     }
-    __syncthreads();
+    if (!SM::DBLX || (ph & 1)) __syncthreads();   // as in the dK/dV pass
   }
 
   // ---- epilogue (dQ wave): lane = query, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
