@@ -63,6 +63,10 @@ bool strides_ok(const int64_t s[3], int esize) {
   return true;
 }
 
+// The tile loaders address 64 rows of a tile with 32-bit byte offsets from the tile's
+// first row: the sequence stride must keep 64 rows under 2^31 bytes.
+bool seq_stride_fits(const int64_t s[3], int esize) { return s[1] * esize * 64 < ((int64_t)1 << 31); }
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int validate_mask(const fmha_mask& m) {
@@ -115,6 +119,9 @@ int validate_fwd(const fmha_fwd_args* a) {
   if (!strides_ok(a->q_stride, es) || !strides_ok(a->k_stride, es) || !strides_ok(a->v_stride, es) ||
       !strides_ok(a->o_stride, es))
     return FMHA_ERR_INVALID_ARG;
+  if (!seq_stride_fits(a->q_stride, es) || !seq_stride_fits(a->k_stride, es) || !seq_stride_fits(a->v_stride, es) ||
+      !seq_stride_fits(a->o_stride, es))
+    return FMHA_ERR_UNSUPPORTED;
   return FMHA_OK;
 }
 
@@ -264,6 +271,7 @@ int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
   if (!strides_ok(g->do_stride, 2) || !strides_ok(g->dq_stride, 2) || !strides_ok(g->dk_stride, 2) ||
       !strides_ok(g->dv_stride, 2))
     return FMHA_ERR_INVALID_ARG;
+  if (!seq_stride_fits(g->do_stride, 2)) return FMHA_ERR_UNSUPPORTED;
   const size_t need = fmha_bwd_workspace_size(a->B, a->H, a->Nq);
   if (g->workspace == nullptr || g->workspace_bytes < need || !aligned16(g->workspace)) return FMHA_ERR_WORKSPACE;
   if (a->block_sparse) {

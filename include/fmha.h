@@ -120,7 +120,8 @@ typedef struct {
 
 /* Forward problem. Q [B,Nq,H,Dqk], K [B,Nk,H,Dqk], V [B,Nk,H,Dv], O [B,Nq,H,Dv] are
  * addressed with element strides {batch, seq, head}; the head dim is contiguous
- * (so BSHD and BHSD both work). Rows (seq-stride * elem size) must be 16-byte aligned.
+ * (so BSHD and BHSD both work). Rows (seq-stride * elem size) must be 16-byte aligned,
+ * and 64 rows must span less than 2^31 bytes (FMHA_ERR_UNSUPPORTED otherwise).
  * LSE is fp32 [B, H, Nq] contiguous. dtype applies to Q, K, V and O.
  * Supported (dtype, Dqk, Dv): bf16 (64,64), (128,128), (192,128); fp32 (64,64),
  * (128,128), (1024,1024) (fp32: no block-sparse lists, no softcap/bias). */

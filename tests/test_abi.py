@@ -121,6 +121,29 @@ def test_block_sparse_tile_constraints(lib):
     assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_INVALID_ARG
 
 
+def test_fwd_rejects_sequence_stride_beyond_32bit_tile_offsets(lib):
+    a = _args()
+    a.k_stride[1] = (1 << 31) // (2 * 64)          # 64 rows of bf16 reach 2^31 bytes
+    a.k_stride[0] = a.k_stride[1] * 64
+    assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_UNSUPPORTED
+    # (requests that pass validation are not made here: with fake pointers they would
+    # launch on a machine that has a GPU)
+
+
+def test_block_sparse_list_granularity(lib):
+    # forward lists need tile_m % 128 and tile_n % 64 (accepted shapes such as 384 x 192
+    # are exercised by the GPU tests)
+    bs = fa.CBlockSparse()
+    for name in ("partial_cnt", "partial_idx", "full_cnt", "full_idx"):
+        setattr(bs, name, 0x100000)
+    a = _args()
+    a.block_sparse = ctypes.pointer(bs)
+    for tm, tn in ((128, 32), (192, 64), (64, 128)):
+        bs.tile_m, bs.tile_n, bs.heads = tm, tn, 1
+        bs.n_q_tiles, bs.n_kv_tiles = -(-a.Nq // tm), -(-a.Nk // tn)
+        assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_UNSUPPORTED, (tm, tn)
+
+
 def test_bwd_and_splitkv_workspace_checks(lib):
     a = _args()
     g = fa.CBwdArgs()
@@ -130,6 +153,8 @@ def test_bwd_and_splitkv_workspace_checks(lib):
     need = lib.fmha_bwd_workspace_size(1, 2, 64)
     assert need >= 1 * 2 * 64 * 4 and need % 256 == 0
     g.workspace, g.workspace_bytes = 0x200000, need - 1
+    assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_WORKSPACE
+    g.workspace, g.workspace_bytes = 0x200008, need   # large enough but not 16-byte aligned
     assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_WORKSPACE
     assert lib.fmha_bwd(ctypes.byref(a), None, None) == fa.FMHA_ERR_INVALID_ARG
     need = lib.fmha_fwd_splitkv_workspace_size(1, 2, 64, 128, 4)
