@@ -151,7 +151,7 @@ template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
 void bwd_dkdv_kernel(const BwdParams bp) {
   using SM = DkdvSmem<DQK, DV>;
-  constexpr int DM = DQK > DV ? DQK : DV;
+  constexpr int DM = DQK > DV ? DQK : DV, DN = DQK < DV ? DQK : DV;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnParams& p = bp.a;
 
@@ -223,6 +223,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   int qlo = 0, qhi = 0x3fffffff;
   if (mk == kMaskCausal || mk == kMaskWindow || (mk == kMaskPrefix && key >= p.mask.prefix)) qlo = key - delta;
   if (mk == kMaskWindow) qhi = key - delta + p.mask.window;
+  const uint32_t qspan = (uint32_t)qhi - (uint32_t)qlo;   // qlo <= i <= qhi as one unsigned test
+  const int kdoc = (mk == kMaskBlockDiag && key < Nk) ? p.mask.doc_k[(int64_t)b * Nk + key] : 0;
 
   LdsDma<kQS, DQK, SM::QPC, kThreads> qdma;
   LdsDma<kQS, DV, SM::OPC, kThreads> odma;
@@ -272,6 +274,9 @@ void bwd_dkdv_kernel(const BwdParams bp) {
         if (tv >= 0) {
 #pragma unroll
           for (int db = 0; db < DM / 32; ++db) {
+            // An early exit, so the loop stays rolled and bf[] is indexed at run time: it
+            // then lives in scratch memory, which at these widths beats the spills of the
+            // fully unrolled form (acc + bf + s would exceed the registers of two waves).
             if (db >= na) break;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -315,39 +320,48 @@ void bwd_dkdv_kernel(const BwdParams bp) {
           else if (mk == kMaskPrefix) need = (kw + 31 >= p.mask.prefix) && (kw + 31 > i0 + delta);
           else if (mk == kMaskBlockDiag) need = true;
         }
+        auto p_phase = [&](auto test_c) {
+          constexpr int TEST = decltype(test_c)::value;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int qi = 32 * kb + 16 * hh + 8 * g;
-            const f32x4 la = *(const f32x4*)(LD + qi), lb = *(const f32x4*)(LD + qi + 4);
-            u32x4 pk, pc;
+            for (int hh = 0; hh < 2; ++hh) {
+              const int qi = 32 * kb + 16 * hh + 8 * g;
+              const f32x4 la = *(const f32x4*)(LD + qi), lb = *(const f32x4*)(LD + qi + 4);
+              const int qb = (TEST != kTestNone || BIAS) ? opaque_int(i0 + qi) : 0;
+              u32x4 pk, pc;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float pv[2], pd[2];
+              for (int e = 0; e < 4; ++e) {
+                float pv[2], pd[2];
 #pragma unroll
-              for (int z = 0; z < 2; ++z) {
-                const int ee = 2 * e + z, r = 8 * hh + ee;
-                const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
-                const int qidx = i0 + qi + ee;
-                float dcap = 1.0f, u;
-                if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
-                else u = s[kb][r] * p.scale_log2;
-                if (need) {
-                  bool vis;
-                  if (mk == kMaskBlockDiag) vis = qidx >= Nq || key >= Nk || mask_visible(p.mask, b, qidx, key, Nq, Nk);
-                  else vis = qidx >= qlo && qidx <= qhi;
-                  if (!vis) u = kNegInf;
+                for (int z = 0; z < 2; ++z) {
+                  const int ee = 2 * e + z, r = 8 * hh + ee;
+                  const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
+                  const int qidx = qb + ee;
+                  float dcap = 1.0f, u;
+                  if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
+                  else u = s[kb][r] * p.scale_log2;
+                  // rows past Nq carry lse2 = +inf, so their P is 0 whatever the test says
+                  if constexpr (TEST == kTestBand) {
+                    if ((uint32_t)qidx - (uint32_t)qlo > qspan) u = kNegInf;
+                  } else if constexpr (TEST == kTestDoc) {
+                    // unconditional (clamped) load, so the loads of a chunk issue back to back
+                    const int dq = p.mask.doc_q[(int64_t)b * Nq + min(qidx, Nq - 1)];
+                    if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) u = kNegInf;
+                  }
+                  pv[z] = fast_exp2(u - lse2);
+                  pd[z] = pv[z] * dcap;
                 }
-                pv[z] = fast_exp2(u - lse2);
-                pd[z] = pv[z] * dcap;
+                pk[e] = pack_bf16x2(pv[0], pv[1]);
+                pc[e] = SOFTCAP ? pack_bf16x2(pd[0], pd[1]) : pk[e];
               }
-              pk[e] = pack_bf16x2(pv[0], pv[1]);
-              pc[e] = SOFTCAP ? pack_bf16x2(pd[0], pd[1]) : pk[e];
+              bop[kb][hh] = __builtin_bit_cast(bf16x8, pk);
+              xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pc;
             }
-            bop[kb][hh] = __builtin_bit_cast(bf16x8, pk);
-            xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pc;
-          }
+        };
+        if (!need) p_phase(IntC<kTestNone>{});
+        else if (mk != kMaskBlockDiag) p_phase(IntC<kTestBand>{});
+        else p_phase(IntC<kTestDoc>{});
       } else {
         const float* Dl = LD + 64;
 #pragma unroll
@@ -398,7 +412,7 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     const int dw = isk ? DQK : DV;
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) {
-      if (32 * db >= dw) break;
+      if (32 * db >= DN && 32 * db >= dw) continue;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         u32x2 v;
@@ -432,7 +446,7 @@ template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
 void bwd_dq_kernel(const BwdParams bp) {
   using SM = DqSmem<DQK, DV, LISTS>;
-  constexpr int DM = DQK > DV ? DQK : DV;
+  constexpr int DM = DQK > DV ? DQK : DV, DN = DQK < DV ? DQK : DV;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnParams& p = bp.a;
 
@@ -490,6 +504,7 @@ void bwd_dq_kernel(const BwdParams bp) {
   // lse2 (S wave) or D (dQ wave) of the lane's query
   float rowv = role ? 0.0f : __builtin_huge_valf();
   if (qrow < Nq) rowv = bp.ws[((int64_t)bh * bp.n_qblk + qrow / 64) * 128 + (role ? 64 : 0) + qrow % 64];
+  const int dqd = (mk == kMaskBlockDiag && qrow < Nq) ? p.mask.doc_q[(int64_t)b * Nq + qrow] : 0;
 
   f32x16 dq[DQK / 32];
 #pragma unroll
@@ -555,7 +570,7 @@ void bwd_dq_kernel(const BwdParams bp) {
         s[1] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < DM / 16; ++ks) {
-          if (16 * ks >= dr) break;
+          if (16 * ks >= DN && 16 * ks >= dr) continue;   // a predicate: the loop must unroll
           const bf16x8 a0 = *(const bf16x8*)(ap + 32 * ks);
           const bf16x8 a1 = *(const bf16x8*)(ap + 32 * pitch + 32 * ks);
           s[0] = mfma_bf16(a0, bf[ks], s[0]);
@@ -582,43 +597,50 @@ void bwd_dq_kernel(const BwdParams bp) {
           else if (mk == kMaskBlockDiag) need = true;
         }
         // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents)
-        int lo = 0, hi = Nk, dqd = 0;
+        int lo = 0, hi = Nk;
         const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
-        const bool bd = need && !hide && elem && qrow < Nq && mk == kMaskBlockDiag;
+        // wave-uniform; rows past Nq carry rowv = +inf, so their P is 0 whatever the test says
+        const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;
         if (need) {
           if (hide) hi = 0;
           else if (elem && qrow < Nq && mk != kMaskBlockDiag) band_interval(p.mask, qrow, Nq, Nk, lo, hi);
           hi = min(hi, Nk);
-          if (bd) dqd = p.mask.doc_q[(int64_t)b * Nq + qrow];
         }
         const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
         // reg r of block kb holds key n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of row qrow
+        auto p_phase = [&](auto test_c) {
+          constexpr int TEST = decltype(test_c)::value;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4 pk;
+            for (int hh = 0; hh < 2; ++hh) {
+              const int jb = (TEST != kTestNone || BIAS) ? opaque_int(n0 + 32 * kb + 16 * hh + 8 * g) : 0;
+              u32x4 pk;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float pv[2];
+              for (int e = 0; e < 4; ++e) {
+                float pv[2];
 #pragma unroll
-              for (int z = 0; z < 2; ++z) {
-                const int r = 8 * hh + 2 * e + z;
-                const int j = n0 + 32 * kb + 16 * hh + 8 * g + 2 * e + z;
-                float dcap = 1.0f, u = s[kb][r];
-                if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
-                if (need) {
-                  bool vis = (unsigned)(j - lo) < span;
-                  if (bd) vis = vis && dkd[min(j, Nk - 1)] == dqd;
-                  if (!vis) u = kNegInf;
+                for (int z = 0; z < 2; ++z) {
+                  const int r = 8 * hh + 2 * e + z;
+                  const int j = jb + 2 * e + z;
+                  float dcap = 1.0f, u = s[kb][r];
+                  if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
+                  if constexpr (TEST != kTestNone) {
+                    bool vis = (unsigned)(j - lo) < span;
+                    if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
+                    if (!vis) u = kNegInf;
+                  }
+                  pv[z] = fast_exp2(__builtin_fmaf(u, c_eff, -rowv));
+                  if constexpr (SOFTCAP) pv[z] *= dcap;
                 }
-                pv[z] = fast_exp2(__builtin_fmaf(u, c_eff, -rowv));
-                if constexpr (SOFTCAP) pv[z] *= dcap;
+                pk[e] = pack_bf16x2(pv[0], pv[1]);
               }
-              pk[e] = pack_bf16x2(pv[0], pv[1]);
+              xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pk;
             }
-            xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pk;
-          }
+        };
+        if (!need) p_phase(IntC<kTestNone>{});
+        else if (!bdw) p_phase(IntC<kTestBand>{});
+        else p_phase(IntC<kTestDoc>{});
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)

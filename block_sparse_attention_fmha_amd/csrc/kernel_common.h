@@ -36,6 +36,21 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskBlockDiag = 3, kMaskPrefix = 4 };
 
+// Per-tile element-mask test, chosen once per tile so the unrolled element loops carry no
+// run-time case: none, a visible interval per row or column, or the document comparison.
+enum MaskTest { kTestNone = 0, kTestBand = 1, kTestDoc = 2 };
+template <int V> struct IntC { static constexpr int value = V; };
+
+// A value the optimiser may not look through. Used on per-step row or column bases so the
+// per-element offsets added to them are not hoisted out of the main loop as dozens of
+// loop-invariant registers.
+__device__ __forceinline__ int opaque_int(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+  return x;
+}
+
 // ---------------------------------------------------------------------------------------
 // Parameter blocks (passed by value as kernel arguments).
 
