@@ -115,26 +115,30 @@ struct DkdvSmem {
 // One matrix phase of a dK/dV wave. First acc^T += T^T bop for the previous step (T = dO
 // for the P wave, Q for the dS wave, read transposed; DA = its width), then
 // s = R bf^T for the current step (R = Q for the P wave, dO for the dS wave, rows in the
-// permuted order; DR = its width). Either half may be absent.
+// permuted order; DR = its width). Either half may be absent. toff / roff: LDS byte
+// offsets of the lane's first T and R reads; they are made opaque so that every other
+// read of the phase is a constant immediate offset from them (otherwise the compiler
+// keeps dozens of precomputed addresses in registers across the main loop).
 template <int DR, int DA, int RP, int TP, int NBF, int NACC>
-__device__ __forceinline__ void dkdv_matrix(const char* Tl, const char* Rl, bool do_acc, bool do_s,
+__device__ __forceinline__ void dkdv_matrix(const char* lds, int toff, int roff, bool do_acc, bool do_s,
                                             f32x16 (&acc)[NACC], const bf16x8 (&bop)[2][2], f32x16 (&s)[2],
-                                            const bf16x8 (&bf)[NBF], int trow, int tcol, int prow, int g) {
+                                            const bf16x8 (&bf)[NBF]) {
   if (do_acc) {
+    const char* t0 = lds + opaque_int(toff);
 #pragma unroll
     for (int db = 0; db < DA / 32; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const char* tp = Tl + (32 * kb + 16 * hh + trow) * TP + (32 * db + tcol) * 2;
+          const char* tp = t0 + (32 * kb + 16 * hh) * TP + 64 * db;
           const u32x2 lo = lds_read_tr(tp);
           const u32x2 hi = lds_read_tr(tp + 4 * TP);
           acc[db] = mfma_bf16(join_bf16x8(lo, hi), bop[kb][hh], acc[db]);
         }
   }
   if (do_s) {
-    const char* rp = Rl + prow * RP + 16 * g;
+    const char* rp = lds + opaque_int(roff);
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
@@ -246,161 +250,208 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   wait_all_vmem();
   __syncthreads();
 
-  // Phase ph = 0 .. 2T+1, local phase lp = ph - role (the dS waves run one phase behind).
-  //   lp even: matrix phase: acc += T(lp/2 - 1)^T bop, s = R(lp/2) bf^T
-  //   lp odd:  vector phase of step (lp-1)/2: P wave: P (into bop and the hand-over
-  //            buffer); dS wave: dS from the handed-over P (into bop)
-  // The P wave writes the hand-over buffer at phase 2t+1 and the dS wave reads it at
-  // phase 2t+2; the next write comes at 2t+3. Stage t is read during phases 2t .. 2t+3.
-  for (int ph = 0; ph < 2 * T + 2; ++ph) {
-    if ((ph & 1) == 0 && ph / 2 + SM::NST - 2 < T) issue_step(ph / 2 + SM::NST - 2);
-    const int lp = ph - role;
-    if (lp >= 0 && (lp & 1) == 0) {
-      // ------------------------------------------------------------- matrix phase
-      const int ts = lp >> 1, tv = ts - 1;
+  // Steps t = 0 .. T, two phases each; the dS waves run one phase behind the P waves:
+  //   P wave,  step t: matrix  s = Q_t K^T (t < T), dV^T += dO_{t-1}^T P_{t-1} (t > 0);
+  //                    vector  P_t from s and the saved LSE, into bop and the hand-over
+  //   dS wave, step t: vector  dS_{t-1} = P_{t-1} (dP_{t-1} - D) from the hand-over (t > 0);
+  //                    matrix  s = dO_t V^T (t < T), dK^T += Q_{t-1}^T dS_{t-1} (t > 0)
+  // The hand-over of step t is written in phase 2t+1 and read in phase 2t+2; stage t is
+  // read during phases 2t .. 2t+3 and refilled in phase 2t+4 at the earliest.
+  // Each role runs its own loop with the first and last steps peeled, so nothing
+  // conditional sits between the phases and the loop-carried operands (s, bop, acc) keep
+  // their registers from one step to the next.
+  auto matrix = [&](int ts, bool do_acc, bool do_s) {
+    const int tv = ts - 1;
+    if constexpr (DQK == DV) {
+      const int sv = ((tv < 0 ? 0 : tv) % SM::NST) * SM::STAGE + (role ? 0 : SM::QB);
+      const int ss = (ts % SM::NST) * SM::STAGE + (role ? SM::QB : 0);
+      dkdv_matrix<DQK, DQK, SM::QP, SM::QP>(smem, sv + trow * SM::QP + tcol * 2, ss + prow * SM::QP + 16 * g,
+                                            do_acc, do_s, acc, bop, s, bf);
+    } else {
       const char* Sv = smem + ((tv < 0 ? 0 : tv) % SM::NST) * SM::STAGE;
       const char* Ss = smem + (ts % SM::NST) * SM::STAGE;
-      if constexpr (DQK == DV) {
-        const char* Tl = Sv + (role ? 0 : SM::QB);
-        const char* Rl = Ss + (role ? SM::QB : 0);
-        dkdv_matrix<DQK, DQK, SM::QP, SM::QP>(Tl, Rl, tv >= 0, ts < T, acc, bop, s, bf, trow, tcol, prow, g);
-      } else {
-        // one code path for both roles (two inlined variants would not fit the registers):
-        // wave-uniform widths and pitches, loops bounded by the wider head
-        const char* Tl = role ? Sv : Sv + SM::QB;
-        const char* Rl = role ? Ss + SM::QB : Ss;
-        const int tp = role ? SM::QP : SM::OP, rp = role ? SM::OP : SM::QP;
-        const int na = (role ? DQK : DV) / 32, nr = (role ? DV : DQK) / 16;
-        if (tv >= 0) {
+      // one code path for both roles (two inlined variants would not fit the registers):
+      // wave-uniform widths and pitches, loops bounded by the wider head
+      const char* Tl = role ? Sv : Sv + SM::QB;
+      const char* Rl = role ? Ss + SM::QB : Ss;
+      const int tp = role ? SM::QP : SM::OP, rp = role ? SM::OP : SM::QP;
+      const int na = (role ? DQK : DV) / 32, nr = (role ? DV : DQK) / 16;
+      if (do_acc) {
 #pragma unroll
-          for (int db = 0; db < DM / 32; ++db) {
-            // An early exit, so the loop stays rolled and bf[] is indexed at run time: it
-            // then lives in scratch memory, which at these widths beats the spills of the
-            // fully unrolled form (acc + bf + s would exceed the registers of two waves).
-            if (db >= na) break;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                const char* tq = Tl + (32 * kb + 16 * hh + trow) * tp + (32 * db + tcol) * 2;
-                const u32x2 lo = lds_read_tr(tq);
-                const u32x2 hi = lds_read_tr(tq + 4 * tp);
-                acc[db] = mfma_bf16(join_bf16x8(lo, hi), bop[kb][hh], acc[db]);
-              }
-          }
-        }
-        if (ts < T) {
-          const char* rq = Rl + prow * rp + 16 * g;
-          s[0] = f32x16{};
-          s[1] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < DM / 16; ++ks) {
-            if (ks >= nr) break;
-            const bf16x8 a0 = *(const bf16x8*)(rq + 32 * ks);
-            const bf16x8 a1 = *(const bf16x8*)(rq + 32 * rp + 32 * ks);
-            s[0] = mfma_bf16(a0, bf[ks], s[0]);
-            s[1] = mfma_bf16(a1, bf[ks], s[1]);
-          }
-        }
-      }
-    } else if (lp >= 0 && (lp >> 1) < T) {
-      // ------------------------------------------------------------- vector phase
-      const int ts = lp >> 1;
-      const int i0 = seq.start(ts, LISTS);
-      const float* LD = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB);
-      // register r of block kb holds query i0 + 32 kb + 16 (r / 8) + 8 g + r % 8
-      if (role == 0) {
-        bool need;
-        if constexpr (LISTS) {
-          need = seq.cls(ts, 0, true) != 2u;
-        } else {
-          need = false;
-          if (mk == kMaskCausal) need = kw + 31 > i0 + delta;
-          else if (mk == kMaskWindow) need = (kw + 31 > i0 + delta) || (kw < i0 + kQS - 1 + delta - p.mask.window);
-          else if (mk == kMaskPrefix) need = (kw + 31 >= p.mask.prefix) && (kw + 31 > i0 + delta);
-          else if (mk == kMaskBlockDiag) need = true;
-        }
-        auto p_phase = [&](auto test_c) {
-          constexpr int TEST = decltype(test_c)::value;
+        for (int db = 0; db < DM / 32; ++db) {
+          // An early exit, so the loop stays rolled and bf[] is indexed at run time: it
+          // then lives in scratch memory, which at these widths beats the spills of the
+          // fully unrolled form (acc + bf + s would exceed the registers of two waves).
+          if (db >= na) break;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-              const int qi = 32 * kb + 16 * hh + 8 * g;
-              const f32x4 la = *(const f32x4*)(LD + qi), lb = *(const f32x4*)(LD + qi + 4);
-              const int qb = (TEST != kTestNone || BIAS) ? opaque_int(i0 + qi) : 0;
-              u32x4 pk, pc;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float pv[2], pd[2];
-#pragma unroll
-                for (int z = 0; z < 2; ++z) {
-                  const int ee = 2 * e + z, r = 8 * hh + ee;
-                  const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
-                  const int qidx = qb + ee;
-                  float dcap = 1.0f, u;
-                  if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
-                  else u = s[kb][r] * p.scale_log2;
-                  // rows past Nq carry lse2 = +inf, so their P is 0 whatever the test says
-                  if constexpr (TEST == kTestBand) {
-                    if ((uint32_t)qidx - (uint32_t)qlo > qspan) u = kNegInf;
-                  } else if constexpr (TEST == kTestDoc) {
-                    // unconditional (clamped) load, so the loads of a chunk issue back to back
-                    const int dq = p.mask.doc_q[(int64_t)b * Nq + min(qidx, Nq - 1)];
-                    if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) u = kNegInf;
-                  }
-                  pv[z] = fast_exp2(u - lse2);
-                  pd[z] = pv[z] * dcap;
-                }
-                pk[e] = pack_bf16x2(pv[0], pv[1]);
-                pc[e] = SOFTCAP ? pack_bf16x2(pd[0], pd[1]) : pk[e];
-              }
-              bop[kb][hh] = __builtin_bit_cast(bf16x8, pk);
-              xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pc;
+              const char* tq = Tl + (32 * kb + 16 * hh + trow) * tp + (32 * db + tcol) * 2;
+              const u32x2 lo = lds_read_tr(tq);
+              const u32x2 hi = lds_read_tr(tq + 4 * tp);
+              acc[db] = mfma_bf16(join_bf16x8(lo, hi), bop[kb][hh], acc[db]);
             }
-        };
-        if (!need) p_phase(IntC<kTestNone>{});
-        else if (mk != kMaskBlockDiag) p_phase(IntC<kTestBand>{});
-        else p_phase(IntC<kTestDoc>{});
-      } else {
-        const float* Dl = LD + 64;
+        }
+      }
+      if (do_s) {
+        const char* rq = Rl + prow * rp + 16 * g;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int qi = 32 * kb + 16 * hh + 8 * g;
-            const f32x4 da = *(const f32x4*)(Dl + qi), db4 = *(const f32x4*)(Dl + qi + 4);
-            const u32x4 pc = xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)];
-            u32x4 dk4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float pf[2];
-              bf16x2_to_f32(pc[e], pf);
-              float dsv[2];
-#pragma unroll
-              for (int z = 0; z < 2; ++z) {
-                const int ee = 2 * e + z, r = 8 * hh + ee;
-                const float dd = ee < 4 ? da[ee] : db4[ee - 4];
-                dsv[z] = pf[z] * (s[kb][r] - dd);
-              }
-              dk4[e] = pack_bf16x2(dsv[0], dsv[1]);
-            }
-            bop[kb][hh] = __builtin_bit_cast(bf16x8, dk4);
-          }
+        for (int ks = 0; ks < DM / 16; ++ks) {
+          if (ks >= nr) break;
+          const bf16x8 a0 = *(const bf16x8*)(rq + 32 * ks);
+          const bf16x8 a1 = *(const bf16x8*)(rq + 32 * rp + 32 * ks);
+          s[0] = mfma_bf16(a0, bf[ks], s[0]);
+          s[1] = mfma_bf16(a1, bf[ks], s[1]);
+        }
       }
     }
-    if (ph & 1) {
-      // step (ph + 1) / 2 is read from the next phase on; the NST - 3 steps issued after
-      // it may stay in flight (loads complete in order)
-      const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
-      const bool exact = later > 0;
-      if (exact) wait_vmcnt_at_most(later * per_step);
-      else wait_lds_dma();
+  };
+
+  // P wave: P_ts = exp2(s * scale_log2 - lse2) (score transform and element mask applied),
+  // register r of block kb holding query i0 + 32 kb + 16 (r / 8) + 8 g + r % 8
+  auto p_vector = [&](int ts) {
+    const int i0 = seq.start(ts, LISTS);
+    const float* LD = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB);
+    bool need;
+    if constexpr (LISTS) {
+      need = seq.cls(ts, 0, true) != 2u;
+    } else {
+      need = false;
+      if (mk == kMaskCausal) need = kw + 31 > i0 + delta;
+      else if (mk == kMaskWindow) need = (kw + 31 > i0 + delta) || (kw < i0 + kQS - 1 + delta - p.mask.window);
+      else if (mk == kMaskPrefix) need = (kw + 31 >= p.mask.prefix) && (kw + 31 > i0 + delta);
+      else if (mk == kMaskBlockDiag) need = true;
     }
-    // Stages are refilled only at even phases and the hand-over of step t is written at
-    // phase 2t + 1 and read at 2t + 2, so with a double-buffered hand-over the odd-phase
-    // barrier alone orders every LDS reuse; otherwise barrier after every phase.
-    if (!SM::DBLX || (ph & 1)) __syncthreads();
+    auto body = [&](auto test_c) {
+      constexpr int TEST = decltype(test_c)::value;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int qi = 32 * kb + 16 * hh + 8 * g;
+          const f32x4 la = *(const f32x4*)(LD + qi), lb = *(const f32x4*)(LD + qi + 4);
+          const int qb = (TEST != kTestNone || BIAS) ? opaque_int(i0 + qi) : 0;
+          u32x4 pk, pc;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv[2], pd[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const int ee = 2 * e + z, r = 8 * hh + ee;
+              const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
+              const int qidx = qb + ee;
+              float dcap = 1.0f, u;
+              if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
+              else u = s[kb][r] * p.scale_log2;
+              // rows past Nq carry lse2 = +inf, so their P is 0 whatever the test says
+              if constexpr (TEST == kTestBand) {
+                if ((uint32_t)qidx - (uint32_t)qlo > qspan) u = kNegInf;
+              } else if constexpr (TEST == kTestDoc) {
+                // unconditional (clamped) load, so the loads of a chunk issue back to back
+                const int dq = p.mask.doc_q[(int64_t)b * Nq + min(qidx, Nq - 1)];
+                if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) u = kNegInf;
+              }
+              pv[z] = fast_exp2(u - lse2);
+              pd[z] = pv[z] * dcap;
+            }
+            pk[e] = pack_bf16x2(pv[0], pv[1]);
+            pc[e] = SOFTCAP ? pack_bf16x2(pd[0], pd[1]) : pk[e];
+          }
+          bop[kb][hh] = __builtin_bit_cast(bf16x8, pk);
+          xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pc;
+        }
+    };
+    if (!need) body(IntC<kTestNone>{});
+    else if (mk != kMaskBlockDiag) body(IntC<kTestBand>{});
+    else body(IntC<kTestDoc>{});
+  };
+
+  // dS wave: dS_ts = P (dP - D) from the handed-over P, into bop
+  auto ds_vector = [&](int ts) {
+    const float* Dl = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB) + 64;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int qi = 32 * kb + 16 * hh + 8 * g;
+        const f32x4 da = *(const f32x4*)(Dl + qi), db4 = *(const f32x4*)(Dl + qi + 4);
+        const u32x4 pc = xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)];
+        u32x4 dk4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pf[2];
+          bf16x2_to_f32(pc[e], pf);
+          float dsv[2];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int ee = 2 * e + z, r = 8 * hh + ee;
+            const float dd = ee < 4 ? da[ee] : db4[ee - 4];
+            dsv[z] = pf[z] * (s[kb][r] - dd);
+          }
+          dk4[e] = pack_bf16x2(dsv[0], dsv[1]);
+        }
+        bop[kb][hh] = __builtin_bit_cast(bf16x8, dk4);
+      }
+  };
+
+  auto step_begin = [&](int t) {
+    if (t + SM::NST - 2 < T) issue_step(t + SM::NST - 2);
+  };
+  // Stages are refilled only at the start of a step and the hand-over of step t is
+  // written in its second phase and read in the first phase of step t + 1, so with a
+  // double-buffered hand-over the end-of-step barrier alone orders every LDS reuse;
+  // otherwise a barrier also separates the two phases.
+  auto mid = [&]() {
+    if (!SM::DBLX) __syncthreads();
+  };
+  auto step_end = [&](int t) {
+    // stage t + 1 is read from the next step on; the NST - 3 steps issued after it may
+    // stay in flight (loads complete in order)
+    const int later = min(SM::NST - 3, max(0, T - 2 - t));
+    if (later > 0) wait_vmcnt_at_most(later * per_step);
+    else wait_lds_dma();
+    __syncthreads();
+  };
+
+  if (T > 0) {
+    if (role == 0) {
+      step_begin(0);
+      matrix(0, false, true);
+      mid();
+      p_vector(0);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        matrix(t, true, true);
+        mid();
+        p_vector(t);
+        step_end(t);
+      }
+      step_begin(T);
+      matrix(T, true, false);
+      mid();
+      step_end(T);
+    } else {
+      step_begin(0);
+      mid();
+      matrix(0, false, true);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        ds_vector(t - 1);
+        mid();
+        matrix(t, true, true);
+        step_end(t);
+      }
+      step_begin(T);
+      ds_vector(T - 1);
+      mid();
+      matrix(T, true, false);
+      step_end(T);
+    }
   }
 
   // ---- epilogue: lane = key, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
