@@ -585,138 +585,183 @@ void bwd_dq_kernel(const BwdParams bp) {
   wait_all_vmem();
   __syncthreads();
 
-  // Phase ph = 0 .. 2T+1, local phase lp = ph - role (the dQ waves run one phase behind).
-  //   S wave:  lp even: S^T of tile lp/2;                 lp odd: P of tile (lp-1)/2 -> hand-over
-  //   dQ wave: lp even: dQ^T += K^T dS^T of tile lp/2 - 1, dP^T of tile lp/2;
-  //            lp odd:  dS of tile (lp-1)/2 from the handed-over P
-  // The hand-over buffer is written at phase 2t+1 and read at 2t+2; tile t's stage is read
-  // during phases 2t .. 2t+3.
-  for (int ph = 0; ph < 2 * T + 2; ++ph) {
-    if ((ph & 1) == 0 && ph / 2 + SM::NST - 2 < T) issue_tile(ph / 2 + SM::NST - 2);
-    const int lp = ph - role;
-    if (lp >= 0 && (lp & 1) == 0) {
-      // ------------------------------------------------------------- matrix phase
-      const int ts = lp >> 1, tv = ts - 1;
-      if (role != 0 && tv >= 0) {
-        const char* Kl = smem + (tv % SM::NST) * SM::STAGE;
+  // Steps t = 0 .. T, two phases each; the dQ waves run one phase behind the S waves:
+  //   S wave,  step t (t < T): matrix  s = S^T of tile t;  vector  P of tile t -> hand-over
+  //   dQ wave, step t: vector  dS of tile t-1 from the handed-over P (t > 0);
+  //                    matrix  dQ^T += K^T dS^T of tile t-1 (t > 0), s = dP^T of tile t (t < T)
+  // The hand-over of tile t is written in phase 2t+1 and read in phase 2t+2; tile t's
+  // stage is read during phases 2t .. 2t+3. Each role runs its own loop (first and last
+  // steps peeled) so nothing conditional sits between the phases.
+  auto matrix_s = [&](int ts) {
+    // A = K rows in the permuted order, width DQK
+    const char* ap = smem + opaque_int((ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-        for (int db = 0; db < DQK / 32; ++db)
+    for (int ks = 0; ks < DQK / 16; ++ks) {
+      const bf16x8 a0 = *(const bf16x8*)(ap + 32 * ks);
+      const bf16x8 a1 = *(const bf16x8*)(ap + 32 * SM::KP + 32 * ks);
+      s[0] = mfma_bf16(a0, bf[ks], s[0]);
+      s[1] = mfma_bf16(a1, bf[ks], s[1]);
+    }
+  };
+  auto matrix_dq = [&](int ts, bool do_acc, bool do_s) {
+    if (do_acc) {
+      // dQ^T += K^T dS^T of tile ts - 1 (K read transposed)
+      const char* kp0 = smem + opaque_int(((ts - 1) % SM::NST) * SM::STAGE + trow * SM::KP + tcol * 2);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const char* kp = Kl + (32 * kb + 16 * hh + trow) * SM::KP + (32 * db + tcol) * 2;
-              const u32x2 lo = lds_read_tr(kp);
-              const u32x2 hi = lds_read_tr(kp + 4 * SM::KP);
-              dq[db] = mfma_bf16(join_bf16x8(lo, hi), dsb[kb][hh], dq[db]);
-            }
-      }
-      if (ts < T) {
-        // S wave: A = K rows, width DQK; dQ wave: A = V rows, width DV
-        const char* st = smem + (ts % SM::NST) * SM::STAGE;
-        const char* ap = role ? st + SM::KB + prow * SM::VP + 16 * g : st + prow * SM::KP + 16 * g;
-        const int pitch = role ? SM::VP : SM::KP;
-        const int dr = role ? DV : DQK;
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < DM / 16; ++ks) {
-          if (16 * ks >= DN && 16 * ks >= dr) continue;   // a predicate: the loop must unroll
-          const bf16x8 a0 = *(const bf16x8*)(ap + 32 * ks);
-          const bf16x8 a1 = *(const bf16x8*)(ap + 32 * pitch + 32 * ks);
-          s[0] = mfma_bf16(a0, bf[ks], s[0]);
-          s[1] = mfma_bf16(a1, bf[ks], s[1]);
-        }
-      }
-    } else if (lp >= 0 && (lp >> 1) < T) {
-      // ------------------------------------------------------------- vector phase
-      const int ts = lp >> 1;
-      if (role == 0) {
-        const int n0 = seq.start(ts, LISTS);
-        bool need = (n0 + kKN > Nk);
-        bool elem = true, hide = false;
-        if constexpr (LISTS) {
-          const uint32_t c = seq.cls(ts, 0, true);
-          hide = c == 0u;
-          elem = c == 1u;
-          need = need || c != 2u;
-        } else {
-          const int last = n0 + kKN - 1;
-          if (mk == kMaskCausal) need = need || (last > qw + delta);
-          else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
-          else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
-          else if (mk == kMaskBlockDiag) need = true;
-        }
-        // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents)
-        int lo = 0, hi = Nk;
-        const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
-        // wave-uniform; rows past Nq carry rowv = +inf, so their P is 0 whatever the test says
-        const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;
-        if (need) {
-          if (hide) hi = 0;
-          else if (elem && qrow < Nq && mk != kMaskBlockDiag) band_interval(p.mask, qrow, Nq, Nk, lo, hi);
-          hi = min(hi, Nk);
-        }
-        const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
-        // reg r of block kb holds key n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of row qrow
-        auto p_phase = [&](auto test_c) {
-          constexpr int TEST = decltype(test_c)::value;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int jb = (TEST != kTestNone || BIAS) ? opaque_int(n0 + 32 * kb + 16 * hh + 8 * g) : 0;
-              u32x4 pk;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float pv[2];
-#pragma unroll
-                for (int z = 0; z < 2; ++z) {
-                  const int r = 8 * hh + 2 * e + z;
-                  const int j = jb + 2 * e + z;
-                  float dcap = 1.0f, u = s[kb][r];
-                  if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
-                  if constexpr (TEST != kTestNone) {
-                    bool vis = (unsigned)(j - lo) < span;
-                    if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
-                    if (!vis) u = kNegInf;
-                  }
-                  pv[z] = fast_exp2(__builtin_fmaf(u, c_eff, -rowv));
-                  if constexpr (SOFTCAP) pv[z] *= dcap;
-                }
-                pk[e] = pack_bf16x2(pv[0], pv[1]);
-              }
-              xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pk;
-            }
-        };
-        if (!need) p_phase(IntC<kTestNone>{});
-        else if (!bdw) p_phase(IntC<kTestBand>{});
-        else p_phase(IntC<kTestDoc>{});
-      } else {
+      for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 pc = xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)];
-            u32x4 dk4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float pf[2];
-              bf16x2_to_f32(pc[e], pf);
-              const int r = 8 * hh + 2 * e;
-              dk4[e] = pack_bf16x2(pf[0] * (s[kb][r] - rowv), pf[1] * (s[kb][r + 1] - rowv));
-            }
-            dsb[kb][hh] = __builtin_bit_cast(bf16x8, dk4);
+            const char* kp = kp0 + (32 * kb + 16 * hh) * SM::KP + 64 * db;
+            const u32x2 lo = lds_read_tr(kp);
+            const u32x2 hi = lds_read_tr(kp + 4 * SM::KP);
+            dq[db] = mfma_bf16(join_bf16x8(lo, hi), dsb[kb][hh], dq[db]);
           }
+    }
+    if (do_s) {
+      // dP^T: A = V rows in the permuted order, width DV
+      const char* ap = smem + opaque_int((ts % SM::NST) * SM::STAGE + SM::KB + prow * SM::VP + 16 * g);
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks) {
+        const bf16x8 a0 = *(const bf16x8*)(ap + 32 * ks);
+        const bf16x8 a1 = *(const bf16x8*)(ap + 32 * SM::VP + 32 * ks);
+        s[0] = mfma_bf16(a0, bf[ks], s[0]);
+        s[1] = mfma_bf16(a1, bf[ks], s[1]);
       }
     }
-    if (ph & 1) {
-      const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
-      const bool exact = later > 0;
-      if (exact) kdma.wait_leaving(vdma, later);
-      else wait_lds_dma();
+  };
+
+  // S wave: P of tile ts (score transform, element mask, exp against the row's lse2) into
+  // the hand-over; reg r of block kb holds key n0 + 32 kb + 16 (r / 8) + 8 g + r % 8
+  auto p_vector = [&](int ts) {
+    const int n0 = seq.start(ts, LISTS);
+    bool need = (n0 + kKN > Nk);
+    bool elem = true, hide = false;
+    if constexpr (LISTS) {
+      const uint32_t c = seq.cls(ts, 0, true);
+      hide = c == 0u;
+      elem = c == 1u;
+      need = need || c != 2u;
+    } else {
+      const int last = n0 + kKN - 1;
+      if (mk == kMaskCausal) need = need || (last > qw + delta);
+      else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
+      else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
+      else if (mk == kMaskBlockDiag) need = true;
     }
-    if (!SM::DBLX || (ph & 1)) __syncthreads();   // as in the dK/dV pass
+    // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents)
+    int lo = 0, hi = Nk;
+    const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
+    // wave-uniform; rows past Nq carry rowv = +inf, so their P is 0 whatever the test says
+    const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;
+    if (need) {
+      if (hide) hi = 0;
+      else if (elem && qrow < Nq && mk != kMaskBlockDiag) band_interval(p.mask, qrow, Nq, Nk, lo, hi);
+      hi = min(hi, Nk);
+    }
+    const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
+    auto body = [&](auto test_c) {
+      constexpr int TEST = decltype(test_c)::value;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int jb = (TEST != kTestNone || BIAS) ? opaque_int(n0 + 32 * kb + 16 * hh + 8 * g) : 0;
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const int r = 8 * hh + 2 * e + z;
+              const int j = jb + 2 * e + z;
+              float dcap = 1.0f, u = s[kb][r];
+              if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
+              if constexpr (TEST != kTestNone) {
+                bool vis = (unsigned)(j - lo) < span;
+                if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
+                if (!vis) u = kNegInf;
+              }
+              pv[z] = fast_exp2(__builtin_fmaf(u, c_eff, -rowv));
+              if constexpr (SOFTCAP) pv[z] *= dcap;
+            }
+            pk[e] = pack_bf16x2(pv[0], pv[1]);
+          }
+          xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)] = pk;
+        }
+    };
+    if (!need) body(IntC<kTestNone>{});
+    else if (!bdw) body(IntC<kTestBand>{});
+    else body(IntC<kTestDoc>{});
+  };
+
+  // dQ wave: dS = P (dP - D) of tile ts from the handed-over P, into dsb
+  auto ds_vector = [&](int ts) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const u32x4 pc = xch[(SM::DBLX ? 1024 * (ts & 1) : 0) + 64 * (2 * kb + hh)];
+        u32x4 dk4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pf[2];
+          bf16x2_to_f32(pc[e], pf);
+          const int r = 8 * hh + 2 * e;
+          dk4[e] = pack_bf16x2(pf[0] * (s[kb][r] - rowv), pf[1] * (s[kb][r + 1] - rowv));
+        }
+        dsb[kb][hh] = __builtin_bit_cast(bf16x8, dk4);
+      }
+  };
+
+  auto step_begin = [&](int t) {
+    if (t + SM::NST - 2 < T) issue_tile(t + SM::NST - 2);
+  };
+  auto mid = [&]() {   // as in the dK/dV pass
+    if (!SM::DBLX) __syncthreads();
+  };
+  auto step_end = [&](int t) {
+    const int later = min(SM::NST - 3, max(0, T - 2 - t));
+    if (later > 0) kdma.wait_leaving(vdma, later);
+    else wait_lds_dma();
+    __syncthreads();
+  };
+
+  if (T > 0) {
+    if (role == 0) {
+      for (int t = 0; t < T; ++t) {
+        step_begin(t);
+        matrix_s(t);
+        mid();
+        p_vector(t);
+        step_end(t);
+      }
+      step_begin(T);
+      mid();
+      step_end(T);
+    } else {
+      step_begin(0);
+      mid();
+      matrix_dq(0, false, true);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        ds_vector(t - 1);
+        mid();
+        matrix_dq(t, true, true);
+        step_end(t);
+      }
+      step_begin(T);
+      ds_vector(T - 1);
+      mid();
+      matrix_dq(T, true, false);
+      step_end(T);
+    }
   }
 
   // ---- epilogue (dQ wave): lane = query, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
