@@ -99,7 +99,8 @@ void fwd_bf16_kernel(const AttnParams p) {
   const int q0 = qt * kBM;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so per-wave tests branch on scalars
+  const int l = tid & 63, g = l >> 5, lq = l & 31;
   const int Nq = p.Nq, Nk = p.Nk, delta = Nk - Nq;
 
   const __bf16* Qg = (const __bf16*)p.q + b * p.qs_b + h * p.qs_h;
@@ -169,130 +170,163 @@ void fwd_bf16_kernel(const AttnParams p) {
   wait_all_vmem();   // Q fragments and the first tiles
   __syncthreads();
 
-  // Phase ph = 0 .. 2T+1. Local phase lp = ph - grp (waves 4-7 run one phase behind).
-  //   lp even: matrix phase  -> S(lp/2) = K Q^T (if < T), O += V(lp/2 - 1) P (if >= 0)
-  //   lp odd:  vector phase  -> softmax of S((lp-1)/2) into P (if < T)
-  // Tile t's stage is busy during phases 2t .. 2t+3. Tile t is issued at phase
-  // 2 (t - NST + 2) (the first NST - 2 tiles before the loop), i.e. 2 NST - 4 phases
-  // before its first use, once the stage's previous tile (t - NST) is done; the wave
-  // then waits for it at the end of phase 2t - 1.
-  for (int ph = 0; ph < 2 * T + 2; ++ph) {
-    if ((ph & 1) == 0 && ph / 2 + SM::NST - 2 < T) issue_tile(ph / 2 + SM::NST - 2);
-    const int lp = ph - grp;
-    if (lp >= 0 && (lp & 1) == 0) {
-      // ------------------------------------------------------------- matrix phase
-      const int ts = lp >> 1;          // tile whose S is computed
-      const int tv = ts - 1;           // tile whose P V is accumulated
-      if (tv >= 0) {
-        const char* Vl = smem + (tv % SM::NST) * SM::STAGE + SM::KB;
+  // Steps t = 0 .. T, two phases each; waves 4-7 run one phase behind waves 0-3:
+  //   waves 0-3, step t: matrix  S(t) = K Q^T (t < T), O += V(t-1) P (t > 0);
+  //                      vector  softmax of S(t) into P (t < T)
+  //   waves 4-7, step t: vector  softmax of S(t-1) (t > 0);  matrix as above
+  // so the two waves of a SIMD alternate between MFMA and VALU work. Tile t's stage is
+  // busy during phases 2t .. 2t+3; tile t is issued at the start of step t - NST + 2 (the
+  // first NST - 2 tiles before the loop), once the stage's previous tile (t - NST) is
+  // done. Each group runs its own loop with the first and last steps peeled, so nothing
+  // conditional sits between the phases and the loop-carried operands keep their
+  // registers.
+  auto matrix = [&](int ts, bool do_acc, bool do_s) {
+    if (do_acc) {
+      // O += V(ts - 1) P, V read transposed at immediate offsets from one per-lane base
+      const char* v0 = smem + opaque_int(((ts - 1) % SM::NST) * SM::STAGE + SM::KB + trow * SM::VP + tcol * 2);
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db) {
+      for (int db = 0; db < DV / 32; ++db) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const char* vp = Vl + (32 * kb + 16 * hh + trow) * SM::VP + (32 * db + tcol) * 2;
-              const u32x2 lo = lds_read_tr(vp);
-              const u32x2 hi = lds_read_tr(vp + 4 * SM::VP);
-              o[db] = mfma_bf16(join_bf16x8(lo, hi), pb[kb][hh], o[db]);
-            }
+          for (int hh = 0; hh < 2; ++hh) {
+            const char* vp = v0 + (32 * kb + 16 * hh) * SM::VP + 64 * db;
+            const u32x2 lo = lds_read_tr(vp);
+            const u32x2 hi = lds_read_tr(vp + 4 * SM::VP);
+            o[db] = mfma_bf16(join_bf16x8(lo, hi), pb[kb][hh], o[db]);
           }
         }
       }
-      if (ts < T) {
-        // two independent accumulation chains (key blocks) interleaved
-        const char* Kl = smem + (ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g;
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < DQK / 16; ++ks) {
-          const bf16x8 a0 = *(const bf16x8*)(Kl + 32 * ks);
-          const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * SM::KP + 32 * ks);
-          s[0] = mfma_bf16(a0, qf[ks], s[0]);
-          s[1] = mfma_bf16(a1, qf[ks], s[1]);
-        }
-      }
-    } else if (lp >= 0 && (lp >> 1) < T) {
-      // ------------------------------------------------------------- vector phase
-      const int ts = lp >> 1;
-      const int n0 = seq.start(ts, LISTS);
-      bool need = (n0 + kBN > Nk);
-      bool elem = true, hide = false;
-      if constexpr (LISTS) {
-        const uint32_t c = seq.cls(ts, grp, true);   // this wave's query half
-        hide = c == 0u;
-        elem = c == 1u;
-        need = need || c != 2u;
-      } else {
-        const int last = n0 + kBN - 1;
-        if (mk == kMaskCausal) need = need || (last > qw + delta);
-        else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
-        else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
-        else if (mk == kMaskBlockDiag) need = true;
-      }
-      // score transform (softcap / bias) and mask; reg r of block kb holds key
-      // n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of query row qrow.
-      if constexpr (SOFTCAP || BIAS) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[kb][r] = score_log2<SOFTCAP, BIAS>(s[kb][r], p, qrow, n0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7));
-      }
-      if (need) mask_tile(s, p.mask, b, qrow, n0 + 8 * g, Nq, Nk, elem && qrow < Nq, hide);
-
-      // online softmax (log2 domain). The O / l rescale is skipped when no row of the
-      // wave raised its running max. O already holds every P V up to tile ts - 1.
-      // row max as a shallow tree (short dependency chains: this phase has one wave per
-      // SIMD, so latency, not issue rate, bounds it)
-      float mt = tree_max32(s);
-      mt = pair_max(mt) * c_eff;
-      // lazy rescale: keep a stale running max until some row's max exceeds it by more
-      // than kRescaleLog2, so p = exp2(s - m) <= 2^kRescaleLog2 and the rescale runs only
-      // on large jumps (usually just the first tile); O and l always share the same m
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.0f : m_new));
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
-      // four independent partial row sums of the fp32 probabilities (plain adds: the packed
-      // bf16 dot product would stall the partner wave's MFMAs, as it shares their pipe)
-      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
-            pk[e] = pack_bf16x2(p0, p1);
-            ls[e] += p0 + p1;
-          }
-          pb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
-        }
-      }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-    if (ph & 1) {
-      // tile (ph + 1) / 2 is read from the next phase on; the NST - 3 tiles issued after
-      // it may stay in flight (loads complete in order; every tile costs each wave the
-      // same number of load instructions)
-      const int later = min(SM::NST - 3, max(0, T - 1 - (ph + 1) / 2));
-      const bool exact = later > 0;
-      if (exact) kdma.wait_leaving(vdma, later);
-      else wait_lds_dma();
-      // Once per tile: tile (ph + 1) / 2 is visible to all waves and every wave is done
-      // with the stage that the next phase refills. Within a tile the partner waves need
-      // no barrier (their state is private and no stage changes), so they alternate freely.
-      __syncthreads();
+    if (do_s) {
+      // two independent accumulation chains (key blocks) interleaved
+      const char* Kl = smem + opaque_int((ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g);
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < DQK / 16; ++ks) {
+        const bf16x8 a0 = *(const bf16x8*)(Kl + 32 * ks);
+        const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * SM::KP + 32 * ks);
+        s[0] = mfma_bf16(a0, qf[ks], s[0]);
+        s[1] = mfma_bf16(a1, qf[ks], s[1]);
+      }
+    }
+  };
+
+  auto vector = [&](int ts) {
+    const int n0 = seq.start(ts, LISTS);
+    bool need = (n0 + kBN > Nk);
+    bool elem = true, hide = false;
+    if constexpr (LISTS) {
+      const uint32_t c = seq.cls(ts, grp, true);   // this wave's query half
+      hide = c == 0u;
+      elem = c == 1u;
+      need = need || c != 2u;
+    } else {
+      const int last = n0 + kBN - 1;
+      if (mk == kMaskCausal) need = need || (last > qw + delta);
+      else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
+      else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
+      else if (mk == kMaskBlockDiag) need = true;
+    }
+    // score transform (softcap / bias) and mask; reg r of block kb holds key
+    // n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of query row qrow.
+    if constexpr (SOFTCAP || BIAS) {
+      const int jb = opaque_int(n0 + 8 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = score_log2<SOFTCAP, BIAS>(s[kb][r], p, qrow, jb + 32 * kb + 16 * (r >> 3) + (r & 7));
+    }
+    if (need) mask_tile(s, p.mask, b, qrow, opaque_int(n0 + 8 * g), Nq, Nk, elem && qrow < Nq, hide);
+
+    // online softmax (log2 domain). The O / l rescale is skipped when no row of the
+    // wave raised its running max. O already holds every P V up to tile ts - 1.
+    // row max as a shallow tree (short dependency chains: this phase has one wave per
+    // SIMD, so latency, not issue rate, bounds it)
+    float mt = tree_max32(s);
+    mt = pair_max(mt) * c_eff;
+    // lazy rescale: keep a stale running max until some row's max exceeds it by more
+    // than kRescaleLog2, so p = exp2(s - m) <= 2^kRescaleLog2 and the rescale runs only
+    // on large jumps (usually just the first tile); O and l always share the same m
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+    // four independent partial row sums of the fp32 probabilities (plain adds: the packed
+    // bf16 dot product would stall the partner wave's MFMAs, as it shares their pipe)
+    float ls[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
+          pk[e] = pack_bf16x2(p0, p1);
+          ls[e] = (kb == 0 && hh == 0) ? p0 + p1 : ls[e] + (p0 + p1);   // no 0 + x: it does not fold
+        }
+        pb[kb][hh] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  auto step_begin = [&](int t) {
+    if (t + SM::NST - 2 < T) issue_tile(t + SM::NST - 2);
+  };
+  auto step_end = [&](int t) {
+    // tile t + 1 is read from the next step on; the NST - 3 tiles issued after it may
+    // stay in flight (loads complete in order; every tile costs each wave the same
+    // number of load instructions)
+    const int later = min(SM::NST - 3, max(0, T - 2 - t));
+    if (later > 0) kdma.wait_leaving(vdma, later);
+    else wait_lds_dma();
+    // Once per step: tile t + 1 is visible to all waves and every wave is done with the
+    // stage that the next step refills. Within a step the partner waves need no barrier
+    // (their state is private and no stage changes), so they alternate freely.
+    __syncthreads();
+  };
+
+  if (T > 0) {
+    if (grp == 0) {
+      step_begin(0);
+      matrix(0, false, true);
+      vector(0);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        matrix(t, true, true);
+        vector(t);
+        step_end(t);
+      }
+      step_begin(T);
+      matrix(T, true, false);
+      step_end(T);
+    } else {
+      step_begin(0);
+      matrix(0, false, true);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        vector(t - 1);
+        matrix(t, true, true);
+        step_end(t);
+      }
+      step_begin(T);
+      vector(T - 1);
+      matrix(T, true, false);
+      step_end(T);
     }
   }
 
