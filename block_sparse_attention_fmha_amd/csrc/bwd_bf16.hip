@@ -229,6 +229,13 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   if (mk == kMaskWindow) qhi = key - delta + p.mask.window;
   const uint32_t qspan = (uint32_t)qhi - (uint32_t)qlo;   // qlo <= i <= qhi as one unsigned test
   const int kdoc = (mk == kMaskBlockDiag && key < Nk) ? p.mask.doc_k[(int64_t)b * Nk + key] : 0;
+  // query steps (start i0) that need the element mask for the wave's 32 keys: i0 < need_below
+  // or i0 > need_above (computed once, so the per-step test is two scalar compares)
+  int need_below = INT32_MIN, need_above = INT32_MAX;
+  if (mk == kMaskCausal || mk == kMaskWindow || (mk == kMaskPrefix && kw + 31 >= p.mask.prefix))
+    need_below = kw + 31 - delta;
+  if (mk == kMaskWindow) need_above = kw - kQS + 1 - delta + p.mask.window;
+  if (mk == kMaskBlockDiag) need_below = INT32_MAX;
 
   LdsDma<kQS, DQK, SM::QPC, kThreads> qdma;
   LdsDma<kQS, DV, SM::OPC, kThreads> odma;
@@ -260,54 +267,17 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   // Each role runs its own loop with the first and last steps peeled, so nothing
   // conditional sits between the phases and the loop-carried operands (s, bop, acc) keep
   // their registers from one step to the next.
-  auto matrix = [&](int ts, bool do_acc, bool do_s) {
+  // role R's matrix phase: R = 0 (P wave): T = dO (width DV), R-side = Q (width DQK);
+  // R = 1 (dS wave): T = Q (width DQK), R-side = dO (width DV)
+  auto matrix = [&](auto role_c, int ts, bool do_acc, bool do_s) {
+    constexpr int R = decltype(role_c)::value;
+    constexpr int TP = R ? SM::QP : SM::OP, RP = R ? SM::OP : SM::QP;
+    constexpr int DA = R ? DQK : DV, DR = R ? DV : DQK;
     const int tv = ts - 1;
-    if constexpr (DQK == DV) {
-      const int sv = ((tv < 0 ? 0 : tv) % SM::NST) * SM::STAGE + (role ? 0 : SM::QB);
-      const int ss = (ts % SM::NST) * SM::STAGE + (role ? SM::QB : 0);
-      dkdv_matrix<DQK, DQK, SM::QP, SM::QP>(smem, sv + trow * SM::QP + tcol * 2, ss + prow * SM::QP + 16 * g,
-                                            do_acc, do_s, acc, bop, s, bf);
-    } else {
-      const char* Sv = smem + ((tv < 0 ? 0 : tv) % SM::NST) * SM::STAGE;
-      const char* Ss = smem + (ts % SM::NST) * SM::STAGE;
-      // one code path for both roles (two inlined variants would not fit the registers):
-      // wave-uniform widths and pitches, loops bounded by the wider head
-      const char* Tl = role ? Sv : Sv + SM::QB;
-      const char* Rl = role ? Ss + SM::QB : Ss;
-      const int tp = role ? SM::QP : SM::OP, rp = role ? SM::OP : SM::QP;
-      const int na = (role ? DQK : DV) / 32, nr = (role ? DV : DQK) / 16;
-      if (do_acc) {
-#pragma unroll
-        for (int db = 0; db < DM / 32; ++db) {
-          // An early exit, so the loop stays rolled and bf[] is indexed at run time: it
-          // then lives in scratch memory, which at these widths beats the spills of the
-          // fully unrolled form (acc + bf + s would exceed the registers of two waves).
-          if (db >= na) break;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const char* tq = Tl + (32 * kb + 16 * hh + trow) * tp + (32 * db + tcol) * 2;
-              const u32x2 lo = lds_read_tr(tq);
-              const u32x2 hi = lds_read_tr(tq + 4 * tp);
-              acc[db] = mfma_bf16(join_bf16x8(lo, hi), bop[kb][hh], acc[db]);
-            }
-        }
-      }
-      if (do_s) {
-        const char* rq = Rl + prow * rp + 16 * g;
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < DM / 16; ++ks) {
-          if (ks >= nr) break;
-          const bf16x8 a0 = *(const bf16x8*)(rq + 32 * ks);
-          const bf16x8 a1 = *(const bf16x8*)(rq + 32 * rp + 32 * ks);
-          s[0] = mfma_bf16(a0, bf[ks], s[0]);
-          s[1] = mfma_bf16(a1, bf[ks], s[1]);
-        }
-      }
-    }
+    const int sv = ((tv < 0 ? 0 : tv) % SM::NST) * SM::STAGE + (R ? 0 : SM::QB);
+    const int ss = (ts % SM::NST) * SM::STAGE + (R ? SM::QB : 0);
+    dkdv_matrix<DR, DA, RP, TP>(smem, sv + trow * TP + tcol * 2, ss + prow * RP + 16 * g, do_acc, do_s, acc, bop,
+                                s, bf);
   };
 
   // P wave: P_ts = exp2(s * scale_log2 - lse2) (score transform and element mask applied),
@@ -316,15 +286,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     const int i0 = seq.start(ts, LISTS);
     const float* LD = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB);
     bool need;
-    if constexpr (LISTS) {
-      need = seq.cls(ts, 0, true) != 2u;
-    } else {
-      need = false;
-      if (mk == kMaskCausal) need = kw + 31 > i0 + delta;
-      else if (mk == kMaskWindow) need = (kw + 31 > i0 + delta) || (kw < i0 + kQS - 1 + delta - p.mask.window);
-      else if (mk == kMaskPrefix) need = (kw + 31 >= p.mask.prefix) && (kw + 31 > i0 + delta);
-      else if (mk == kMaskBlockDiag) need = true;
-    }
+    if constexpr (LISTS) need = seq.cls(ts, 0, true) != 2u;
+    else need = i0 < need_below || i0 > need_above;
     auto body = [&](auto test_c) {
       constexpr int TEST = decltype(test_c)::value;
 #pragma unroll
@@ -416,47 +379,10 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     __syncthreads();
   };
 
-  if (T > 0) {
-    if (role == 0) {
-      step_begin(0);
-      matrix(0, false, true);
-      mid();
-      p_vector(0);
-      step_end(0);
-      for (int t = 1; t < T; ++t) {
-        step_begin(t);
-        matrix(t, true, true);
-        mid();
-        p_vector(t);
-        step_end(t);
-      }
-      step_begin(T);
-      matrix(T, true, false);
-      mid();
-      step_end(T);
-    } else {
-      step_begin(0);
-      mid();
-      matrix(0, false, true);
-      step_end(0);
-      for (int t = 1; t < T; ++t) {
-        step_begin(t);
-        ds_vector(t - 1);
-        mid();
-        matrix(t, true, true);
-        step_end(t);
-      }
-      step_begin(T);
-      ds_vector(T - 1);
-      mid();
-      matrix(T, true, false);
-      step_end(T);
-    }
-  }
-
-  // ---- epilogue: lane = key, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
-  if (key < Nk) {
-    const bool isk = role != 0;
+  // ---- epilogue: lane = key, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4. Called on
+  // each role's own path, so registers only one role uses are not kept live by the other.
+  auto store = [&](bool isk) {
+    if (key >= Nk) return;
     __bf16* dst = isk ? (__bf16*)bp.dk + b * bp.dks_b + h * bp.dks_h + (int64_t)key * bp.dks_s
                       : (__bf16*)bp.dv + b * bp.dvs_b + h * bp.dvs_h + (int64_t)key * bp.dvs_s;
     const float sc = isk ? p.scale : 1.0f;
@@ -472,6 +398,48 @@ void bwd_dkdv_kernel(const BwdParams bp) {
         *(u32x2*)(dst + 32 * db + 8 * jj + 4 * g) = v;
       }
     }
+  };
+
+  if (role == 0) {
+    if (T > 0) {
+      step_begin(0);
+      matrix(IntC<0>{}, 0, false, true);
+      mid();
+      p_vector(0);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        matrix(IntC<0>{}, t, true, true);
+        mid();
+        p_vector(t);
+        step_end(t);
+      }
+      step_begin(T);
+      matrix(IntC<0>{}, T, true, false);
+      mid();
+      step_end(T);
+    }
+    store(false);
+  } else {
+    if (T > 0) {
+      step_begin(0);
+      mid();
+      matrix(IntC<1>{}, 0, false, true);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        ds_vector(t - 1);
+        mid();
+        matrix(IntC<1>{}, t, true, true);
+        step_end(t);
+      }
+      step_begin(T);
+      ds_vector(T - 1);
+      mid();
+      matrix(IntC<1>{}, T, true, false);
+      step_end(T);
+    }
+    store(true);
   }
 }
 
@@ -497,7 +465,7 @@ template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
 void bwd_dq_kernel(const BwdParams bp) {
   using SM = DqSmem<DQK, DV, LISTS>;
-  constexpr int DM = DQK > DV ? DQK : DV, DN = DQK < DV ? DQK : DV;
+  constexpr int DM = DQK > DV ? DQK : DV;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnParams& p = bp.a;
 
@@ -556,6 +524,12 @@ void bwd_dq_kernel(const BwdParams bp) {
   float rowv = role ? 0.0f : __builtin_huge_valf();
   if (qrow < Nq) rowv = bp.ws[((int64_t)bh * bp.n_qblk + qrow / 64) * 128 + (role ? 64 : 0) + qrow % 64];
   const int dqd = (mk == kMaskBlockDiag && qrow < Nq) ? p.mask.doc_q[(int64_t)b * Nq + qrow] : 0;
+  // element-mask geometry, computed once (as in the forward)
+  int need_above, need_below;
+  key_tile_need(p.mask, qw, Nk, delta, kKN, need_above, need_below);
+  if constexpr (LISTS) need_above = Nk - kKN, need_below = INT32_MIN;   // the list classes decide
+  int band_lo, band_hi;
+  band_interval(p.mask, qrow, Nq, Nk, band_lo, band_hi);
 
   f32x16 dq[DQK / 32];
 #pragma unroll
@@ -640,30 +614,20 @@ void bwd_dq_kernel(const BwdParams bp) {
   // the hand-over; reg r of block kb holds key n0 + 32 kb + 16 (r / 8) + 8 g + r % 8
   auto p_vector = [&](int ts) {
     const int n0 = seq.start(ts, LISTS);
-    bool need = (n0 + kKN > Nk);
+    bool need = n0 > need_above || n0 < need_below;
     bool elem = true, hide = false;
     if constexpr (LISTS) {
       const uint32_t c = seq.cls(ts, 0, true);
       hide = c == 0u;
       elem = c == 1u;
       need = need || c != 2u;
-    } else {
-      const int last = n0 + kKN - 1;
-      if (mk == kMaskCausal) need = need || (last > qw + delta);
-      else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
-      else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
-      else if (mk == kMaskBlockDiag) need = true;
     }
-    // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents)
-    int lo = 0, hi = Nk;
+    // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents);
+    // rows past Nq carry rowv = +inf, so their P is 0 whatever the test says
     const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
-    // wave-uniform; rows past Nq carry rowv = +inf, so their P is 0 whatever the test says
-    const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;
-    if (need) {
-      if (hide) hi = 0;
-      else if (elem && qrow < Nq && mk != kMaskBlockDiag) band_interval(p.mask, qrow, Nq, Nk, lo, hi);
-      hi = min(hi, Nk);
-    }
+    const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;   // wave-uniform
+    const bool band = elem && mk != kMaskBlockDiag;
+    const int lo = band ? band_lo : 0, hi = hide ? 0 : band ? band_hi : Nk;
     const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
     auto body = [&](auto test_c) {
       constexpr int TEST = decltype(test_c)::value;
@@ -732,8 +696,24 @@ void bwd_dq_kernel(const BwdParams bp) {
     __syncthreads();
   };
 
-  if (T > 0) {
-    if (role == 0) {
+  // ---- epilogue (dQ wave): lane = query, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4;
+  // on the dQ waves' own path, so the S waves do not keep dq[] live through their loop
+  auto store = [&]() {
+    if (qrow >= Nq) return;
+    __bf16* dQg = (__bf16*)bp.dq + b * bp.dqs_b + h * bp.dqs_h + (int64_t)qrow * bp.dqs_s;
+#pragma unroll
+    for (int db = 0; db < DQK / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x2 v;
+        v[0] = pack_bf16x2(dq[db][4 * jj] * p.scale, dq[db][4 * jj + 1] * p.scale);
+        v[1] = pack_bf16x2(dq[db][4 * jj + 2] * p.scale, dq[db][4 * jj + 3] * p.scale);
+        *(u32x2*)(dQg + 32 * db + 8 * jj + 4 * g) = v;
+      }
+  };
+
+  if (role == 0) {
+    if (T > 0) {
       for (int t = 0; t < T; ++t) {
         step_begin(t);
         matrix_s(t);
@@ -744,7 +724,9 @@ void bwd_dq_kernel(const BwdParams bp) {
       step_begin(T);
       mid();
       step_end(T);
-    } else {
+    }
+  } else {
+    if (T > 0) {
       step_begin(0);
       mid();
       matrix_dq(0, false, true);
@@ -762,20 +744,7 @@ void bwd_dq_kernel(const BwdParams bp) {
       matrix_dq(T, true, false);
       step_end(T);
     }
-  }
-
-  // ---- epilogue (dQ wave): lane = query, reg r <-> d = 32 db + 8 (r/4) + 4 g + r % 4
-  if (role != 0 && qrow < Nq) {
-    __bf16* dQg = (__bf16*)bp.dq + b * bp.dqs_b + h * bp.dqs_h + (int64_t)qrow * bp.dqs_s;
-#pragma unroll
-    for (int db = 0; db < DQK / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x2 v;
-        v[0] = pack_bf16x2(dq[db][4 * jj] * p.scale, dq[db][4 * jj + 1] * p.scale);
-        v[1] = pack_bf16x2(dq[db][4 * jj + 2] * p.scale, dq[db][4 * jj + 3] * p.scale);
-        *(u32x2*)(dQg + 32 * db + 8 * jj + 4 * g) = v;
-      }
+    store();
   }
 }
 

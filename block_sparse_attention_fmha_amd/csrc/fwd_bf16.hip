@@ -150,6 +150,15 @@ void fwd_bf16_kernel(const AttnParams p) {
   const int trow = 8 * g + ((l & 15) >> 2);
   const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
   const int grp = w >> 2;   // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
+  // element-mask geometry, computed once: tiles starting past need_above or before
+  // need_below need the mask; the lane's row sees keys band_lo <= j < band_hi (band
+  // masks) or the keys of its document (block-diagonal mask)
+  int need_above, need_below;
+  key_tile_need(p.mask, qw, Nk, delta, kBN, need_above, need_below);
+  if constexpr (LISTS) need_above = Nk - kBN, need_below = INT32_MIN;   // the list classes decide
+  int band_lo, band_hi;
+  band_interval(p.mask, qrow, Nq, Nk, band_lo, band_hi);
+  const int row_doc = (mk == kMaskBlockDiag && qrow < Nq) ? p.mask.doc_q[(int64_t)b * Nq + qrow] : 0;
 
   LdsDma<kBN, DQK, SM::KPC, kThreads> kdma;
   LdsDma<kBN, DV, SM::VPC, kThreads> vdma;
@@ -215,19 +224,13 @@ void fwd_bf16_kernel(const AttnParams p) {
 
   auto vector = [&](int ts) {
     const int n0 = seq.start(ts, LISTS);
-    bool need = (n0 + kBN > Nk);
+    bool need = n0 > need_above || n0 < need_below;
     bool elem = true, hide = false;
     if constexpr (LISTS) {
       const uint32_t c = seq.cls(ts, grp, true);   // this wave's query half
       hide = c == 0u;
       elem = c == 1u;
       need = need || c != 2u;
-    } else {
-      const int last = n0 + kBN - 1;
-      if (mk == kMaskCausal) need = need || (last > qw + delta);
-      else if (mk == kMaskWindow) need = need || (last > qw + delta) || (n0 < qw + 31 + delta - p.mask.window);
-      else if (mk == kMaskPrefix) need = need || (last > qw + delta && last >= p.mask.prefix);
-      else if (mk == kMaskBlockDiag) need = true;
     }
     // score transform (softcap / bias) and mask; reg r of block kb holds key
     // n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of query row qrow.
@@ -239,7 +242,13 @@ void fwd_bf16_kernel(const AttnParams p) {
         for (int r = 0; r < 16; ++r)
           s[kb][r] = score_log2<SOFTCAP, BIAS>(s[kb][r], p, qrow, jb + 32 * kb + 16 * (r >> 3) + (r & 7));
     }
-    if (need) mask_tile(s, p.mask, b, qrow, opaque_int(n0 + 8 * g), Nq, Nk, elem && qrow < Nq, hide);
+    if (need) {
+      // rows past Nq are never stored, so their mask does not matter
+      const int kbase = opaque_int(n0 + 8 * g);
+      if (hide) mask_tile_band(s, kbase, 0, 0);
+      else if (elem && mk == kMaskBlockDiag) mask_tile_doc(s, p.mask.doc_k + (int64_t)b * Nk, row_doc, kbase, Nk);
+      else mask_tile_band(s, kbase, elem ? band_lo : 0, elem ? band_hi : Nk);
+    }
 
     // online softmax (log2 domain). The O / l rescale is skipped when no row of the
     // wave raised its running max. O already holds every P V up to tile ts - 1.

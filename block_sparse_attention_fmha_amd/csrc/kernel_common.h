@@ -391,32 +391,8 @@ __device__ __forceinline__ void band_interval(const MaskParams& m, int i, int nq
 // Set to -inf the entries of a 32-query x 64-key S^T tile (lane = query row, the layout of
 // S^T = K Q^T with permuted K rows) whose key is hidden from the lane's query row.
 // Register r of block kb holds key kbase + 32 kb + 16 (r / 8) + r % 8 (kbase = tile start
-// + 8 g).
-// `elem` = apply the element mask (else only keys past Nk are hidden); `hide` = hide all.
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const MaskParams& m, int b, int qrow, int kbase,
-                                          int nq, int nk, bool elem, bool hide) {
-  if (hide) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = kNegInf;
-    return;
-  }
-  if (elem && m.kind == kMaskBlockDiag) {
-    const int dq = m.doc_q[(int64_t)b * nq + qrow];
-    const int* dk = m.doc_k + (int64_t)b * nk;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kbase + 32 * kb + 16 * (r >> 3) + (r & 7);
-        const bool vis = j < nk && dk[min(j, nk - 1)] == dq;
-        s[kb][r] = vis ? s[kb][r] : kNegInf;
-      }
-    return;
-  }
-  int lo = 0, hi = nk;
-  if (elem) band_interval(m, qrow, nq, nk, lo, hi);
+// + 8 g). Keys lo <= j < hi stay visible (an interval computed once per row).
+__device__ __forceinline__ void mask_tile_band(f32x16 (&s)[2], int kbase, int lo, int hi) {
   // key j visible iff lo <= j < hi, i.e. (unsigned)(j - lo) < (unsigned)(hi - lo)
   const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
   const int base = kbase - lo;
@@ -427,6 +403,33 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const MaskParams& m, i
       const unsigned rel = (unsigned)(base + 32 * kb + 16 * (r >> 3) + (r & 7));
       s[kb][r] = rel < span ? s[kb][r] : kNegInf;
     }
+}
+
+// Document (block-diagonal) variant: key j visible iff j < nk and its document is dq.
+__device__ __forceinline__ void mask_tile_doc(f32x16 (&s)[2], const int* doc_k, int dq, int kbase, int nk) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = kbase + 32 * kb + 16 * (r >> 3) + (r & 7);
+      const bool vis = (j < nk) & (doc_k[min(j, nk - 1)] == dq);   // unconditional (clamped) load
+      s[kb][r] = vis ? s[kb][r] : kNegInf;
+    }
+}
+
+// Tiles of a row band that need the element mask: with tile start n0 (a multiple of
+// `tile`), the mask can hide something only if n0 > above or n0 < below. Computed once
+// per wave from the band masks' geometry for rows [r0, r0 + 32) (n_other = the column
+// side's length, delta = Nk - Nq), so the per-tile test is two scalar compares.
+// Columns here are keys (forward and dQ passes).
+__device__ __forceinline__ void key_tile_need(const MaskParams& m, int r0, int nk, int delta, int tile,
+                                              int& above, int& below) {
+  above = nk - tile;            // ragged last tile
+  below = INT32_MIN;
+  if (m.kind == kMaskCausal || m.kind == kMaskWindow) above = min(above, r0 + delta - tile + 1);
+  if (m.kind == kMaskPrefix) above = min(above, max(r0 + delta - tile + 1, m.prefix - tile));
+  if (m.kind == kMaskWindow) below = r0 + 31 + delta - m.window;
+  if (m.kind == kMaskBlockDiag) above = -1;
 }
 
 // ---------------------------------------------------------------------------------------
