@@ -212,22 +212,34 @@ __device__ __forceinline__ int swap_bits23(int m) {
 // the next LDS read, even when that read targets a different tile, which serialises the
 // prefetch with the MFMA phase. Callers order it explicitly instead: wait_lds_dma() and
 // a barrier before the destination tile is read, and never read a tile while its DMA is
-// in flight. gbase and lds_block must be wave-uniform. M0 has no other user in these
-// kernels.
-__device__ __forceinline__ void dma_16b(const char* gbase, uint32_t voff, const char* lds_block) {
+// in flight. M0 has no other user in these kernels. Here the bases are already
+// wave-uniform (SGPR values): gu = global byte address, laddr = LDS byte address of the
+// 1 KiB block; dma_16b below takes pointers instead.
+__device__ __forceinline__ void dma_16b_u(uint64_t gu, uint32_t voff, uint32_t laddr) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // both bases are wave-uniform by contract; readfirstlane makes that visible to the
-  // compiler where it cannot prove it (free when the value already sits in an SGPR)
-  // (the flat address of an LDS location holds its LDS offset in the low 32 bits)
-  const uint32_t laddr = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_block);
-  const uint64_t ga = (uint64_t)(uintptr_t)gbase;
-  // readfirstlane returns int: go through uint32_t so the low word is zero-extended
-  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
-  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
-  const uint64_t gu = ((uint64_t)ghi << 32) | (uint64_t)glo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"((const char*)(uintptr_t)gu), "s"(laddr) : "memory");
 #endif
+}
+
+// Wave-uniform copies of a global pointer and of the LDS offset of an LDS pointer. Both
+// must be wave-uniform by contract; readfirstlane makes that visible to the compiler where
+// it cannot prove it (free when the value already sits in an SGPR).
+__device__ __forceinline__ uint64_t uniform_addr(const void* gp) {
+  const uint64_t ga = (uint64_t)(uintptr_t)gp;
+  // readfirstlane returns int: go through uint32_t so the low word is zero-extended
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
+  return ((uint64_t)ghi << 32) | (uint64_t)glo;
+}
+// (the flat address of an LDS location holds its LDS offset in the low 32 bits)
+__device__ __forceinline__ uint32_t uniform_lds(const void* lp) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lp);
+}
+
+// Pointer form of dma_16b_u; gbase and lds_block must be wave-uniform.
+__device__ __forceinline__ void dma_16b(const char* gbase, uint32_t voff, const char* lds_block) {
+  dma_16b_u(uniform_addr(gbase), voff, uniform_lds(lds_block));
 }
 
 // s_waitcnt vmcnt(n) for a run-time n (wave-uniform); n above 15 waits for 15, which is
@@ -299,20 +311,22 @@ struct LdsDma {
   __device__ __forceinline__ void issue_part(const __bf16* g, int64_t row_stride, int row0, int nrows,
                                              char* lds_tile) const {
     const int left = nrows - row0;
-    const char* base = (const char*)(g + (int64_t)row0 * row_stride);
+    // bases made uniform once per call, not once per instruction
+    const uint64_t base = uniform_addr(g + (int64_t)row0 * row_stride);
+    const uint32_t lbase = uniform_lds(lds_tile) + (uint32_t)w * 1024u;
     const int cnt = __builtin_amdgcn_readfirstlane(count());   // scalar: blocks of this wave
     if (left >= ROWS) {
 #pragma unroll
       for (int j = PART; j < NI; j += NPART) {
         if (j >= cnt) break;
-        dma_16b(base, off[j], lds_tile + (j * NW + w) * 1024);
+        dma_16b_u(base, off[j], lbase + (uint32_t)(j * NW) * 1024u);
       }
     } else {
       const uint32_t lim = (uint32_t)(left * (int)(row_stride * 2));
 #pragma unroll
       for (int j = PART; j < NI; j += NPART) {
         if (j >= cnt) break;
-        dma_16b(base, off[j] < lim ? off[j] : 0u, lds_tile + (j * NW + w) * 1024);
+        dma_16b_u(base, off[j] < lim ? off[j] : 0u, lbase + (uint32_t)(j * NW) * 1024u);
       }
     }
   }
