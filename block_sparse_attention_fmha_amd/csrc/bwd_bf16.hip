@@ -112,45 +112,6 @@ struct DkdvSmem {
   static constexpr int BYTES = NST * STAGE + XB;
 };
 
-// One matrix phase of a dK/dV wave. First acc^T += T^T bop for the previous step (T = dO
-// for the P wave, Q for the dS wave, read transposed; DA = its width), then
-// s = R bf^T for the current step (R = Q for the P wave, dO for the dS wave, rows in the
-// permuted order; DR = its width). Either half may be absent. toff / roff: LDS byte
-// offsets of the lane's first T and R reads; they are made opaque so that every other
-// read of the phase is a constant immediate offset from them (otherwise the compiler
-// keeps dozens of precomputed addresses in registers across the main loop).
-template <int DR, int DA, int RP, int TP, int NBF, int NACC>
-__device__ __forceinline__ void dkdv_matrix(const char* lds, int toff, int roff, bool do_acc, bool do_s,
-                                            f32x16 (&acc)[NACC], const bf16x8 (&bop)[2][2], f32x16 (&s)[2],
-                                            const bf16x8 (&bf)[NBF]) {
-  if (do_acc) {
-    const char* t0 = lds + opaque_int(toff);
-#pragma unroll
-    for (int db = 0; db < DA / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const char* tp = t0 + (32 * kb + 16 * hh) * TP + 64 * db;
-          const u32x2 lo = lds_read_tr(tp);
-          const u32x2 hi = lds_read_tr(tp + 4 * TP);
-          acc[db] = mfma_bf16(join_bf16x8(lo, hi), bop[kb][hh], acc[db]);
-        }
-  }
-  if (do_s) {
-    const char* rp = lds + opaque_int(roff);
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < DR / 16; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(rp + 32 * ks);
-      const bf16x8 a1 = *(const bf16x8*)(rp + 32 * RP + 32 * ks);
-      s[0] = mfma_bf16(a0, bf[ks], s[0]);
-      s[1] = mfma_bf16(a1, bf[ks], s[1]);
-    }
-  }
-}
-
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
 void bwd_dkdv_kernel(const BwdParams bp) {
@@ -276,8 +237,10 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     const int tv = ts - 1;
     const int sv = ((tv < 0 ? 0 : tv) % SM::NST) * SM::STAGE + (R ? 0 : SM::QB);
     const int ss = (ts % SM::NST) * SM::STAGE + (R ? SM::QB : 0);
-    dkdv_matrix<DR, DA, RP, TP>(smem, sv + trow * TP + tcol * 2, ss + prow * RP + 16 * g, do_acc, do_s, acc, bop,
-                                s, bf);
+    // one software pipeline: acc^T += T^T bop for the previous step, then s = R bf^T
+    pipelined_matrix<4 * (DA / 32), DR / 16, TP, RP, 2>(smem + opaque_int(sv + trow * TP + tcol * 2),
+                                                         smem + opaque_int(ss + prow * RP + 16 * g), do_acc, do_s,
+                                                         acc, bop, s, bf);
   };
 
   // P wave: P_ts = exp2(s * scale_log2 - lse2) (score transform and element mask applied),
@@ -566,48 +529,17 @@ void bwd_dq_kernel(const BwdParams bp) {
   // The hand-over of tile t is written in phase 2t+1 and read in phase 2t+2; tile t's
   // stage is read during phases 2t .. 2t+3. Each role runs its own loop (first and last
   // steps peeled) so nothing conditional sits between the phases.
+  // S^T of tile ts: A = K rows in the permuted order, width DQK
   auto matrix_s = [&](int ts) {
-    // A = K rows in the permuted order, width DQK
-    const char* ap = smem + opaque_int((ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g);
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(ap + 32 * ks);
-      const bf16x8 a1 = *(const bf16x8*)(ap + 32 * SM::KP + 32 * ks);
-      s[0] = mfma_bf16(a0, bf[ks], s[0]);
-      s[1] = mfma_bf16(a1, bf[ks], s[1]);
-    }
+    const char* k0 = smem + opaque_int((ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g);
+    pipelined_matrix<0, DQK / 16, SM::KP, SM::KP, 2>(k0, k0, false, true, dq, dsb, s, bf);
   };
+  // dQ^T += K^T dS^T of tile ts - 1 (K read transposed), then dP^T of tile ts (A = V rows
+  // in the permuted order, width DV)
   auto matrix_dq = [&](int ts, bool do_acc, bool do_s) {
-    if (do_acc) {
-      // dQ^T += K^T dS^T of tile ts - 1 (K read transposed)
-      const char* kp0 = smem + opaque_int(((ts - 1) % SM::NST) * SM::STAGE + trow * SM::KP + tcol * 2);
-#pragma unroll
-      for (int db = 0; db < DQK / 32; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const char* kp = kp0 + (32 * kb + 16 * hh) * SM::KP + 64 * db;
-            const u32x2 lo = lds_read_tr(kp);
-            const u32x2 hi = lds_read_tr(kp + 4 * SM::KP);
-            dq[db] = mfma_bf16(join_bf16x8(lo, hi), dsb[kb][hh], dq[db]);
-          }
-    }
-    if (do_s) {
-      // dP^T: A = V rows in the permuted order, width DV
-      const char* ap = smem + opaque_int((ts % SM::NST) * SM::STAGE + SM::KB + prow * SM::VP + 16 * g);
-      s[0] = f32x16{};
-      s[1] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks) {
-        const bf16x8 a0 = *(const bf16x8*)(ap + 32 * ks);
-        const bf16x8 a1 = *(const bf16x8*)(ap + 32 * SM::VP + 32 * ks);
-        s[0] = mfma_bf16(a0, bf[ks], s[0]);
-        s[1] = mfma_bf16(a1, bf[ks], s[1]);
-      }
-    }
+    const char* k0 = smem + opaque_int(((ts - 1 + SM::NST) % SM::NST) * SM::STAGE + trow * SM::KP + tcol * 2);
+    const char* v0 = smem + opaque_int((ts % SM::NST) * SM::STAGE + SM::KB + prow * SM::VP + 16 * g);
+    pipelined_matrix<4 * (DQK / 32), DV / 16, SM::KP, SM::VP, 2>(k0, v0, do_acc, do_s, dq, dsb, s, bf);
   };
 
   // S wave: P of tile ts (score transform, element mask, exp against the row's lse2) into

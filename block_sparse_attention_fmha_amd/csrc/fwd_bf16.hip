@@ -189,37 +189,12 @@ void fwd_bf16_kernel(const AttnParams p) {
   // done. Each group runs its own loop with the first and last steps peeled, so nothing
   // conditional sits between the phases and the loop-carried operands keep their
   // registers.
+  // Matrix phase: O += V(ts - 1) P (V read transposed) and S = K Q^T (two accumulation
+  // chains), one software pipeline with the LDS reads issued two items ahead
   auto matrix = [&](int ts, bool do_acc, bool do_s) {
-    if (do_acc) {
-      // O += V(ts - 1) P, V read transposed at immediate offsets from one per-lane base
-      const char* v0 = smem + opaque_int(((ts - 1) % SM::NST) * SM::STAGE + SM::KB + trow * SM::VP + tcol * 2);
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const char* vp = v0 + (32 * kb + 16 * hh) * SM::VP + 64 * db;
-            const u32x2 lo = lds_read_tr(vp);
-            const u32x2 hi = lds_read_tr(vp + 4 * SM::VP);
-            o[db] = mfma_bf16(join_bf16x8(lo, hi), pb[kb][hh], o[db]);
-          }
-        }
-      }
-    }
-    if (do_s) {
-      // two independent accumulation chains (key blocks) interleaved
-      const char* Kl = smem + opaque_int((ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g);
-      s[0] = f32x16{};
-      s[1] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks) {
-        const bf16x8 a0 = *(const bf16x8*)(Kl + 32 * ks);
-        const bf16x8 a1 = *(const bf16x8*)(Kl + 32 * SM::KP + 32 * ks);
-        s[0] = mfma_bf16(a0, qf[ks], s[0]);
-        s[1] = mfma_bf16(a1, qf[ks], s[1]);
-      }
-    }
+    const char* v0 = smem + opaque_int(((ts - 1 + SM::NST) % SM::NST) * SM::STAGE + SM::KB + trow * SM::VP + tcol * 2);
+    const char* k0 = smem + opaque_int((ts % SM::NST) * SM::STAGE + prow * SM::KP + 16 * g);
+    pipelined_matrix<4 * (DV / 32), DQK / 16, SM::VP, SM::KP, 2>(v0, k0, do_acc, do_s, o, pb, s, qf);
   };
 
   auto vector = [&](int ts) {

@@ -151,6 +151,68 @@ __device__ __forceinline__ bf16x8 join_bf16x8(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// One matrix phase as a software pipeline over "items": NA accumulation items
+// (acc[i / 4] += T^T bop[(i / 2) % 2][i % 2], one MFMA and two transposed 8-byte reads
+// each) followed by NS score items (s[0], s[1] += R bf[ks]^T, two MFMAs and two 16-byte
+// row reads each). The LDS reads of item i + AHEAD are issued right after the MFMAs of
+// item i and the scheduler is fenced per item, so they stay in flight across the MFMAs
+// instead of being sunk next to their use (left to itself the compiler keeps only one or
+// two reads in flight and every MFMA waits out the LDS latency).
+//   t0: the lane's first transposed-read address (row trow, column tcol of the T tile;
+//       item (db, kb, hh) reads rows + 32 kb + 16 hh and + 4, columns + 32 db)
+//   r0: the lane's first row-read address (permuted row, half g of the R tile; score
+//       item ks reads 16-byte chunk 2 ks and the same 32 rows further)
+// Either part may be absent (do_acc / do_s); s is cleared when do_s.
+template <int NA, int NS, int TP, int RP, int AHEAD, int NACC, int NBF>
+__device__ __forceinline__ void pipelined_matrix(const char* t0, const char* r0, bool do_acc, bool do_s,
+                                                 f32x16 (&acc)[NACC], const bf16x8 (&bop)[2][2],
+                                                 f32x16 (&s)[2], const bf16x8 (&bf)[NBF]) {
+  struct Operand { bf16x8 a, b; };
+  constexpr int N = NA + NS;
+  auto load = [&](int i) {
+    Operand op;
+    if (i < NA) {
+      const int db = i >> 2, kb = (i >> 1) & 1, hh = i & 1;
+      const char* tp = t0 + (32 * kb + 16 * hh) * TP + 64 * db;
+      const u32x2 lo = lds_read_tr(tp);
+      const u32x2 hi = lds_read_tr(tp + 4 * TP);
+      op.a = join_bf16x8(lo, hi);
+    } else {
+      const int ks = i - NA;
+      op.a = *(const bf16x8*)(r0 + 32 * ks);
+      op.b = *(const bf16x8*)(r0 + 32 * RP + 32 * ks);
+    }
+    return op;
+  };
+  auto run = [&](int i, const Operand& op) {
+    if (i < NA) {
+      const int db = i >> 2, kb = (i >> 1) & 1, hh = i & 1;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.a, bop[kb][hh], acc[db], 0, 0, 0);
+    } else {
+      const int ks = i - NA;
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.a, bf[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.b, bf[ks], s[1], 0, 0, 0);
+    }
+  };
+  const int first = do_acc ? 0 : NA, last = do_s ? N : NA;
+  if (do_s) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+  }
+  Operand ring[AHEAD];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i >= first && i < first + AHEAD && i < last) ring[i % AHEAD] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < first || i >= last) continue;
+    __builtin_amdgcn_sched_barrier(0);
+    run(i, ring[i % AHEAD]);
+    if (i + AHEAD < last) ring[i % AHEAD] = load(i + AHEAD);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Is key j visible from query i under the element mask (delta = Nk - Nq)?
 __device__ __forceinline__ bool mask_visible(const MaskParams& m, int b, int i, int j, int nq,
                                              int nk) {
