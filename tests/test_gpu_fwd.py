@@ -96,18 +96,22 @@ def test_fwd_bf16_strided_bhsd_layout():
 
 
 FP32_SMALL = [
-    (1, 128, 128, 1, 64, "causal"),      # the fp32 parity workload
-    (2, 150, 170, 2, 64, "none"),
-    (1, 200, 200, 2, 128, "sliding_window"),
-    (1, 100, 130, 2, 1024, "causal"),
+    # (B, Nq, Nk, H, D, kind, prefix)
+    (1, 128, 128, 1, 64, "causal", 0),      # the fp32 parity workload
+    (2, 150, 170, 2, 64, "none", 0),
+    (1, 200, 200, 2, 128, "sliding_window", 0),
+    (1, 100, 130, 2, 1024, "causal", 0),
+    (1, 600, 600, 1, 64, "block_diagonal", 0),
+    (1, 130, 160, 2, 128, "prefix_lm", 70),
+    (1, 90, 90, 2, 1024, "prefix_lm", 40),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(FP32_SMALL)))
 def test_fwd_fp32_small(case):
-    B, Nq, Nk, H, D, kind = FP32_SMALL[case]
+    B, Nq, Nk, H, D, kind, prefix = FP32_SMALL[case]
     seed = synth.case_seed(1, 0) if case == 0 else synth.case_seed(9, 100 + case)
-    _case(seed, B, Nq, Nk, H, D, D, "fp32", kind, window=50)
+    _case(seed, B, Nq, Nk, H, D, D, "fp32", kind, window=50, prefix=prefix)
 
 
 # ------------------------------------------------------------------ full-size workloads
