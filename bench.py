@@ -142,6 +142,34 @@ def gpu_step_timing(steps: int, warmup: int):
     return total_ms / steps, per
 
 
+def profile_other_rows(reps: int):
+    """For rocprofv3 runs: `reps` launches each of the split-KV decode (B=8 H=32 Nq=1
+    Nk=32768 D=128, 16 splits; partial + combine kernels), the fp32 wide-head forward
+    (B=4 H=8 N=512 D=1024) and the block-sparse causal forward (B=2 H=8 N=8192 D=128,
+    128 x 128 tiles, relative bias) with its block-mask build."""
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    dev = torch.device("cuda:0")
+    q = torch.randn(8, 1, 32, 128, device=dev).bfloat16()
+    k = torch.randn(8, 32768, 32, 128, device=dev).bfloat16()
+    v = torch.randn(8, 32768, 32, 128, device=dev).bfloat16()
+    for _ in range(reps):
+        fa.fmha_fwd_splitkv(q, k, v, 16)
+    torch.cuda.synchronize()
+    del q, k, v
+    q, k, v = (torch.randn(4, 512, 8, 1024, device=dev) for _ in range(3))
+    for _ in range(reps):
+        fa.fmha_fwd(q, k, v)
+    torch.cuda.synchronize()
+    del q, k, v
+    q, k, v = (torch.randn(2, 8192, 8, 128, device=dev).bfloat16() for _ in range(3))
+    m = fa.Mask("causal")
+    for _ in range(reps):
+        bs = fa.build_block_mask(m, 2, 8192, 8192, 128, 128)
+        fa.fmha_fwd(q, k, v, mask=m, bias_slope=-0.01, block_sparse=bs)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline():
     """The CPU fp64 oracle, as it stands, on one head of the workload (fwd + bwd)."""
     import numpy as np
@@ -167,7 +195,7 @@ def all_configs_report():
     import numpy as np
     import torch
     import block_sparse_attention_fmha_amd as fa
-    from block_sparse_attention_fmha_amd import synth
+    from block_sparse_attention_fmha_amd import synth  # document ids (data only)
     dev = torch.device("cuda:0")
 
     def timeit(fn, reps=20, warm=3):
@@ -219,6 +247,67 @@ def all_configs_report():
     f = 2.0 * 4 * 8 * 2048 * 512 * 512
     log(workload="fwd_fp32_d1024", ms=round(ms, 4), tflops=round(f / ms / 1e9, 2),
         frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 4))
+    del q, k, v
+    # fp32 parity workload (latency-bound: one 32-row workgroup)
+    q, k, v = (torch.randn(1, 128, 1, 64, device=dev) for _ in range(3))
+    m = fa.Mask("causal")
+    ms = timeit(lambda: fa.fmha_fwd(q, k, v, mask=m))
+    f = 2.0 * 2 * 64 * causal_pairs(128)
+    log(workload="fwd_fp32_n128_d64_causal", ms=round(ms, 4), tflops=round(f / ms / 1e9, 4),
+        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 6))
+    # block-sparse forward: B=2 H=8 N=8192 D=128, 128 x 128 sparse tiles from the element
+    # mask, relative bias -0.01 |i - j|; useful FLOPs on the visible pairs only
+    n, bsz, hh = 8192, 2, 8
+    q, k, v = (torch.randn(bsz, n, hh, 128, device=dev).bfloat16() for _ in range(3))
+    docs = synth.document_ids(synth.case_seed(3, 2), bsz, n)
+    dev_docs = torch.from_numpy(docs).to(dev)
+    for kind, w_, p_ in (("causal", 0, 0), ("sliding_window", 2730, 0), ("block_diagonal", 0, 0),
+                         ("prefix_lm", 0, 1024)):
+        m = fa.Mask(kind, window=w_, prefix=p_, doc_q=dev_docs if kind == "block_diagonal" else None,
+                    doc_k=dev_docs if kind == "block_diagonal" else None)
+        ms_bm = timeit(lambda: fa.build_block_mask(m, bsz, n, n, 128, 128))
+        bs = fa.build_block_mask(m, bsz, n, n, 128, 128)
+        ms = timeit(lambda: fa.fmha_fwd(q, k, v, mask=m, bias_slope=-0.01, block_sparse=bs))
+        a = visible_pairs(kind, n, w_, p_, docs)
+        f = 2.0 * hh * 256 * a
+        tiles = int(bs.partial_cnt.sum().item() + bs.full_cnt.sum().item())
+        log(workload="fwd_bf16_block_sparse", N=n, B=bsz, H=hh, D=128, mask=kind, ms=round(ms, 4),
+            tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            visited_tiles=tiles, of_tiles=bsz * (n // 128) ** 2, build_block_mask_ms=round(ms_bm, 4))
+    del q, k, v
+    # backward workloads (causal, B=1 H=16), incl. the MLA-shaped head Dqk=192 Dv=128
+    for n, dqk, dv in ((4096, 64, 64), (4096, 128, 128), (16384, 64, 64), (8192, 192, 128)):
+        q = torch.randn(1, n, 16, dqk, device=dev).bfloat16()
+        k = torch.randn(1, n, 16, dqk, device=dev).bfloat16()
+        v = torch.randn(1, n, 16, dv, device=dev).bfloat16()
+        do = torch.randn(1, n, 16, dv, device=dev).bfloat16()
+        m = fa.Mask("causal")
+        out, lse = fa.fmha_fwd(q, k, v, mask=m)
+        dq, dk, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.bwd_workspace_size(1, 16, n), dtype=torch.uint8, device=dev)
+        ms = timeit(lambda: fa.fmha_bwd(q, k, v, out, lse, do, mask=m, dq=dq, dk=dk, dv=dv_, workspace=ws))
+        f = useful_flops(1, 16, causal_pairs(n), dqk, dv)[1]
+        log(workload="bwd_bf16", N=n, Dqk=dqk, Dv=dv, mask="causal", ms=round(ms, 4),
+            tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+        del q, k, v, do, out, lse, dq, dk, dv_, ws
+
+
+def visible_pairs(kind, n, window, prefix, docs):
+    """Visible (i, j) pairs summed over the batch rows (Nq = Nk = n)."""
+    import numpy as np
+    rows = docs.shape[0]
+    i = np.arange(n, dtype=np.int64)
+    if kind == "causal":
+        per = int((i + 1).sum())
+    elif kind == "sliding_window":
+        per = int((np.minimum(i, window) + 1).sum())
+    elif kind == "prefix_lm":
+        per = int(np.minimum(n, np.maximum(prefix, i + 1)).sum())
+    elif kind == "block_diagonal":
+        return int(sum((np.bincount(docs[b]).astype(np.int64) ** 2).sum() for b in range(rows)))
+    else:
+        per = n * n
+    return per * rows
 
 
 def main():
@@ -240,6 +329,7 @@ def main():
     if args.profile:
         import torch
         step_ms, per = gpu_step_timing(args.steps, args.warmup)
+        profile_other_rows(args.steps)
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
