@@ -7,14 +7,17 @@
 // only on partial tiles ("Summary"). The page also records a latent out-of-bounds bug in
 // mask definitions; here the predicate is never evaluated outside [0, Nq) x [0, Nk).
 //
-// One workgroup per (b, mask head, tile row). Each thread classifies whole tiles: it
-// counts the visible in-bounds elements of its tile row by row -- in closed form for the
-// band masks (causal, sliding window, prefix-LM: the visible keys of a row are one
-// interval) and by comparing document ids for the block-diagonal mask -- then compares
-// the count with the tile's in-bounds size (0 = empty, all = full, else partial). The
-// classes go to LDS and one thread compacts them into ascending lists (slots past the
-// count are -1). The transposed lists are produced by the same kernel with the roles of
-// the two axes swapped, so both orientations come from one classification function.
+// One workgroup per (b, mask head, tile row). Each tile's visible in-bounds elements are
+// counted and compared with the tile's in-bounds size (0 = empty, all = full, else
+// partial). For the band masks (causal, sliding window, prefix-LM: the visible keys of a
+// row are one interval) each thread counts whole tiles in closed form, row by row. For
+// the block-diagonal mask the workgroup stages the document ids of the column axis in
+// LDS (in chunks); every thread takes one row element and a slice of the column tiles,
+// counts the matching ids of each tile, and the counts are summed exactly in one 64-bit
+// LDS counter per tile. The classes go to LDS and one thread compacts them into ascending lists
+// (slots past the count are -1). The transposed lists are produced by the same kernel
+// with the roles of the two axes swapped, so both orientations come from one
+// classification.
 #include "kernel_common.h"
 #include "launch.h"
 
@@ -22,28 +25,31 @@ namespace fmha {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kIdChunk = 8192;     // document ids staged in LDS at a time
+constexpr int kMaxCounted = 4096;  // tiles per row counted in one pass (one 64-bit LDS counter each)
 
-// visible keys of query row i inside [k0, k1)
-__device__ __forceinline__ int64_t row_visible(const MaskParams& m, int b, int i, int k0, int k1, int nq,
-                                               int nk) {
+// dynamic LDS layout: tile classes (n_cols bytes), id chunk, 64-bit counters
+__host__ __device__ constexpr int ids_offset(int n_cols) { return (n_cols + 15) / 16 * 16; }
+__host__ __device__ constexpr int cnt_offset(int n_cols) { return ids_offset(n_cols) + kIdChunk * 4; }
+__host__ __device__ constexpr int lds_bytes(int n_cols) {
+  return cnt_offset(n_cols) + 8 * (n_cols < kMaxCounted ? n_cols : kMaxCounted) + 16;
+}
+
+// visible keys of query row i inside [k0, k1) under a band mask
+__device__ __forceinline__ int64_t row_visible(const MaskParams& m, int i, int k0, int k1, int nq, int nk) {
   const int d = nk - nq;
   int lo = k0, hi = k1;
   switch (m.kind) {
-    case kMaskNone: break;
     case kMaskCausal: hi = min(k1, i + d + 1); break;
     case kMaskWindow: lo = max(k0, i + d - m.window); hi = min(k1, i + d + 1); break;
     case kMaskPrefix: hi = min(k1, max(m.prefix, i + d + 1)); break;
-    case kMaskBlockDiag: {
-      const int di = m.doc_q[(int64_t)b * nq + i];
-      const int* dk = m.doc_k + (int64_t)b * nk;
-      int64_t c = 0;
-      for (int j = k0; j < k1; ++j) c += (dk[j] == di);
-      return c;
-    }
     default: break;
   }
   return hi > lo ? hi - lo : 0;
 }
+
+// end of the tile starting at t0 with size ts, clipped to n (no int overflow)
+__device__ __forceinline__ int tile_end(int t0, int ts, int n) { return (int)min((int64_t)n, (int64_t)t0 + ts); }
 
 // TRANSPOSED = false: grid rows are query tiles, entries are key tiles.
 // TRANSPOSED = true:  grid rows are key tiles, entries are query tiles.
@@ -51,19 +57,68 @@ template <bool TRANSPOSED>
 __global__ __launch_bounds__(kThreads)
 void classify_kernel(const MaskParams m, int Hm, int nq, int nk, int tile_m, int tile_n, int n_rows,
                      int n_cols, int* pcnt, int* pidx, int* fcnt, int* fidx) {
-  extern __shared__ unsigned char cls[];
+  extern __shared__ __attribute__((aligned(16))) unsigned char cls[];
   const int row = blockIdx.x % n_rows;
   const int bhm = blockIdx.x / n_rows;
   const int b = bhm / Hm;
-  for (int col = threadIdx.x; col < n_cols; col += kThreads) {
-    const int qt = TRANSPOSED ? col : row;
-    const int kt = TRANSPOSED ? row : col;
-    const int q0 = qt * tile_m, q1 = min(nq, q0 + tile_m);
-    const int k0 = kt * tile_n, k1 = min(nk, k0 + tile_n);
-    int64_t vis = 0;
-    for (int i = q0; i < q1; ++i) vis += row_visible(m, b, i, k0, k1, nq, nk);
-    const int64_t all = (int64_t)(q1 - q0) * (k1 - k0);
-    cls[col] = (vis == 0) ? 0 : (vis == all ? 2 : 1);
+  if (m.kind == kMaskBlockDiag) {
+    int* ids = (int*)(cls + ids_offset(n_cols));
+    unsigned long long* cnt = (unsigned long long*)(cls + cnt_offset(n_cols));
+    // row axis: the grid row's tile; column axis: the tiles being classified
+    const int* rdoc = TRANSPOSED ? m.doc_k + (int64_t)b * nk : m.doc_q + (int64_t)b * nq;
+    const int* cdoc = TRANSPOSED ? m.doc_q + (int64_t)b * nq : m.doc_k + (int64_t)b * nk;
+    const int rt = TRANSPOSED ? tile_n : tile_m, ct = TRANSPOSED ? tile_m : tile_n;
+    const int rn = TRANSPOSED ? nk : nq, cn = TRANSPOSED ? nq : nk;
+    const int r0 = row * rt, r1 = tile_end(r0, rt, rn), nr = r1 - r0;
+    // thread -> (row element, slice of the column tiles): with fewer row elements than
+    // threads, the threads of one element split the tiles between them
+    const int t = threadIdx.x;
+    const int nsl = (nr >= kThreads) ? 1 : kThreads / nr;
+    const int slice = (nr >= kThreads) ? 0 : t / nr;
+    const int i0 = (slice < nsl) ? r0 + ((nr >= kThreads) ? t : t % nr) : r1;
+    const int istep = (nr >= kThreads) ? kThreads : nr;
+    // tiles [g0, g1) counted per pass (one 64-bit counter each)
+    for (int g0 = 0; g0 < n_cols; g0 += kMaxCounted) {
+      const int g1 = min(n_cols, g0 + kMaxCounted);
+      for (int c = t; c < g1 - g0; c += kThreads) cnt[c] = 0;
+      const int a0 = g0 * ct, a1 = tile_end((g1 - 1) * ct, ct, cn);   // column elements covered
+      for (int cc = a0; cc < a1; cc += kIdChunk) {
+        const int ce = tile_end(cc, kIdChunk, a1);
+        __syncthreads();   // counters cleared / readers of the previous chunk done
+        for (int j = cc + t; j < ce; j += kThreads) ids[j - cc] = cdoc[j];
+        __syncthreads();
+        const int cf = cc / ct, cl = (ce - 1) / ct;   // tiles overlapping this chunk
+        for (int i = i0; i < r1; i += istep) {
+          const int di = rdoc[i];
+          for (int col = cf + slice; col <= cl; col += nsl) {
+            const int j0 = max(col * ct, cc) - cc, j1 = tile_end(col * ct, ct, ce) - cc;
+            int c = 0;
+#pragma unroll 8
+            for (int j = j0; j < j1; ++j) c += (ids[j] == di);
+            if (c) atomicAdd(&cnt[col - g0], (unsigned long long)c);   // exact in any order
+          }
+        }
+      }
+      __syncthreads();
+      for (int col = g0 + t; col < g1; col += kThreads) {
+        const int c0 = col * ct, c1 = tile_end(c0, ct, cn);
+        const unsigned long long vis = cnt[col - g0];
+        const unsigned long long all = (unsigned long long)nr * (unsigned long long)(c1 - c0);
+        cls[col] = (vis == 0) ? 0 : (vis == all ? 2 : 1);
+      }
+      __syncthreads();   // before the counters are reused
+    }
+  } else {
+    for (int col = threadIdx.x; col < n_cols; col += kThreads) {
+      const int qt = TRANSPOSED ? col : row;
+      const int kt = TRANSPOSED ? row : col;
+      const int q0 = qt * tile_m, q1 = tile_end(q0, tile_m, nq);
+      const int k0 = kt * tile_n, k1 = tile_end(k0, tile_n, nk);
+      int64_t vis = 0;
+      for (int i = q0; i < q1; ++i) vis += row_visible(m, i, k0, k1, nq, nk);
+      const int64_t all = (int64_t)(q1 - q0) * (k1 - k0);
+      cls[col] = (vis == 0) ? 0 : (vis == all ? 2 : 1);
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -87,12 +142,18 @@ hipError_t launch_build_block_mask(const MaskParams& m, int B, int Hm, int Nq, i
                                    int tile_n, const BlockMaskOut& out, hipStream_t st) {
   const int nqt = (Nq + tile_m - 1) / tile_m;
   const int nkt = (Nk + tile_n - 1) / tile_n;
-  hipLaunchKernelGGL(classify_kernel<false>, dim3(B * Hm * nqt), dim3(kThreads), nkt, st, m, Hm, Nq, Nk,
-                     tile_m, tile_n, nqt, nkt, out.pcnt, out.pidx, out.fcnt, out.fidx);
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipFuncSetAttribute((const void*)classify_kernel<false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(nkt));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(classify_kernel<true>, dim3(B * Hm * nkt), dim3(kThreads), nqt, st, m, Hm, Nq, Nk,
-                     tile_m, tile_n, nkt, nqt, out.tpcnt, out.tpidx, out.tfcnt, out.tfidx);
+  e = hipFuncSetAttribute((const void*)classify_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          lds_bytes(nqt));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(classify_kernel<false>, dim3(B * Hm * nqt), dim3(kThreads), lds_bytes(nkt), st, m, Hm, Nq,
+                     Nk, tile_m, tile_n, nqt, nkt, out.pcnt, out.pidx, out.fcnt, out.fidx);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(classify_kernel<true>, dim3(B * Hm * nkt), dim3(kThreads), lds_bytes(nqt), st, m, Hm, Nq,
+                     Nk, tile_m, tile_n, nkt, nqt, out.tpcnt, out.tpidx, out.tfcnt, out.tfidx);
   return hipGetLastError();
 }
 

@@ -36,6 +36,39 @@ def test_block_lists_bit_exact(kind, W, P, B, Nq, Nk, tm, tn):
         assert np.array_equal(got, getattr(ref, f)), f
 
 
+def _label_runs(rng, B, N, nlab):
+    """Runs of 50..3000 tokens, each labelled from nlab labels at random: a label recurs in
+    runs that are not adjacent, so one 'document' spans separate ranges."""
+    out = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        pos = 0
+        while pos < N:
+            end = min(N, pos + int(rng.integers(50, 3000, endpoint=True)))
+            out[b, pos:end] = rng.integers(0, nlab)
+            pos = end
+    return out
+
+
+@pytest.mark.parametrize("B,Nq,Nk,tm,tn,ndoc", [(1, 9000, 7500, 1500, 1100, 3), (2, 5000, 6000, 64, 128, 4),
+                                                (1, 12300, 8197, 2050, 1025, 2)])
+def test_block_lists_unsorted_documents(B, Nq, Nk, tm, tn, ndoc):
+    # document ids that are not sorted (a label recurs in separate runs), and tiles wider
+    # than the builder's 1024-id LDS chunk
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    rng = np.random.default_rng(synth.case_seed(3, 50 + ndoc))
+    dq, dk = _label_runs(rng, B, Nq, ndoc), _label_runs(rng, B, Nk, ndoc)
+    om = oracle.MaskSpec("block_diagonal", doc_q=dq, doc_k=dk)
+    dev = torch.device("cuda:0")
+    gm = fa.Mask("block_diagonal", doc_q=torch.from_numpy(dq).to(dev), doc_k=torch.from_numpy(dk).to(dev))
+    announce(f"build_block_mask unsorted docs B={B} Nq={Nq} Nk={Nk} tile={tm}x{tn} ndoc={ndoc}")
+    bs = _build(gm, B, Nq, Nk, tm, tn)
+    ref = oracle.build_lists(om, B, 1, Nq, Nk, tm, tn)
+    for f in FIELDS:
+        got = getattr(bs, f).cpu().numpy()
+        assert np.array_equal(got, getattr(ref, f)), f
+
+
 BS_CASES = [("causal", 0, 0), ("sliding_window", 2730, 0), ("block_diagonal", 0, 0), ("prefix_lm", 0, 1024)]
 
 
