@@ -209,7 +209,18 @@ void fwd_bf16_kernel(const AttnParams p) {
     }
     // score transform (softcap / bias) and mask; reg r of block kb holds key
     // n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of query row qrow.
-    if constexpr (SOFTCAP || BIAS) {
+    if constexpr (BIAS && !SOFTCAP) {
+      // relative bias alone: i - j = (qrow - n0 - 8 g) - (register offset), exact in fp32,
+      // so each score costs a subtraction with a literal, a multiply with |.| and an fma
+      const float dq = __int_as_float(opaque_int(__float_as_int((float)(qrow - n0 - 8 * g))));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float t = dq - (float)(32 * kb + 16 * (r >> 3) + (r & 7));
+          s[kb][r] = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(t));
+        }
+    } else if constexpr (SOFTCAP || BIAS) {
       const int jb = opaque_int(n0 + 8 * g);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
