@@ -274,6 +274,17 @@ def all_configs_report():
         log(workload="fwd_bf16_block_sparse", N=n, B=bsz, H=hh, D=128, mask=kind, ms=round(ms, 4),
             tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
             visited_tiles=tiles, of_tiles=bsz * (n // 128) ** 2, build_block_mask_ms=round(ms_bm, 4))
+        # the backward through the transposed lists (dQ, dK, dV), same mask and bias
+        do = torch.randn_like(q)
+        out, lse = fa.fmha_fwd(q, k, v, mask=m, bias_slope=-0.01, block_sparse=bs)
+        dq, dk, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.bwd_workspace_size(bsz, hh, n), dtype=torch.uint8, device=dev)
+        ms = timeit(lambda: fa.fmha_bwd(q, k, v, out, lse, do, mask=m, bias_slope=-0.01, block_sparse=bs,
+                                        dq=dq, dk=dk, dv=dv_, workspace=ws))
+        fb = 2.0 * hh * (3 * 128 + 2 * 128) * a
+        log(workload="bwd_bf16_block_sparse", N=n, B=bsz, H=hh, D=128, mask=kind, ms=round(ms, 4),
+            tflops=round(fb / ms / 1e9, 1), frac=round(fb / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+        del do, out, lse, dq, dk, dv_, ws
     del q, k, v
     # backward workloads (causal, B=1 H=16), incl. the MLA-shaped head Dqk=192 Dv=128
     for n, dqk, dv in ((4096, 64, 64), (4096, 128, 128), (16384, 64, 64), (8192, 192, 128)):

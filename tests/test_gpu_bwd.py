@@ -66,6 +66,21 @@ def test_bwd_block_sparse_lists(kind):
           slope=-0.01, lists=(128, 128))
 
 
+@pytest.mark.parametrize("kind", ["causal", "prefix_lm"])
+def test_bwd_block_sparse_lists_mla(kind):
+    # MLA-shaped heads (Dqk 192, Dv 128) through the transposed / forward lists
+    _case(synth.case_seed(9, 310), 1, 1024, 1024, 2, 192, 128, kind, prefix=256, slope=-0.01,
+          lists=(128, 128))
+
+
+@pytest.mark.parametrize("kind", ["causal", "block_diagonal"])
+def test_bwd_block_sparse_full_size(kind):
+    # the block-sparse workload's shape (B=2 H=8 N=8192 D=128, 128x128 tiles, relative bias),
+    # gradients compared on one head of both batch rows
+    _case(synth.case_seed(9, 320), 2, 8192, 8192, 8, 128, 128, kind, slope=-0.01, heads=[3],
+          lists=(128, 128))
+
+
 def test_bwd_deterministic():
     import torch
     q, k, v, do = synth.attention_inputs(synth.case_seed(9, 400), 1, 1024, 1024, 4, 128, 128, "bf16",
