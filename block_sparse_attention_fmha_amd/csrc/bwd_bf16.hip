@@ -260,6 +260,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
           const int qi = 32 * kb + 16 * hh + 8 * g;
           const f32x4 la = *(const f32x4*)(LD + qi), lb = *(const f32x4*)(LD + qi + 4);
           const int qb = (TEST != kTestNone || BIAS) ? opaque_int(i0 + qi) : 0;
+          // relative bias alone: i - j = (i0 + qi - key) + ee, exact in fp32 (as in the forward)
+          const float dij = (BIAS && !SOFTCAP) ? __int_as_float(opaque_int(__float_as_int((float)(i0 + qi - key)))) : 0.0f;
           u32x4 pk, pc;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -270,7 +272,9 @@ void bwd_dkdv_kernel(const BwdParams bp) {
               const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
               const int qidx = qb + ee;
               float dcap = 1.0f, u;
-              if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
+              if constexpr (BIAS && !SOFTCAP)
+                u = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee));
+              else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
               else u = s[kb][r] * p.scale_log2;
               // rows past Nq carry lse2 = +inf, so their P is 0 whatever the test says
               if constexpr (TEST == kTestBand) {
@@ -568,6 +572,8 @@ void bwd_dq_kernel(const BwdParams bp) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int jb = (TEST != kTestNone || BIAS) ? opaque_int(n0 + 32 * kb + 16 * hh + 8 * g) : 0;
+          // relative bias alone: i - j = (qrow - jb) - (2 e + z), exact in fp32 (as in the forward)
+          const float dij = (BIAS && !SOFTCAP) ? __int_as_float(opaque_int(__float_as_int((float)(qrow - jb)))) : 0.0f;
           u32x4 pk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -577,7 +583,9 @@ void bwd_dq_kernel(const BwdParams bp) {
               const int r = 8 * hh + 2 * e + z;
               const int j = jb + 2 * e + z;
               float dcap = 1.0f, u = s[kb][r];
-              if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
+              if constexpr (BIAS && !SOFTCAP)
+                u = __builtin_fmaf(u, p.scale_log2, p.bias_log2 * __builtin_fabsf(dij - (float)(2 * e + z)));
+              else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
               if constexpr (TEST != kTestNone) {
                 bool vis = (unsigned)(j - lo) < span;
                 if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
