@@ -93,15 +93,30 @@ def forward_bh(q_rows, k, v, qidx, b, h, nq, nk, *, scale, softcap=0.0, bias_slo
     return o, lse
 
 
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    """K/V head read by query head h when H query heads share Hkv K/V heads (grouped-query
+    attention, as in the reference call with ``enable_gqa=True`` and separate query and
+    key/value head counts of "Enable 2CTA for SM100 block-sparse backward", section
+    "Testing Testing Testing"): consecutive groups of H / Hkv query heads share one K/V
+    head. Hkv = H is multi-head attention, Hkv = 1 multi-query attention."""
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"{H} query heads cannot share {Hkv} key/value heads")
+    return h // (H // Hkv)
+
+
 def forward(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: MaskSpec = MaskSpec(),
             lists=None, heads=None, rows=None):
-    """Full forward. q [B,Nq,H,Dqk], k [B,Nk,H,Dqk], v [B,Nk,H,Dv].
+    """Full forward. q [B,Nq,H,Dqk], k [B,Nk,Hkv,Dqk], v [B,Nk,Hkv,Dv] (Hkv divides H;
+    query head h reads K/V head kv_head(h, H, Hkv)).
 
     ``heads``/``rows`` restrict the computation to a subset (the rest of the output is
     NaN), for sampled comparisons at sizes where the full product is too large."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, nq, H, dqk = q.shape
     nk, dv = k.shape[1], v.shape[3]
+    hkv = k.shape[2]
+    if v.shape[2] != hkv:
+        raise ValueError("k and v must have the same number of heads")
     scale = default_scale(dqk) if scale is None else scale
     heads = range(H) if heads is None else heads
     qidx = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -109,7 +124,8 @@ def forward(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: MaskSpec 
     lse = np.full((B, H, nq), np.nan)
     for b in range(B):
         for h in heads:
-            ob, lb = forward_bh(q[b, qidx, h], k[b, :, h], v[b, :, h], qidx, b, h, nq, nk,
+            g = kv_head(h, H, hkv)
+            ob, lb = forward_bh(q[b, qidx, h], k[b, :, g], v[b, :, g], qidx, b, h, nq, nk,
                                 scale=scale, softcap=softcap, bias_slope=bias_slope,
                                 mask=mask, lists=lists)
             o[b, qidx, h] = ob
@@ -149,6 +165,8 @@ def backward(q, k, v, do, *, scale=None, softcap=0.0, bias_slope=0.0,
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, nq, H, dqk = q.shape
     nk, dv_ = k.shape[1], v.shape[3]
+    if k.shape[2] != H or v.shape[2] != H:
+        raise ValueError("the backward oracle covers multi-head attention only (Hkv = H)")
     scale = default_scale(dqk) if scale is None else scale
     heads = range(H) if heads is None else heads
     dq = np.full(q.shape, np.nan)
@@ -182,10 +200,11 @@ def split_partials(q, k, v, splits, tile_n, *, scale=None, softcap=0.0, bias_slo
                    mask: MaskSpec = MaskSpec()):
     """Per-split normalised partial outputs: list of (O_s [B,Nq,H,Dv], LSE_s [B,H,Nq]).
     An empty split (or a row with no visible key in the split) gives O_s = 0,
-    LSE_s = -inf."""
+    LSE_s = -inf. K/V may have fewer heads than Q (see kv_head)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, nq, H, dqk = q.shape
     nk, dv = k.shape[1], v.shape[3]
+    hkv = k.shape[2]
     scale = default_scale(dqk) if scale is None else scale
     qidx = np.arange(nq)
     parts = []
@@ -196,11 +215,12 @@ def split_partials(q, k, v, splits, tile_n, *, scale=None, softcap=0.0, bias_slo
             kidx = np.arange(lo, hi)
             for b in range(B):
                 for h in range(H):
-                    s, _ = scores_bh(q[b, :, h], k[b, lo:hi, h], qidx, kidx, scale, softcap, bias_slope)
+                    g = kv_head(h, H, hkv)
+                    s, _ = scores_bh(q[b, :, h], k[b, lo:hi, g], qidx, kidx, scale, softcap, bias_slope)
                     vis = allowed(mask, b, qidx, kidx, nq, nk)
                     p, m, l, empty = _softmax_rows(s, vis)
                     safe_l = np.where(empty, 1.0, l)
-                    ob = (p @ v[b, lo:hi, h]) / safe_l[:, None]
+                    ob = (p @ v[b, lo:hi, g]) / safe_l[:, None]
                     ob[empty] = 0.0
                     o[b, :, h] = ob
                     lse[b, h] = np.where(empty, -np.inf, m + np.log(safe_l))
