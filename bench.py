@@ -241,6 +241,17 @@ def all_configs_report():
         log(workload="splitkv", splits=s, ms=round(ms, 4), GBs=round(byts / ms / 1e6, 1),
             frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
     del k, v
+    # grouped-query and multi-query decode: H=32 query heads over 8 or 1 K/V heads; the
+    # algorithmic bytes are the K/V of the K/V heads
+    for hkv in (8, 1):
+        k = torch.randn(8, 32768, hkv, 128, device=dev).bfloat16()
+        v = torch.randn(8, 32768, hkv, 128, device=dev).bfloat16()
+        for s in (4, 16, 64):
+            ms = timeit(lambda: fa.fmha_fwd_splitkv(q, k, v, s))
+            byts = 2 * k.numel() * 2
+            log(workload="splitkv_grouped", H=32, Hkv=hkv, splits=s, ms=round(ms, 4),
+                GBs=round(byts / ms / 1e6, 1), frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+        del k, v
     # fp32 wide head
     q, k, v = (torch.randn(4, 512, 8, 1024, device=dev) for _ in range(3))
     ms = timeit(lambda: fa.fmha_fwd(q, k, v))

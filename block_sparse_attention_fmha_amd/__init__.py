@@ -60,7 +60,7 @@ Strides3 = ctypes.c_int64 * 3
 class CFwdArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
                 ("Nk", ctypes.c_int32), ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("q_stride", Strides3), ("k_stride", Strides3), ("v_stride", Strides3),
@@ -219,15 +219,16 @@ def _fwd_args(q, k, v, out, lse, scale, softcap, bias_slope, mask, block_sparse)
     if not (q.dtype == k.dtype == v.dtype == out.dtype):
         raise ValueError("q, k, v and out must share one dtype")
     B, Nq, H, Dqk = q.shape
-    Nk, Dv = k.shape[1], v.shape[3]
-    if k.shape != (B, Nk, H, Dqk) or v.shape != (B, Nk, H, Dv) or out.shape != (B, Nq, H, Dv):
+    Nk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape != (B, Nk, Hkv, Dqk) or v.shape != (B, Nk, Hkv, Dv) or out.shape != (B, Nq, H, Dv):
         raise ValueError("inconsistent q / k / v / out shapes")
     if tuple(lse.shape) != (B, H, Nq) or str(lse.dtype) != "torch.float32" or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     a = CFwdArgs()
     a.B, a.H, a.Nq, a.Nk, a.Dqk, a.Dv = B, H, Nq, Nk, Dqk, Dv
     a.dtype = _dtype_code(q)
-    a.reserved = a.reserved2 = 0
+    a.kv_heads = 0 if Hkv == H else Hkv   # grouped K/V heads: the library decides support
+    a.reserved2 = 0
     a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
     a.q_stride, a.k_stride, a.v_stride, a.o_stride = _strides(q), _strides(k), _strides(v), _strides(out)
     a.scale = float(1.0 / math.sqrt(Dqk) if scale is None else scale)

@@ -98,7 +98,8 @@ bool supported_dims(int dtype, int dqk, int dv) {
 int validate_fwd(const fmha_fwd_args* a) {
   if (a == nullptr) return FMHA_ERR_INVALID_ARG;
   if (a->B < 0 || a->H < 0 || a->Nq < 0 || a->Nk < 0) return FMHA_ERR_INVALID_ARG;
-  if (a->reserved != 0 || a->reserved2 != 0) return FMHA_ERR_INVALID_ARG;
+  if (a->reserved2 != 0) return FMHA_ERR_INVALID_ARG;
+  if (a->kv_heads < 0 || (a->kv_heads > 0 && a->H % a->kv_heads != 0)) return FMHA_ERR_INVALID_ARG;
   if (a->dtype != FMHA_BF16 && a->dtype != FMHA_FP32) return FMHA_ERR_INVALID_ARG;
   if (!supported_dims(a->dtype, a->Dqk, a->Dv)) return FMHA_ERR_UNSUPPORTED;
   if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return FMHA_ERR_INVALID_ARG;
@@ -146,6 +147,9 @@ int validate_lists(const fmha_block_sparse* bs, int B, int H, int Nq, int Nk, in
   (void)B;
   return FMHA_OK;
 }
+
+// K/V carry one head per query head (kv_heads 0 or H)
+bool multi_head(const fmha_fwd_args* a) { return a->kv_heads == 0 || a->kv_heads == a->H; }
 
 AttnParams attn_params(const fmha_fwd_args* a) {
   AttnParams p;
@@ -233,6 +237,7 @@ const char* fmha_status_string(int status) {
 int fmha_fwd(const fmha_fwd_args* a, void* stream) {
   int rc = validate_fwd(a);
   if (rc != FMHA_OK) return rc;
+  if (!multi_head(a)) return FMHA_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->H * a->Nq == 0) return FMHA_OK;
   if (a->block_sparse) {
     if (a->dtype != FMHA_BF16) return FMHA_ERR_UNSUPPORTED;
@@ -261,6 +266,7 @@ size_t fmha_bwd_workspace_size(int32_t B, int32_t H, int32_t Nq) {
 int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
   int rc = validate_fwd(a);
   if (rc != FMHA_OK) return rc;
+  if (!multi_head(a)) return FMHA_ERR_UNSUPPORTED;
   if (g == nullptr) return FMHA_ERR_INVALID_ARG;
   if (a->dtype != FMHA_BF16) return FMHA_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->H * a->Nq == 0 && (int64_t)a->B * a->H * a->Nk == 0) return FMHA_OK;
@@ -321,8 +327,11 @@ int fmha_fwd_splitkv(const fmha_fwd_args* a, int32_t num_splits, void* workspace
   rc = check_device();
   if (rc != FMHA_OK) return rc;
   AttnParams p = attn_params(a);
-  FMHA_LOG("fwd splitkv B=%d H=%d Nq=%d Nk=%d D=%d splits=%d", a->B, a->H, a->Nq, a->Nk, a->Dv, num_splits);
-  return hip_status(fmha::launch_fwd_splitkv(p, a->Dv, num_splits, workspace, reinterpret_cast<hipStream_t>(stream)));
+  const int group = a->kv_heads > 0 ? a->H / a->kv_heads : 1;
+  FMHA_LOG("fwd splitkv B=%d H=%d Hkv=%d Nq=%d Nk=%d D=%d splits=%d", a->B, a->H, a->H / group, a->Nq, a->Nk, a->Dv,
+           num_splits);
+  return hip_status(
+      fmha::launch_fwd_splitkv(p, a->Dv, num_splits, group, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int build_block_mask(const fmha_mask* mask, int32_t B, int32_t Hm, int32_t Nq, int32_t Nk, int32_t tile_m,

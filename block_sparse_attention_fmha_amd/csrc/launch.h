@@ -22,7 +22,8 @@ hipError_t launch_fwd_f32(AttnParams p, int d, hipStream_t st);
 // bf16 split-KV forward (partials + combine). `ws` holds the partials.
 size_t splitkv_workspace_bytes(int B, int H, int Nq, int Dv, int splits);
 int splitkv_tile_keys();
-hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, void* ws, hipStream_t st);
+// `group` query heads share each K/V head (1 = multi-head).
+hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* ws, hipStream_t st);
 
 // bf16 backward: preprocess, dK/dV pass, dQ pass.
 hipError_t launch_bwd_bf16(BwdParams p, int dqk, int dv, hipStream_t st);

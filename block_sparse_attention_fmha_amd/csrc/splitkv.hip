@@ -15,8 +15,14 @@
 //     (quad permutes and row mirrors: no LDS traffic);
 //   * every lane keeps its own running (m, l, O-slice) in the log2 domain; 8 keys per
 //     lane are loaded per iteration so that 16 x 16-byte loads are in flight per lane;
-//   * at the end the key slots of the wave and the four waves are merged with the same
-//     (m, l, O) merge and the normalised partial (O_s, LSE_s) is written in fp32.
+//   * at the end the key slots of the wave and the waves of the same query head are
+//     merged with the same (m, l, O) merge and the normalised partial (O_s, LSE_s) is
+//     written in fp32.
+// Grouped K/V heads (several query heads reading one K/V head): the four waves of a
+// workgroup take up to four query heads of one group, each streaming the whole key range
+// of the split; their loads of the same K/V rows are issued close together and served
+// once from memory, so the group's K/V bytes cross HBM once instead of once per query
+// head. With fewer heads per workgroup the remaining waves split the keys as above.
 // The combine kernel then computes LSE = ln sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s per row (empty splits carry LSE_s = -inf).
 #include "kernel_common.h"
@@ -47,6 +53,8 @@ struct SplitParams {
   float* part_lse;   // [B*H, S, Nq]
   int splits;
   int per_split;     // keys per split (multiple of kTileKeys)
+  int group;         // query heads per K/V head (1 = multi-head)
+  int hpw;           // query heads per workgroup, one per wave group: 1, 2 or 4 (divides group)
 };
 
 template <int D>
@@ -61,16 +69,22 @@ void splitkv_partial_kernel(const SplitParams sp) {
   const int s = blockIdx.x % sp.splits;
   const int rest = blockIdx.x / sp.splits;
   const int qrow = rest % p.Nq;
-  const int bh = rest / p.Nq;
-  const int b = bh / p.H, h = bh % p.H;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int bhc = rest / p.Nq;                  // (batch, run of hpw query heads)
+  const int nhc = p.H / sp.hpw;
+  const int b = bhc / nhc;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  // wave w: query head h0 + w % hpw, key slice w / hpw of nsl
+  const int hpw = sp.hpw, nsl = 4 / hpw, slice = w / hpw;
+  const int h = (bhc - b * nhc) * hpw + w % hpw;
+  const int hk = h / sp.group;                  // the K/V head it reads
+  const int bh = b * p.H + h;
   const int slot = l / LPK, dl = l % LPK;
   const int k_lo = min(p.Nk, s * sp.per_split);
   const int k_hi = min(p.Nk, k_lo + sp.per_split);
 
   const __bf16* Qg = (const __bf16*)p.q + b * p.qs_b + h * p.qs_h + (int64_t)qrow * p.qs_s;
-  const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + h * p.ks_h;
-  const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + h * p.vs_h;
+  const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + hk * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + hk * p.vs_h;
 
   float qv[8];
   bf16x8_to_f32(*(const u32x4*)(Qg + 8 * dl), qv);
@@ -82,7 +96,7 @@ void splitkv_partial_kernel(const SplitParams sp) {
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   const bool masked = p.mask.kind != kMaskNone;
 
-  for (int base = k_lo + w * CHUNK; base < k_hi; base += 4 * CHUNK) {
+  for (int base = k_lo + slice * CHUNK; base < k_hi; base += nsl * CHUNK) {
     u32x4 kr[kUnroll], vr[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -142,9 +156,12 @@ void splitkv_partial_kernel(const SplitParams sp) {
     for (int e = 0; e < 8; ++e) xw[w][dl][2 + e] = acc[e];
   }
   __syncthreads();
-  if (w == 0 && slot == 0) {
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) merge_state<8>(m, lsum, acc, xw[ww][dl][0], xw[ww][dl][1], &xw[ww][dl][2]);
+  if (slice == 0 && slot == 0) {
+    // the waves of this query head (w + hpw, w + 2 hpw, ...) in slice order
+    for (int sl = 1; sl < nsl; ++sl) {
+      const int ww = w + sl * hpw;
+      merge_state<8>(m, lsum, acc, xw[ww][dl][0], xw[ww][dl][1], &xw[ww][dl][2]);
+    }
     const bool empty = !(lsum > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / lsum;
     const int64_t row = ((int64_t)bh * sp.splits + s) * p.Nq + qrow;
@@ -194,16 +211,18 @@ size_t splitkv_workspace_bytes(int B, int H, int Nq, int Dv, int splits) {
   return ((o_bytes + 255) / 256) * 256 + rows * sizeof(float);
 }
 
-hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, void* ws, hipStream_t st) {
+hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* ws, hipStream_t st) {
   SplitParams sp;
   sp.a = p;
   sp.splits = splits;
+  sp.group = group;
+  sp.hpw = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
   const int tiles = (p.Nk + kTileKeys - 1) / kTileKeys;
   sp.per_split = ((tiles + splits - 1) / splits) * kTileKeys;
   const size_t rows = (size_t)p.B * p.H * splits * p.Nq;
   sp.part_o = (float*)ws;
   sp.part_lse = (float*)((char*)ws + ((rows * d * sizeof(float) + 255) / 256) * 256);
-  const unsigned nblk = (unsigned)(p.B * p.H * p.Nq * splits);
+  const unsigned nblk = (unsigned)(p.B * (p.H / sp.hpw) * p.Nq * splits);
   const unsigned nrow = (unsigned)(p.B * p.H * p.Nq);
   if (d == 128) {
     hipLaunchKernelGGL(splitkv_partial_kernel<128>, dim3(nblk), dim3(kThreads), 0, st, sp);

@@ -118,7 +118,7 @@ typedef struct {
   int32_t *t_partial_cnt, *t_partial_idx, *t_full_cnt, *t_full_idx;
 } fmha_block_sparse;
 
-/* Forward problem. Q [B,Nq,H,Dqk], K [B,Nk,H,Dqk], V [B,Nk,H,Dv], O [B,Nq,H,Dv] are
+/* Forward problem. Q [B,Nq,H,Dqk], K [B,Nk,Hkv,Dqk], V [B,Nk,Hkv,Dv], O [B,Nq,H,Dv] are
  * addressed with element strides {batch, seq, head}; the head dim is contiguous
  * (so BSHD and BHSD both work). Rows (seq-stride * elem size) must be 16-byte aligned,
  * and 64 rows must span less than 2^31 bytes (FMHA_ERR_UNSUPPORTED otherwise).
@@ -128,7 +128,13 @@ typedef struct {
 typedef struct {
   int32_t B, H, Nq, Nk, Dqk, Dv;
   int32_t dtype;       /* fmha_dtype */
-  int32_t reserved;    /* must be 0 */
+  int32_t kv_heads;    /* Hkv: K/V heads, 0 (= H) or a divisor of H. Grouped-query
+                          attention: query head h reads K/V head h / (H / Hkv) (the grouping
+                          of the reference call with enable_gqa in "Enable 2CTA for SM100
+                          block-sparse backward", section "Testing Testing Testing").
+                          Only fmha_fwd_splitkv accepts Hkv != H; fmha_fwd and fmha_bwd
+                          return FMHA_ERR_UNSUPPORTED for it. Not dividing H, or negative:
+                          FMHA_ERR_INVALID_ARG. */
   const void* q;
   const void* k;
   const void* v;
@@ -182,7 +188,9 @@ int fmha_bwd(const fmha_fwd_args* args, const fmha_bwd_args* bwd, void* stream);
  * num_splits contiguous, 64-key-aligned chunks of ceil(ceil(Nk/64)/num_splits) tiles;
  * each chunk produces a normalised partial (O_s, LSE_s) in the workspace, then a
  * combine kernel merges them: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
- * bf16 only, no block-sparse lists, 1 <= num_splits <= 64. */
+ * bf16 only, no block-sparse lists, 1 <= num_splits <= 64. Accepts grouped K/V heads
+ * (args->kv_heads): the query heads of one group (up to 4 per workgroup) stream each
+ * K/V row of the group once from memory. The workspace is sized by query heads H. */
 size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t Dv,
                                        int32_t num_splits);
 int fmha_fwd_splitkv(const fmha_fwd_args* args, int32_t num_splits, void* workspace,

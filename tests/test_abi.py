@@ -76,7 +76,10 @@ def _args(**kw):
     ({"scale": float("nan")}, fa.FMHA_ERR_INVALID_ARG),
     ({"softcap": -1.0}, fa.FMHA_ERR_INVALID_ARG),
     ({"dtype": 7}, fa.FMHA_ERR_INVALID_ARG),
-    ({"reserved": 1}, fa.FMHA_ERR_INVALID_ARG),
+    ({"kv_heads": -1}, fa.FMHA_ERR_INVALID_ARG),
+    ({"kv_heads": 3}, fa.FMHA_ERR_INVALID_ARG),           # does not divide H = 2
+    ({"kv_heads": 1}, fa.FMHA_ERR_UNSUPPORTED),           # grouped heads: split-KV only
+    ({"reserved2": 1}, fa.FMHA_ERR_INVALID_ARG),
     ({"Nq": -1}, fa.FMHA_ERR_INVALID_ARG),
     ({"dtype": fa.FMHA_FP32, "Dqk": 1024, "Dv": 1024, "softcap": 30.0}, fa.FMHA_ERR_UNSUPPORTED),
 ])
@@ -192,7 +195,7 @@ def test_ctypes_layout_matches_c_compiler(tmp_path):
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fmha.h"\n'
                    "#define P(s, f) printf(#s \".\" #f \" %zu\\n\", offsetof(s, f))\n"
                    "int main(void) {\n"
-                   "  P(fmha_fwd_args, q); P(fmha_fwd_args, lse); P(fmha_fwd_args, q_stride);"
+                   "  P(fmha_fwd_args, kv_heads); P(fmha_fwd_args, q); P(fmha_fwd_args, lse); P(fmha_fwd_args, q_stride);"
                    "  P(fmha_fwd_args, o_stride); P(fmha_fwd_args, scale); P(fmha_fwd_args, mask);"
                    "  P(fmha_fwd_args, block_sparse); P(fmha_bwd_args, workspace);"
                    "  P(fmha_bwd_args, workspace_bytes); P(fmha_block_sparse, partial_cnt);"
@@ -205,6 +208,7 @@ def test_ctypes_layout_matches_c_compiler(tmp_path):
     got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
                                                        check=True).stdout.splitlines())
     want = {
+        "fmha_fwd_args.kv_heads": fa.CFwdArgs.kv_heads.offset,
         "fmha_fwd_args.q": fa.CFwdArgs.q.offset, "fmha_fwd_args.lse": fa.CFwdArgs.lse.offset,
         "fmha_fwd_args.q_stride": fa.CFwdArgs.q_stride.offset,
         "fmha_fwd_args.o_stride": fa.CFwdArgs.o_stride.offset,

@@ -53,3 +53,42 @@ def test_splitkv_full_size(decode_inputs, splits):
     for (b, h), (o_ref, l_ref) in refs.items():
         check_bf16(f"O[{b},{h}]", o[b, :, h], o_ref)
         check_bf16(f"LSE[{b},{h}]", l[b, h], l_ref)
+
+
+def _gqa_inputs(seed, B, nq, nk, H, Hkv, d):
+    # Q with H heads, K / V with Hkv heads, from the shared seeded generator
+    q = synth.attention_inputs(seed, B, nq, nk, H, d, d, "bf16")[0]
+    _, k, v = synth.attention_inputs(seed + 1, B, nq, nk, Hkv, d, d, "bf16")
+    return q, k, v
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (8, 4), (6, 2), (8, 1), (12, 1)])
+@pytest.mark.parametrize("nq,nk,d,kind", [(1, 1000, 128, "none"), (3, 777, 64, "causal")])
+def test_splitkv_grouped_heads_small(splits, H, Hkv, nq, nk, d, kind):
+    # grouped-query (Hkv divides H) and multi-query (Hkv = 1) heads: query head h reads
+    # K/V head h // (H / Hkv)
+    seed = synth.case_seed(9, 700 + 10 * H + Hkv + d)
+    q, k, v = _gqa_inputs(seed, 2, nq, nk, H, Hkv, d)
+    om, gm = mask_pair(kind, 2, nq, nk)
+    announce(f"splitkv grouped heads seed={seed} H={H} Hkv={Hkv} Nq={nq} Nk={nk} D={d} mask={kind} splits={splits}")
+    out, lse = run_split(to_dev(q), to_dev(k), to_dev(v), splits, gm)
+    o_ref, l_ref = oracle.forward(q.values, k.values, v.values, mask=om)
+    check_bf16("O", host(out), o_ref)
+    check_bf16("LSE", host(lse), l_ref)
+
+
+@pytest.mark.parametrize("Hkv,splits", [(8, 1), (8, 16), (1, 16)])
+def test_splitkv_grouped_heads_full_size(Hkv, splits):
+    # B=8 H=32 Nq=1 Nk=32768 D=128 with 8 (groups of 4) or 1 (multi-query) K/V heads
+    seed = synth.case_seed(5, 10 + Hkv)
+    q, k, v = _gqa_inputs(seed, 8, 1, 32768, 32, Hkv, 128)
+    announce(f"splitkv grouped heads full size seed={seed} B=8 H=32 Hkv={Hkv} Nk=32768 splits={splits}")
+    out, lse = run_split(to_dev(q), to_dev(k), to_dev(v), splits)
+    o, l = host(out), host(lse)
+    for b, h in ((0, 0), (2, 5), (5, 18), (7, 31)):
+        g = oracle.kv_head(h, 32, Hkv)
+        o_ref, l_ref = oracle.forward_bh(q.values[b, :, h], k.values[b, :, g], v.values[b, :, g], np.arange(1),
+                                         b, h, 1, 32768, scale=1 / np.sqrt(128.0))
+        check_bf16(f"O[{b},{h}]", o[b, :, h], o_ref)
+        check_bf16(f"LSE[{b},{h}]", l[b, h], l_ref)
