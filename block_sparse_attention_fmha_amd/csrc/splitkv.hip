@@ -18,11 +18,13 @@
 //   * at the end the key slots of the wave and the waves of the same query head are
 //     merged with the same (m, l, O) merge and the normalised partial (O_s, LSE_s) is
 //     written in fp32.
-// Grouped K/V heads (several query heads reading one K/V head): the four waves of a
-// workgroup take up to four query heads of one group, each streaming the whole key range
-// of the split; their loads of the same K/V rows are issued close together and served
-// once from memory, so the group's K/V bytes cross HBM once instead of once per query
-// head. With fewer heads per workgroup the remaining waves split the keys as above.
+// Grouped K/V heads (several query heads reading one K/V head): with an even group size
+// a workgroup serves GC = 2 or 4 query heads of one group (splitkv_grouped_kernel). Each
+// lane loads its K/V row slice once and uses it for all GC heads: the score dot products
+// are packed bf16 dot products (v_dot2: the product of two bf16 values is exact in
+// fp32) on the bf16 Q and K, and the V slice is converted to fp32 once for the GC heads,
+// so the group's K/V bytes cross HBM once and the per-(head, key) VALU work drops. An odd
+// group size runs the one-head kernel with the head mapping.
 // The combine kernel then computes LSE = ln sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s per row (empty splits carry LSE_s = -inf).
 #include "kernel_common.h"
@@ -54,7 +56,6 @@ struct SplitParams {
   int splits;
   int per_split;     // keys per split (multiple of kTileKeys)
   int group;         // query heads per K/V head (1 = multi-head)
-  int hpw;           // query heads per workgroup, one per wave group: 1, 2 or 4 (divides group)
 };
 
 template <int D>
@@ -69,15 +70,10 @@ void splitkv_partial_kernel(const SplitParams sp) {
   const int s = blockIdx.x % sp.splits;
   const int rest = blockIdx.x / sp.splits;
   const int qrow = rest % p.Nq;
-  const int bhc = rest / p.Nq;                  // (batch, run of hpw query heads)
-  const int nhc = p.H / sp.hpw;
-  const int b = bhc / nhc;
-  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  // wave w: query head h0 + w % hpw, key slice w / hpw of nsl
-  const int hpw = sp.hpw, nsl = 4 / hpw, slice = w / hpw;
-  const int h = (bhc - b * nhc) * hpw + w % hpw;
+  const int bh = rest / p.Nq;
+  const int b = bh / p.H, h = bh % p.H;
   const int hk = h / sp.group;                  // the K/V head it reads
-  const int bh = b * p.H + h;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int slot = l / LPK, dl = l % LPK;
   const int k_lo = min(p.Nk, s * sp.per_split);
   const int k_hi = min(p.Nk, k_lo + sp.per_split);
@@ -96,7 +92,7 @@ void splitkv_partial_kernel(const SplitParams sp) {
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   const bool masked = p.mask.kind != kMaskNone;
 
-  for (int base = k_lo + slice * CHUNK; base < k_hi; base += nsl * CHUNK) {
+  for (int base = k_lo + w * CHUNK; base < k_hi; base += 4 * CHUNK) {
     u32x4 kr[kUnroll], vr[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -156,12 +152,9 @@ void splitkv_partial_kernel(const SplitParams sp) {
     for (int e = 0; e < 8; ++e) xw[w][dl][2 + e] = acc[e];
   }
   __syncthreads();
-  if (slice == 0 && slot == 0) {
-    // the waves of this query head (w + hpw, w + 2 hpw, ...) in slice order
-    for (int sl = 1; sl < nsl; ++sl) {
-      const int ww = w + sl * hpw;
-      merge_state<8>(m, lsum, acc, xw[ww][dl][0], xw[ww][dl][1], &xw[ww][dl][2]);
-    }
+  if (w == 0 && slot == 0) {
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) merge_state<8>(m, lsum, acc, xw[ww][dl][0], xw[ww][dl][1], &xw[ww][dl][2]);
     const bool empty = !(lsum > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / lsum;
     const int64_t row = ((int64_t)bh * sp.splits + s) * p.Nq + qrow;
@@ -171,6 +164,145 @@ void splitkv_partial_kernel(const SplitParams sp) {
     *(f32x4*)po = x0;
     *(f32x4*)(po + 4) = x1;
     if (dl == 0) sp.part_lse[row] = empty ? kNegInf : (m + fast_log2(lsum)) * kLn2;
+  }
+}
+
+// The two bf16 values packed in a 32-bit word. (A memcpy, not __builtin_bit_cast of a
+// vector element: hipcc compiles the latter as a cast of element 0 whatever the index.)
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t x) {
+  bf16x2 v;
+  __builtin_memcpy(&v, &x, 4);
+  return v;
+}
+
+// GC query heads (one run of a K/V group) per workgroup, same key walk and merges as the
+// one-head kernel; see the file comment.
+template <int D, int GC>
+__global__ __launch_bounds__(kThreads)
+void splitkv_grouped_kernel(const SplitParams sp) {
+  constexpr int LPK = D / 8;
+  constexpr int KPW = 64 / LPK;
+  constexpr int CHUNK = KPW * kUnroll;
+  const AttnParams& p = sp.a;
+  __shared__ float xw[4][GC][LPK][10];
+
+  const int s = blockIdx.x % sp.splits;
+  const int rest = blockIdx.x / sp.splits;
+  const int qrow = rest % p.Nq;
+  const int bhc = rest / p.Nq;                  // (batch, run of GC query heads)
+  const int nhc = p.H / GC;
+  const int b = bhc / nhc;
+  const int h0 = (bhc - b * nhc) * GC;
+  const int hk = h0 / sp.group;                 // GC divides the group: one K/V head
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int slot = l / LPK, dl = l % LPK;
+  const int k_lo = min(p.Nk, s * sp.per_split);
+  const int k_hi = min(p.Nk, k_lo + sp.per_split);
+
+  const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + hk * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + hk * p.vs_h;
+  u32x4 qb[GC];   // bf16 Q slice of each head
+#pragma unroll
+  for (int gi = 0; gi < GC; ++gi)
+    qb[gi] = *(const u32x4*)((const __bf16*)p.q + b * p.qs_b + (h0 + gi) * p.qs_h + (int64_t)qrow * p.qs_s + 8 * dl);
+
+  float m[GC], lsum[GC], acc[GC][8];
+#pragma unroll
+  for (int gi = 0; gi < GC; ++gi) {
+    m[gi] = kNegInf;
+    lsum[gi] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[gi][e] = 0.0f;
+  }
+  const bool masked = p.mask.kind != kMaskNone;
+
+  for (int base = k_lo + w * CHUNK; base < k_hi; base += 4 * CHUNK) {
+    u32x4 kr[kUnroll], vr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int key = base + u * KPW + slot;
+      const bool in = key < k_hi;
+      kr[u] = in ? *(const u32x4*)(Kg + (int64_t)key * p.ks_s + 8 * dl) : u32x4{};
+      vr[u] = in ? *(const u32x4*)(Vg + (int64_t)key * p.vs_s + 8 * dl) : u32x4{};
+    }
+    float sc[GC][kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int key = base + u * KPW + slot;
+      bool vis = key < k_hi;
+      if (vis && masked) vis = mask_visible(p.mask, b, qrow, key, p.Nq, p.Nk);
+#pragma unroll
+      for (int gi = 0; gi < GC; ++gi) {
+        float x = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qb[gi][e]), as_bf16x2(kr[u][e]), x, false);
+        x = group_sum<LPK>(x);
+        sc[gi][u] = vis ? x * p.scale_log2 : kNegInf;
+      }
+    }
+    float mu[GC];
+#pragma unroll
+    for (int gi = 0; gi < GC; ++gi) {
+      float mt = sc[gi][0];
+#pragma unroll
+      for (int u = 1; u < kUnroll; ++u) mt = fmaxf(mt, sc[gi][u]);
+      const float mn = fmaxf(m[gi], mt);
+      mu[gi] = (mn == kNegInf) ? 0.0f : mn;
+      const float alpha = fast_exp2(m[gi] - mu[gi]);
+      lsum[gi] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[gi][e] *= alpha;
+      m[gi] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float vf[8];
+      bf16x8_to_f32(vr[u], vf);
+#pragma unroll
+      for (int gi = 0; gi < GC; ++gi) {
+        const float pu = fast_exp2(sc[gi][u] - mu[gi]);
+        lsum[gi] += pu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[gi][e] = __builtin_fmaf(pu, vf[e], acc[gi][e]);
+      }
+    }
+  }
+
+  // merge the key slots of the wave, then the four waves, per head
+#pragma unroll
+  for (int gi = 0; gi < GC; ++gi) {
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) {
+      float acc2[8];
+      const float m2 = __shfl_xor(m[gi], off), l2 = __shfl_xor(lsum[gi], off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc2[e] = __shfl_xor(acc[gi][e], off);
+      merge_state<8>(m[gi], lsum[gi], acc[gi], m2, l2, acc2);
+    }
+    if (slot == 0) {
+      xw[w][gi][dl][0] = m[gi];
+      xw[w][gi][dl][1] = lsum[gi];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xw[w][gi][dl][2 + e] = acc[gi][e];
+    }
+  }
+  __syncthreads();
+  if (w == 0 && slot == 0) {
+#pragma unroll
+    for (int gi = 0; gi < GC; ++gi) {
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww)
+        merge_state<8>(m[gi], lsum[gi], acc[gi], xw[ww][gi][dl][0], xw[ww][gi][dl][1], &xw[ww][gi][dl][2]);
+      const bool empty = !(lsum[gi] > 0.0f);
+      const float inv = empty ? 0.0f : 1.0f / lsum[gi];
+      const int64_t row = ((int64_t)(b * p.H + h0 + gi) * sp.splits + s) * p.Nq + qrow;
+      float* po = sp.part_o + row * D + 8 * dl;
+      f32x4 x0 = {acc[gi][0] * inv, acc[gi][1] * inv, acc[gi][2] * inv, acc[gi][3] * inv};
+      f32x4 x1 = {acc[gi][4] * inv, acc[gi][5] * inv, acc[gi][6] * inv, acc[gi][7] * inv};
+      *(f32x4*)po = x0;
+      *(f32x4*)(po + 4) = x1;
+      if (dl == 0) sp.part_lse[row] = empty ? kNegInf : (m[gi] + fast_log2(lsum[gi])) * kLn2;
+    }
   }
 }
 
@@ -216,29 +348,26 @@ hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* 
   sp.a = p;
   sp.splits = splits;
   sp.group = group;
-  sp.hpw = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  const int gc = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;   // query heads per workgroup
   const int tiles = (p.Nk + kTileKeys - 1) / kTileKeys;
   sp.per_split = ((tiles + splits - 1) / splits) * kTileKeys;
   const size_t rows = (size_t)p.B * p.H * splits * p.Nq;
   sp.part_o = (float*)ws;
   sp.part_lse = (float*)((char*)ws + ((rows * d * sizeof(float) + 255) / 256) * 256);
-  const unsigned nblk = (unsigned)(p.B * (p.H / sp.hpw) * p.Nq * splits);
+  const unsigned nblk = (unsigned)(p.B * (p.H / gc) * p.Nq * splits);
   const unsigned nrow = (unsigned)(p.B * p.H * p.Nq);
-  if (d == 128) {
-    hipLaunchKernelGGL(splitkv_partial_kernel<128>, dim3(nblk), dim3(kThreads), 0, st, sp);
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
+  auto partial = [&](auto d_c) {
+    constexpr int DD = decltype(d_c)::value;
+    if (gc == 4) hipLaunchKernelGGL((splitkv_grouped_kernel<DD, 4>), dim3(nblk), dim3(kThreads), 0, st, sp);
+    else if (gc == 2) hipLaunchKernelGGL((splitkv_grouped_kernel<DD, 2>), dim3(nblk), dim3(kThreads), 0, st, sp);
+    else hipLaunchKernelGGL(splitkv_partial_kernel<DD>, dim3(nblk), dim3(kThreads), 0, st, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(splitkv_combine_kernel<128>, dim3(nrow), dim3(128), 0, st, sp);
+    hipLaunchKernelGGL(splitkv_combine_kernel<DD>, dim3(nrow), dim3(DD), 0, st, sp);
     return hipGetLastError();
-  }
-  if (d == 64) {
-    hipLaunchKernelGGL(splitkv_partial_kernel<64>, dim3(nblk), dim3(kThreads), 0, st, sp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(splitkv_combine_kernel<64>, dim3(nrow), dim3(64), 0, st, sp);
-    return hipGetLastError();
-  }
-  return hipErrorInvalidValue;
+  };
+  return d == 128 ? partial(IntC<128>{}) : partial(IntC<64>{});
 }
 
 }  // namespace fmha
