@@ -27,8 +27,8 @@ FMHA_OK, FMHA_ERR_INVALID_ARG, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP, FMHA_ERR_WORK
 FMHA_BF16, FMHA_FP32 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding_window": 2, "block_diagonal": 3, "prefix_lm": 4}
 ENTRY_POINTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_splitkv",
-                "fmha_fwd_splitkv_workspace_size", "build_block_mask", "fmha_status_string",
-                "fmha_abi_version")
+                "fmha_fwd_splitkv_workspace_size", "fmha_fwd_varlen", "build_block_mask",
+                "fmha_status_string", "fmha_abi_version")
 
 
 class FmhaError(RuntimeError):
@@ -70,6 +70,11 @@ class CFwdArgs(ctypes.Structure):
                 ("block_sparse", ctypes.POINTER(CBlockSparse))]
 
 
+class CVarlen(ctypes.Structure):
+    _fields_ = [("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("total_q", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class CBwdArgs(ctypes.Structure):
     _fields_ = [("dout", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p),
                 ("dv", ctypes.c_void_p), ("do_stride", Strides3), ("dq_stride", Strides3),
@@ -105,6 +110,8 @@ def load_library():
     lib.fmha_fwd_splitkv.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
     lib.fmha_fwd_splitkv.restype = ctypes.c_int
+    lib.fmha_fwd_varlen.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.POINTER(CVarlen), ctypes.c_void_p]
+    lib.fmha_fwd_varlen.restype = ctypes.c_int
     lib.fmha_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.build_block_mask.argtypes = [ctypes.POINTER(CMask)] + [ctypes.c_int32] * 6 + [
@@ -321,6 +328,44 @@ def fmha_fwd_splitkv(q, k, v, num_splits: int, *, scale=None, mask: Mask | None 
     _check(lib.fmha_fwd_splitkv(ctypes.byref(a), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
                                 workspace.numel() * workspace.element_size(), _stream(stream)),
            "fmha_fwd_splitkv")
+    return out, lse
+
+
+def fmha_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
+                    scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | None = None, out=None, lse=None,
+                    stream=None):
+    """Forward over packed variable-length sequences. q [total_q, H, Dqk], k [total_k, H, Dqk],
+    v [total_k, H, Dv] (bf16); cu_seqlens_q / cu_seqlens_k: contiguous int32 device tensors
+    [B + 1] of ascending row offsets starting at 0; max_seqlen_q / max_seqlen_k bound every
+    sequence's length (the offsets are not read on the host). Returns (out [total_q, H, Dv],
+    lse [H, total_q] fp32)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        _need_device(t, n)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("varlen q / k / v are [total, H, D]")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if str(t.dtype) != "torch.int32" or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] device tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 offsets")
+    total_q, H, _ = q.shape
+    Dv = v.shape[2]
+    if out is None:
+        out = torch.empty((total_q, H, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if tuple(lse.shape) != (H, total_q) or str(lse.dtype) != "torch.float32" or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [H, total_q] tensor")
+    # one-"batch" views give the seq / head strides; B, Nq, Nk are then the varlen ones
+    a, _keep = _fwd_args(q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), out.unsqueeze(0),
+                         lse.view(1, H, total_q), scale, softcap, bias_slope, mask, None)
+    a.B = cu_seqlens_q.numel() - 1
+    a.Nq, a.Nk = int(max_seqlen_q), int(max_seqlen_k)
+    vl = CVarlen()
+    vl.cu_seqlens_q, vl.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    vl.total_q, vl.reserved = total_q, 0
+    _check(load_library().fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(vl), _stream(stream)), "fmha_fwd_varlen")
     return out, lse
 
 

@@ -221,7 +221,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 extern "C" {
 
-int fmha_abi_version(void) { return 1; }
+int fmha_abi_version(void) { return 2; }
 
 const char* fmha_status_string(int status) {
   switch (status) {
@@ -256,6 +256,25 @@ int fmha_fwd(const fmha_fwd_args* a, void* stream) {
   }
   FMHA_LOG("fwd fp32 B=%d H=%d Nq=%d Nk=%d D=%d mask=%d", a->B, a->H, a->Nq, a->Nk, a->Dqk, a->mask.kind);
   return hip_status(fmha::launch_fwd_f32(p, a->Dqk, st));
+}
+
+int fmha_fwd_varlen(const fmha_fwd_args* a, const fmha_varlen* vl, void* stream) {
+  if (a == nullptr || vl == nullptr) return FMHA_ERR_INVALID_ARG;
+  int rc = validate_fwd(a);
+  if (rc != FMHA_OK) return rc;
+  if (vl->reserved != 0 || vl->total_q < 0 || !vl->cu_seqlens_q || !vl->cu_seqlens_k) return FMHA_ERR_INVALID_ARG;
+  if (a->dtype != FMHA_BF16 || !multi_head(a) || a->block_sparse != nullptr || a->mask.kind == FMHA_MASK_BLOCK_DIAGONAL)
+    return FMHA_ERR_UNSUPPORTED;
+  if ((int64_t)a->B * a->H * a->Nq == 0 || vl->total_q == 0) return FMHA_OK;
+  rc = check_device();
+  if (rc != FMHA_OK) return rc;
+  AttnParams p = attn_params(a);
+  p.cu_q = vl->cu_seqlens_q;
+  p.cu_k = vl->cu_seqlens_k;
+  p.lse_total = vl->total_q;
+  FMHA_LOG("fwd varlen bf16 B=%d H=%d maxNq=%d maxNk=%d total_q=%d Dqk=%d Dv=%d mask=%d", a->B, a->H, a->Nq, a->Nk,
+           vl->total_q, a->Dqk, a->Dv, a->mask.kind);
+  return hip_status(fmha::launch_fwd_bf16(p, a->Dqk, a->Dv, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t fmha_bwd_workspace_size(int32_t B, int32_t H, int32_t Nq) {

@@ -101,11 +101,26 @@ void fwd_bf16_kernel(const AttnParams p) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so per-wave tests branch on scalars
   const int l = tid & 63, g = l >> 5, lq = l & 31;
-  const int Nq = p.Nq, Nk = p.Nk, delta = Nk - Nq;
+  // sequence b: its lengths, the offsets of its first query / key row and of its LSE row
+  int Nq = p.Nq, Nk = p.Nk;
+  int64_t q_off = b * p.qs_b, k_off = b * p.ks_b, v_off = b * p.vs_b, o_off = b * p.os_b;
+  int64_t lse_off = ((int64_t)b * p.H + h) * Nq;
+  if (p.cu_q != nullptr) {   // packed variable-length sequences (the grid covers the longest)
+    const int qs = p.cu_q[b], ks = p.cu_k[b];
+    Nq = p.cu_q[b + 1] - qs;
+    Nk = p.cu_k[b + 1] - ks;
+    if (q0 >= Nq) return;    // whole workgroup, before any barrier
+    q_off = (int64_t)qs * p.qs_s;
+    k_off = (int64_t)ks * p.ks_s;
+    v_off = (int64_t)ks * p.vs_s;
+    o_off = (int64_t)qs * p.os_s;
+    lse_off = (int64_t)h * p.lse_total + qs;
+  }
+  const int delta = Nk - Nq;
 
-  const __bf16* Qg = (const __bf16*)p.q + b * p.qs_b + h * p.qs_h;
-  const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + h * p.ks_h;
-  const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + h * p.vs_h;
+  const __bf16* Qg = (const __bf16*)p.q + q_off + h * p.qs_h;
+  const __bf16* Kg = (const __bf16*)p.k + k_off + h * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + v_off + h * p.vs_h;
 
   // ---- tile sequence
   TileSeq<kBN> seq;
@@ -330,7 +345,7 @@ void fwd_bf16_kernel(const AttnParams p) {
   const bool empty = !(l_tot > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (qrow < Nq) {
-    __bf16* Og = (__bf16*)p.o + b * p.os_b + h * p.os_h + (int64_t)qrow * p.os_s;
+    __bf16* Og = (__bf16*)p.o + o_off + h * p.os_h + (int64_t)qrow * p.os_s;
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
@@ -341,7 +356,7 @@ void fwd_bf16_kernel(const AttnParams p) {
         *(u32x2*)(Og + 32 * db + 8 * jj + 4 * g) = v;
       }
     if (g == 0) {
-      p.lse[((int64_t)b * p.H + h) * Nq + qrow] = empty ? kNegInf : (m_run + fast_log2(l_tot)) * kLn2;
+      p.lse[lse_off + qrow] = empty ? kNegInf : (m_run + fast_log2(l_tot)) * kLn2;
     }
   }
 }

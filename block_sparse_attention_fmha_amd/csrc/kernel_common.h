@@ -88,6 +88,12 @@ struct AttnParams {
   float bias_log2;    // relative-bias slope * log2(e)
   MaskParams mask;
   ListParams lists;
+  // packed variable-length sequences (forward only; nullptr = fixed lengths): batch b is
+  // the sequence of queries [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]) along the
+  // sequence axis (the batch strides are unused); LSE is [H, lse_total]
+  const int* cu_q;
+  const int* cu_k;
+  int64_t lse_total;
 };
 
 struct BwdParams {

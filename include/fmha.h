@@ -196,6 +196,30 @@ size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t
 int fmha_fwd_splitkv(const fmha_fwd_args* args, int32_t num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Packed variable-length sequences ("Enable 2CTA for SM100 block-sparse backward",
+ * section "Testing Testing Testing": the forward's cu_seqlens_q / cu_seqlens_k and
+ * seqused arguments). Sequence b (0 <= b < args->B) owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b], cu_seqlens_k[b+1])
+ * of Q [total_q, H, Dqk], K / V [total_k, H, D*] and O [total_q, H, Dv], addressed with
+ * the seq and head strides of fmha_fwd_args (its batch strides are ignored). The offset
+ * arrays are device int32 [B + 1], ascending, starting at 0; they are read on the device
+ * only, so the caller guarantees that every query length is <= args->Nq, every key length
+ * <= args->Nk, and every row lies inside the tensors. Masks apply within each sequence
+ * (delta = that sequence's key length minus its query length). LSE is fp32 [H, total_q]. */
+typedef struct {
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t total_q;     /* cu_seqlens_q[B] */
+  int32_t reserved;    /* must be 0 */
+} fmha_varlen;
+
+/* Forward over packed variable-length sequences: as fmha_fwd with args->B sequences of at
+ * most args->Nq queries and args->Nk keys. bf16 only; causal, sliding-window, prefix-LM or
+ * no mask (block-diagonal masks and block-sparse lists: FMHA_ERR_UNSUPPORTED; each
+ * sequence already is one document); softcap and relative bias as in fmha_fwd (i, j are
+ * positions within the sequence). */
+int fmha_fwd_varlen(const fmha_fwd_args* args, const fmha_varlen* varlen, void* stream);
+
 /* Block-sparse tile mask builder: classifies every (tile_m x tile_n) tile of the
  * element mask as empty / partial / full by counting visible in-bounds elements, and
  * writes the forward and transposed index lists into the caller-allocated arrays of
@@ -209,7 +233,7 @@ int build_block_mask(const fmha_mask* mask, int32_t B, int32_t Hm, int32_t Nq, i
 const char* fmha_status_string(int status);
 
 /* ABI version: bumped whenever a struct layout changes. */
-int fmha_abi_version(void);
+int fmha_abi_version(void);   /* 2: kv_heads, fmha_fwd_varlen */
 
 #ifdef __cplusplus
 }

@@ -133,6 +133,32 @@ def forward(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: MaskSpec 
     return o, lse
 
 
+def forward_varlen(q, k, v, cu_q, cu_k, *, scale=None, softcap=0.0, bias_slope=0.0,
+                   mask: MaskSpec = MaskSpec()):
+    """Packed variable-length sequences (the forward's cu_seqlens arguments of "Enable 2CTA
+    for SM100 block-sparse backward", section "Testing Testing Testing"): q [total_q,H,Dqk],
+    k [total_k,H,Dqk], v [total_k,H,Dv]; sequence b is query rows cu_q[b]:cu_q[b+1] and key
+    rows cu_k[b]:cu_k[b+1], attended as its own batch entry (positions, masks and the
+    relative bias are sequence-local). Returns o [total_q,H,Dv], lse [H,total_q]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    total_q, H, dqk = q.shape
+    dv = v.shape[2]
+    scale = default_scale(dqk) if scale is None else scale
+    o = np.zeros((total_q, H, dv))
+    lse = np.full((H, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qe == qs:
+            continue
+        if ke == ks:   # no keys: every row is fully masked
+            continue
+        ob, lb = forward(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], scale=scale, softcap=softcap,
+                         bias_slope=bias_slope, mask=mask)
+        o[qs:qe] = ob[0]
+        lse[:, qs:qe] = lb[0]
+    return o, lse
+
+
 def backward_bh(q, k, v, do, b, h, *, scale, softcap=0.0, bias_slope=0.0,
                 mask: MaskSpec = MaskSpec(), lists=None, lse=None):
     """Backward for one (b, h), all rows. Recomputes P from LSE (the oracle's own LSE

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fmha_abi_version() == 1
+    assert lib.fmha_abi_version() == 2
     assert fa.status_string(0) == "FMHA_OK"
     assert fa.status_string(-4) == "FMHA_ERR_WORKSPACE"
     assert fa.status_string(12345) == "FMHA_ERR_UNKNOWN"
@@ -223,3 +223,41 @@ def test_ctypes_layout_matches_c_compiler(tmp_path):
         "sizeof.bs": ctypes.sizeof(fa.CBlockSparse), "sizeof.mask": ctypes.sizeof(fa.CMask),
     }
     assert {k: int(v) for k, v in got.items()} == want
+
+
+def test_varlen_argument_checks(lib):
+    a = _args()
+    vl = fa.CVarlen()
+    vl.cu_seqlens_q = vl.cu_seqlens_k = 0x200000
+    vl.total_q, vl.reserved = 64, 0
+    assert lib.fmha_fwd_varlen(ctypes.byref(a), None, None) == fa.FMHA_ERR_INVALID_ARG
+    bad = fa.CVarlen()
+    bad.cu_seqlens_q, bad.cu_seqlens_k, bad.total_q = 0x200000, None, 64
+    assert lib.fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(bad), None) == fa.FMHA_ERR_INVALID_ARG
+    bad.cu_seqlens_k, bad.total_q = 0x200000, -1
+    assert lib.fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(bad), None) == fa.FMHA_ERR_INVALID_ARG
+    bad.total_q, bad.reserved = 64, 1
+    assert lib.fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(bad), None) == fa.FMHA_ERR_INVALID_ARG
+    for kw in ({"dtype": fa.FMHA_FP32}, {"kv_heads": 1}):
+        b = _args(**kw)
+        assert lib.fmha_fwd_varlen(ctypes.byref(b), ctypes.byref(vl), None) == fa.FMHA_ERR_UNSUPPORTED
+    b = _args()
+    b.mask.kind = fa.MASK_KINDS["block_diagonal"]
+    b.mask.doc_q = b.mask.doc_k = 0x200000
+    assert lib.fmha_fwd_varlen(ctypes.byref(b), ctypes.byref(vl), None) == fa.FMHA_ERR_UNSUPPORTED
+
+
+def test_varlen_struct_layout(tmp_path):
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "vl.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fmha.h"\n'
+                   'int main(void) { printf("%zu %zu %zu\\n", offsetof(fmha_varlen, total_q),'
+                   ' offsetof(fmha_varlen, reserved), sizeof(fmha_varlen)); return 0; }\n')
+    exe = tmp_path / "vl"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [fa.CVarlen.total_q.offset, fa.CVarlen.reserved.offset, ctypes.sizeof(fa.CVarlen)]

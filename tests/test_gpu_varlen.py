@@ -1,0 +1,58 @@
+"""GPU parity of the packed variable-length forward (fmha_fwd_varlen) against the fp64
+oracle's per-sequence definition."""
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_attention_fmha_amd import synth
+from tests.gpu_util import announce, check_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(seed, lq, lk, H, dqk, dv, kind, window=0, prefix=0, softcap=0.0, slope=0.0):
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    # packed rows from the shared seeded generator: [1, total, H, D] -> [total, H, D]
+    q = synth.attention_inputs(seed, 1, int(cu_q[-1]), int(cu_k[-1]), H, dqk, dv, "bf16")
+    qv, kv, vv = (x.values[0] for x in q)
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (x.to_torch(dev)[0] for x in q)
+    announce(f"varlen fwd seed={seed} seqs={len(lq)} total_q={cu_q[-1]} total_k={cu_k[-1]} H={H} "
+             f"D={dqk}/{dv} mask={kind} W={window} P={prefix} softcap={softcap} bias={slope}")
+    out, lse = fa.fmha_fwd_varlen(tq, tk, tv, torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev),
+                                  max(lq), max(lk), mask=fa.Mask(kind, window=window, prefix=prefix),
+                                  softcap=softcap, bias_slope=slope)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.forward_varlen(qv, kv, vv, cu_q, cu_k, softcap=softcap, bias_slope=slope,
+                                         mask=oracle.MaskSpec(kind, window=window, prefix=prefix))
+    check_bf16("O", host(out), o_ref)
+    check_bf16("LSE", host(lse), l_ref)
+
+
+CASES = [
+    # (query lengths, key lengths, H, Dqk, Dv, mask, window, prefix, softcap, slope)
+    ([300, 1, 700, 256, 129], [300, 1, 700, 256, 129], 2, 128, 128, "causal", 0, 0, 0.0, 0.0),
+    ([513, 40, 1000], [769, 200, 1000], 2, 128, 128, "causal", 0, 0, 0.0, 0.0),        # Nk > Nq per sequence
+    ([257, 600], [129, 100], 2, 128, 128, "causal", 0, 0, 0.0, 0.0),                  # rows with no key
+    ([640, 333, 77], [640, 333, 77], 2, 64, 64, "sliding_window", 100, 0, 30.0, 0.0),
+    ([384, 500, 2], [384, 500, 2], 2, 128, 128, "prefix_lm", 0, 100, 0.0, -0.01),
+    ([255, 385], [385, 255], 2, 192, 128, "none", 0, 0, 0.0, -0.05),
+    ([1000, 0, 300], [1000, 50, 0], 1, 128, 128, "none", 0, 0, 0.0, 0.0),             # empty sequences
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_varlen_forward(case):
+    lq, lk, H, dqk, dv, kind, w, p, cap, slope = CASES[case]
+    _run(synth.case_seed(9, 800 + case), lq, lk, H, dqk, dv, kind, w, p, cap, slope)
+
+
+def test_varlen_documents_of_the_block_sparse_workload():
+    # the block-diagonal workload's documents (B=2 rows of N=8192, lengths 256..2048) packed
+    # as one sequence each, no mask inside a document
+    docs = synth.document_ids(synth.case_seed(3, 2), 2, 8192)
+    lens = [int(c) for b in range(2) for c in np.bincount(docs[b])]
+    _run(synth.case_seed(9, 850), lens, lens, 2, 128, 128, "none", slope=-0.01)
