@@ -303,7 +303,16 @@ def all_configs_report():
         log(workload="bwd_bf16_block_sparse", N=n, B=bsz, H=hh, D=128, mask=kind, ms=round(ms, 4),
             tflops=round(fb / ms / 1e9, 1), frac=round(fb / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
         del do, out, lse, dq, dk, dv_, ws
-    del q, k, v
+    # the same documents as packed variable-length sequences (no mask inside a document,
+    # same bias): the block-diagonal workload without lists
+    lens = [int(c) for b in range(bsz) for c in np.bincount(docs[b])]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=dev)
+    qp, kp, vp = (x.reshape(bsz * n, hh, 128) for x in (q, k, v))
+    ms = timeit(lambda: fa.fmha_fwd_varlen(qp, kp, vp, cu, cu, max(lens), max(lens), bias_slope=-0.01))
+    f = 2.0 * hh * 256 * visible_pairs("block_diagonal", n, 0, 0, docs)
+    log(workload="fwd_bf16_varlen_documents", N=n, B=bsz, H=hh, D=128, sequences=len(lens), ms=round(ms, 4),
+        tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+    del q, k, v, qp, kp, vp
     # backward workloads (causal, B=1 H=16), incl. the MLA-shaped head Dqk=192 Dv=128
     for n, dqk, dv in ((4096, 64, 64), (4096, 128, 128), (16384, 64, 64), (8192, 192, 128)):
         q = torch.randn(1, n, 16, dqk, device=dev).bfloat16()
