@@ -27,7 +27,7 @@ FMHA_OK, FMHA_ERR_INVALID_ARG, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP, FMHA_ERR_WORK
 FMHA_BF16, FMHA_FP32 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding_window": 2, "block_diagonal": 3, "prefix_lm": 4}
 ENTRY_POINTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_splitkv",
-                "fmha_fwd_splitkv_workspace_size", "fmha_fwd_varlen", "build_block_mask",
+                "fmha_fwd_splitkv_workspace_size", "fmha_fwd_varlen", "fmha_bwd_varlen", "build_block_mask",
                 "fmha_status_string", "fmha_abi_version")
 
 
@@ -112,6 +112,9 @@ def load_library():
     lib.fmha_fwd_splitkv.restype = ctypes.c_int
     lib.fmha_fwd_varlen.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.POINTER(CVarlen), ctypes.c_void_p]
     lib.fmha_fwd_varlen.restype = ctypes.c_int
+    lib.fmha_bwd_varlen.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.POINTER(CBwdArgs), ctypes.POINTER(CVarlen),
+                                    ctypes.c_void_p]
+    lib.fmha_bwd_varlen.restype = ctypes.c_int
     lib.fmha_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.build_block_mask.argtypes = [ctypes.POINTER(CMask)] + [ctypes.c_int32] * 6 + [
@@ -367,6 +370,52 @@ def fmha_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     vl.total_q, vl.reserved = total_q, 0
     _check(load_library().fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(vl), _stream(stream)), "fmha_fwd_varlen")
     return out, lse
+
+
+def fmha_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
+                    scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | None = None, dq=None, dk=None,
+                    dv=None, workspace=None, stream=None):
+    """Backward over packed variable-length sequences (layouts of fmha_fwd_varlen): returns
+    (dq [total_q, H, Dqk], dk, dv [total_k, H, D]) in bf16."""
+    import torch
+    lib = load_library()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or out.dim() != 3 or dout.dim() != 3:
+        raise ValueError("varlen tensors are [total, H, D]")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        _need_device(t, "cu_seqlens")
+        if str(t.dtype) != "torch.int32" or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] device tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 offsets")
+    total_q, H, _ = q.shape
+    B = cu_seqlens_q.numel() - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = lib.fmha_bwd_workspace_size(B, H, int(max_seqlen_q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    for t, n in ((dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace")):
+        _need_device(t, n)
+    if dout.shape != out.shape or dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shapes must match q / k / v / out")
+    if tuple(lse.shape) != (H, total_q):
+        raise ValueError("lse must be [H, total_q]")
+    a, _keep = _fwd_args(q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), out.unsqueeze(0),
+                         lse.view(1, H, total_q), scale, softcap, bias_slope, mask, None)
+    a.B = B
+    a.Nq, a.Nk = int(max_seqlen_q), int(max_seqlen_k)
+    g = CBwdArgs()
+    g.dout, g.dq, g.dk, g.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    g.do_stride, g.dq_stride, g.dk_stride, g.dv_stride = (_strides(t.unsqueeze(0)) for t in (dout, dq, dk, dv))
+    g.workspace = workspace.data_ptr()
+    g.workspace_bytes = workspace.numel() * workspace.element_size()
+    vl = CVarlen()
+    vl.cu_seqlens_q, vl.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    vl.total_q, vl.reserved = total_q, 0
+    _check(lib.fmha_bwd_varlen(ctypes.byref(a), ctypes.byref(g), ctypes.byref(vl), _stream(stream)),
+           "fmha_bwd_varlen")
+    return dq, dk, dv
 
 
 def splitkv_workspace_size(B, H, Nq, Dv, num_splits) -> int:

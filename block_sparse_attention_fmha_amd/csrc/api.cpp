@@ -282,11 +282,17 @@ size_t fmha_bwd_workspace_size(int32_t B, int32_t H, int32_t Nq) {
   return align256(fmha::bwd_workspace_bytes(B, H, Nq));
 }
 
-int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
+// fmha_bwd and fmha_bwd_varlen (vl != nullptr: packed variable-length sequences)
+static int bwd_impl(const fmha_fwd_args* a, const fmha_bwd_args* g, const fmha_varlen* vl, void* stream) {
   int rc = validate_fwd(a);
   if (rc != FMHA_OK) return rc;
   if (!multi_head(a)) return FMHA_ERR_UNSUPPORTED;
   if (g == nullptr) return FMHA_ERR_INVALID_ARG;
+  if (vl != nullptr) {
+    if (vl->reserved != 0 || vl->total_q < 0 || !vl->cu_seqlens_q || !vl->cu_seqlens_k) return FMHA_ERR_INVALID_ARG;
+    if (a->block_sparse != nullptr || a->mask.kind == FMHA_MASK_BLOCK_DIAGONAL) return FMHA_ERR_UNSUPPORTED;
+    if (vl->total_q == 0) return FMHA_OK;
+  }
   if (a->dtype != FMHA_BF16) return FMHA_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->H * a->Nq == 0 && (int64_t)a->B * a->H * a->Nk == 0) return FMHA_OK;
   if (a->Nq == 0 || a->Nk == 0) return FMHA_ERR_UNSUPPORTED;  // empty side: nothing sensible to launch
@@ -321,9 +327,21 @@ int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) {
   bp.dks_b = g->dk_stride[0]; bp.dks_s = g->dk_stride[1]; bp.dks_h = g->dk_stride[2];
   bp.dvs_b = g->dv_stride[0]; bp.dvs_s = g->dv_stride[1]; bp.dvs_h = g->dv_stride[2];
   bp.stage_events = g->stage_events;
-  FMHA_LOG("bwd bf16 B=%d H=%d Nq=%d Nk=%d Dqk=%d Dv=%d mask=%d lists=%d", a->B, a->H, a->Nq, a->Nk, a->Dqk,
-           a->Dv, a->mask.kind, a->block_sparse != nullptr);
+  if (vl != nullptr) {
+    bp.a.cu_q = vl->cu_seqlens_q;
+    bp.a.cu_k = vl->cu_seqlens_k;
+    bp.a.lse_total = vl->total_q;
+  }
+  FMHA_LOG("bwd bf16 B=%d H=%d Nq=%d Nk=%d Dqk=%d Dv=%d mask=%d lists=%d varlen=%d", a->B, a->H, a->Nq, a->Nk,
+           a->Dqk, a->Dv, a->mask.kind, a->block_sparse != nullptr, vl != nullptr);
   return hip_status(fmha::launch_bwd_bf16(bp, a->Dqk, a->Dv, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fmha_bwd(const fmha_fwd_args* a, const fmha_bwd_args* g, void* stream) { return bwd_impl(a, g, nullptr, stream); }
+
+int fmha_bwd_varlen(const fmha_fwd_args* a, const fmha_bwd_args* g, const fmha_varlen* vl, void* stream) {
+  if (vl == nullptr) return FMHA_ERR_INVALID_ARG;
+  return bwd_impl(a, g, vl, stream);
 }
 
 size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t Dv, int32_t num_splits) {

@@ -74,16 +74,19 @@ void bwd_preprocess_kernel(const BwdParams bp) {
   if (in) {
     i = (int)(r % npad);
     bh = r / npad;
-    if (i < p.Nq) {
-      const int h = (int)(bh % p.H), b = (int)(bh / p.H);
-      const __bf16* Og = (const __bf16*)p.o + b * p.os_b + h * p.os_h + (int64_t)i * p.os_s + 8 * dl;
-      const __bf16* Dg = (const __bf16*)bp.dout + b * bp.dos_b + h * bp.dos_h + (int64_t)i * bp.dos_s + 8 * dl;
+    const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+    const SeqInfo sq = seq_info(p, b);
+    if (i < sq.nq) {
+      const __bf16* Og = (const __bf16*)p.o + row_base(sq, true, b, p.os_b, p.os_s) + h * p.os_h +
+                         (int64_t)i * p.os_s + 8 * dl;
+      const __bf16* Dg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h * bp.dos_h +
+                         (int64_t)i * bp.dos_s + 8 * dl;
       float of[8], df[8];
       bf16x8_to_f32(*(const u32x4*)Og, of);
       bf16x8_to_f32(*(const u32x4*)Dg, df);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x = __builtin_fmaf(of[e], df[e], x);
-      const float ls = p.lse[bh * p.Nq + i];
+      const float ls = p.lse[lse_base(p, sq, b, h) + i];
       lse2 = (ls == kNegInf) ? __builtin_huge_valf() : ls * kLog2e;
     }
   }
@@ -132,14 +135,16 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   const int l = tid & 63, g = l >> 5, lq = l & 31;
   const int role = w >> 2;     // 0: P wave (K; S, P, dV), 1: dS wave (V; dP, dS, dK)
   const int pair = w & 3;      // waves w and w + 4 share a SIMD and the same 32 keys
-  const int Nq = p.Nq, Nk = p.Nk, delta = Nk - Nq;
+  const SeqInfo sq = seq_info(p, b);
+  const int Nq = sq.nq, Nk = sq.nk, delta = Nk - Nq;
+  if (k0 >= Nk) return;        // packed sequences: past this one's keys (whole workgroup, no barrier yet)
   const int kw = k0 + 32 * pair;
   const int key = kw + lq;
 
-  const __bf16* Qg = (const __bf16*)p.q + b * p.qs_b + h * p.qs_h;
-  const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + h * p.ks_h;
-  const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + h * p.vs_h;
-  const __bf16* DOg = (const __bf16*)bp.dout + b * bp.dos_b + h * bp.dos_h;
+  const __bf16* Qg = (const __bf16*)p.q + row_base(sq, true, b, p.qs_b, p.qs_s) + h * p.qs_h;
+  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + h * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + h * p.vs_h;
+  const __bf16* DOg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h * bp.dos_h;
   const char* WSg = (const char*)(bp.ws + (int64_t)bh * bp.n_qblk * 128);
 
   // ---- query-step sequence
@@ -350,8 +355,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   // each role's own path, so registers only one role uses are not kept live by the other.
   auto store = [&](bool isk) {
     if (key >= Nk) return;
-    __bf16* dst = isk ? (__bf16*)bp.dk + b * bp.dks_b + h * bp.dks_h + (int64_t)key * bp.dks_s
-                      : (__bf16*)bp.dv + b * bp.dvs_b + h * bp.dvs_h + (int64_t)key * bp.dvs_s;
+    __bf16* dst = isk ? (__bf16*)bp.dk + row_base(sq, false, b, bp.dks_b, bp.dks_s) + h * bp.dks_h + (int64_t)key * bp.dks_s
+                      : (__bf16*)bp.dv + row_base(sq, false, b, bp.dvs_b, bp.dvs_s) + h * bp.dvs_h + (int64_t)key * bp.dvs_s;
     const float sc = isk ? p.scale : 1.0f;
     const int dw = isk ? DQK : DV;
 #pragma unroll
@@ -449,14 +454,16 @@ void bwd_dq_kernel(const BwdParams bp) {
   const int l = tid & 63, g = l >> 5, lq = l & 31;
   const int role = w >> 2;     // 0: S wave (Q; S^T, P), 1: dQ wave (dO; dP^T, dS, dQ^T)
   const int pair = w & 3;      // waves w and w + 4 share a SIMD and the same 32 queries
-  const int Nq = p.Nq, Nk = p.Nk, delta = Nk - Nq;
+  const SeqInfo sq = seq_info(p, b);
+  const int Nq = sq.nq, Nk = sq.nk, delta = Nk - Nq;
+  if (q0 >= Nq) return;        // packed sequences: past this one's queries (whole workgroup, no barrier yet)
   const int qw = q0 + 32 * pair;
   const int qrow = qw + lq;
 
-  const __bf16* Qg = (const __bf16*)p.q + b * p.qs_b + h * p.qs_h;
-  const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + h * p.ks_h;
-  const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + h * p.vs_h;
-  const __bf16* DOg = (const __bf16*)bp.dout + b * bp.dos_b + h * bp.dos_h;
+  const __bf16* Qg = (const __bf16*)p.q + row_base(sq, true, b, p.qs_b, p.qs_s) + h * p.qs_h;
+  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + h * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + h * p.vs_h;
+  const __bf16* DOg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h * bp.dos_h;
 
   // ---- key-tile sequence (same bands / lists as the forward)
   TileSeq<kKN> seq;
@@ -640,7 +647,7 @@ void bwd_dq_kernel(const BwdParams bp) {
   // on the dQ waves' own path, so the S waves do not keep dq[] live through their loop
   auto store = [&]() {
     if (qrow >= Nq) return;
-    __bf16* dQg = (__bf16*)bp.dq + b * bp.dqs_b + h * bp.dqs_h + (int64_t)qrow * bp.dqs_s;
+    __bf16* dQg = (__bf16*)bp.dq + row_base(sq, true, b, bp.dqs_b, bp.dqs_s) + h * bp.dqs_h + (int64_t)qrow * bp.dqs_s;
 #pragma unroll
     for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll

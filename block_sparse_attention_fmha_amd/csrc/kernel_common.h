@@ -114,6 +114,33 @@ struct BwdParams {
   int grid_padded_kv;
 };
 
+// Batch entry b: its query / key lengths and first rows. Fixed lengths: every entry has
+// p.Nq / p.Nk rows at batch stride b; packed varlen: rows cu[b] .. cu[b+1] of the packed
+// sequence axis. row_base() is the element offset of the entry's row 0 in one tensor;
+// lse_base() that of (b, h, row 0) in LSE ([B, H, Nq], or [H, total_q] when packed).
+struct SeqInfo {
+  int nq, nk, qs, ks;
+  bool packed;
+};
+__device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int b) {
+  SeqInfo s{p.Nq, p.Nk, 0, 0, false};
+  if (p.cu_q != nullptr) {
+    s.qs = p.cu_q[b];
+    s.ks = p.cu_k[b];
+    s.nq = p.cu_q[b + 1] - s.qs;
+    s.nk = p.cu_k[b + 1] - s.ks;
+    s.packed = true;
+  }
+  return s;
+}
+__device__ __forceinline__ int64_t row_base(const SeqInfo& s, bool query_axis, int b, int64_t stride_b,
+                                            int64_t stride_s) {
+  return s.packed ? (int64_t)(query_axis ? s.qs : s.ks) * stride_s : (int64_t)b * stride_b;
+}
+__device__ __forceinline__ int64_t lse_base(const AttnParams& p, const SeqInfo& s, int b, int h) {
+  return s.packed ? (int64_t)h * p.lse_total + s.qs : ((int64_t)b * p.H + h) * p.Nq;
+}
+
 // ---------------------------------------------------------------------------------------
 // Small device helpers.
 

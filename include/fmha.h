@@ -220,6 +220,13 @@ typedef struct {
  * positions within the sequence). */
 int fmha_fwd_varlen(const fmha_fwd_args* args, const fmha_varlen* varlen, void* stream);
 
+/* Backward over packed variable-length sequences: as fmha_bwd, with the sequences, masks
+ * and LSE layout of fmha_fwd_varlen (dO, dQ, dK, dV are packed like O, Q, K, V). The
+ * workspace is fmha_bwd_workspace_size(B, H, args->Nq) with args->Nq the longest query
+ * sequence. Block-diagonal masks and block-sparse lists: FMHA_ERR_UNSUPPORTED. */
+int fmha_bwd_varlen(const fmha_fwd_args* args, const fmha_bwd_args* bwd, const fmha_varlen* varlen,
+                    void* stream);
+
 /* Block-sparse tile mask builder: classifies every (tile_m x tile_n) tile of the
  * element mask as empty / partial / full by counting visible in-bounds elements, and
  * writes the forward and transposed index lists into the caller-allocated arrays of
@@ -233,7 +240,7 @@ int build_block_mask(const fmha_mask* mask, int32_t B, int32_t Hm, int32_t Nq, i
 const char* fmha_status_string(int status);
 
 /* ABI version: bumped whenever a struct layout changes. */
-int fmha_abi_version(void);   /* 2: kv_heads, fmha_fwd_varlen */
+int fmha_abi_version(void);   /* 2: kv_heads, fmha_fwd_varlen, fmha_bwd_varlen */
 
 #ifdef __cplusplus
 }

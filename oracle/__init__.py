@@ -28,7 +28,7 @@ tiling, fusion or reordering beyond what the definition states.
 """
 from .masks import MaskSpec, allowed, block_sparse_allowed  # noqa: F401
 from .attention import (  # noqa: F401
-    forward, forward_bh, forward_varlen, backward, backward_bh, scores_bh, kv_head,
+    forward, forward_bh, forward_varlen, backward, backward_bh, backward_varlen, scores_bh, kv_head,
     split_partials, combine_partials, streaming_forward_bh,
 )
 from .blockmask import classify_tiles, build_lists, BlockLists  # noqa: F401

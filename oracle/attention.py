@@ -159,6 +159,28 @@ def forward_varlen(q, k, v, cu_q, cu_k, *, scale=None, softcap=0.0, bias_slope=0
     return o, lse
 
 
+def backward_varlen(q, k, v, do, cu_q, cu_k, *, scale=None, softcap=0.0, bias_slope=0.0,
+                    mask: MaskSpec = MaskSpec()):
+    """Backward of forward_varlen: each sequence as its own batch entry (the batched
+    backward on its rows). Returns dq [total_q,H,Dqk], dk, dv [total_k,H,D], o, lse
+    [H,total_q]; rows of sequences without keys get zero gradients."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    total_q, H, dqk = q.shape
+    scale = default_scale(dqk) if scale is None else scale
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    o = np.zeros((total_q, H, v.shape[2]))
+    lse = np.full((H, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qe == qs or ke == ks:
+            continue
+        gq, gk, gv, ob, lb = backward(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], do[None, qs:qe], scale=scale,
+                                      softcap=softcap, bias_slope=bias_slope, mask=mask)
+        dq[qs:qe], dk[ks:ke], dv[ks:ke] = gq[0], gk[0], gv[0]
+        o[qs:qe], lse[:, qs:qe] = ob[0], lb[0]
+    return dq, dk, dv, o, lse
+
+
 def backward_bh(q, k, v, do, b, h, *, scale, softcap=0.0, bias_slope=0.0,
                 mask: MaskSpec = MaskSpec(), lists=None, lse=None):
     """Backward for one (b, h), all rows. Recomputes P from LSE (the oracle's own LSE

@@ -5,21 +5,21 @@ import pytest
 
 import oracle
 from block_sparse_attention_fmha_amd import synth
-from tests.gpu_util import announce, check_bf16, host
+from tests.gpu_util import announce, check_bf16, check_grad, host
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(seed, lq, lk, H, dqk, dv, kind, window=0, prefix=0, softcap=0.0, slope=0.0):
+def _run(seed, lq, lk, H, dqk, dv, kind, window=0, prefix=0, softcap=0.0, slope=0.0, backward=False):
     import torch
     import block_sparse_attention_fmha_amd as fa
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
     # packed rows from the shared seeded generator: [1, total, H, D] -> [total, H, D]
-    q = synth.attention_inputs(seed, 1, int(cu_q[-1]), int(cu_k[-1]), H, dqk, dv, "bf16")
-    qv, kv, vv = (x.values[0] for x in q)
+    q = synth.attention_inputs(seed, 1, int(cu_q[-1]), int(cu_k[-1]), H, dqk, dv, "bf16", with_dout=True)
+    qv, kv, vv, dov = (x.values[0] for x in q)
     dev = torch.device("cuda:0")
-    tq, tk, tv = (x.to_torch(dev)[0] for x in q)
+    tq, tk, tv, tdo = (x.to_torch(dev)[0] for x in q)
     announce(f"varlen fwd seed={seed} seqs={len(lq)} total_q={cu_q[-1]} total_k={cu_k[-1]} H={H} "
              f"D={dqk}/{dv} mask={kind} W={window} P={prefix} softcap={softcap} bias={slope}")
     out, lse = fa.fmha_fwd_varlen(tq, tk, tv, torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev),
@@ -30,6 +30,16 @@ def _run(seed, lq, lk, H, dqk, dv, kind, window=0, prefix=0, softcap=0.0, slope=
                                          mask=oracle.MaskSpec(kind, window=window, prefix=prefix))
     check_bf16("O", host(out), o_ref)
     check_bf16("LSE", host(lse), l_ref)
+    if backward:
+        tcu_q, tcu_k = torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev)
+        dq, dk, dv_ = fa.fmha_bwd_varlen(tq, tk, tv, out, lse, tdo, tcu_q, tcu_k, max(lq), max(lk),
+                                         mask=fa.Mask(kind, window=window, prefix=prefix), softcap=softcap,
+                                         bias_slope=slope)
+        torch.cuda.synchronize()
+        ref = oracle.backward_varlen(qv, kv, vv, dov, cu_q, cu_k, softcap=softcap, bias_slope=slope,
+                                     mask=oracle.MaskSpec(kind, window=window, prefix=prefix))
+        for name, got, want in (("dQ", dq, ref[0]), ("dK", dk, ref[1]), ("dV", dv_, ref[2])):
+            check_grad(name, host(got), want)
 
 
 CASES = [
@@ -56,3 +66,9 @@ def test_varlen_documents_of_the_block_sparse_workload():
     docs = synth.document_ids(synth.case_seed(3, 2), 2, 8192)
     lens = [int(c) for b in range(2) for c in np.bincount(docs[b])]
     _run(synth.case_seed(9, 850), lens, lens, 2, 128, 128, "none", slope=-0.01)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_varlen_backward(case):
+    lq, lk, H, dqk, dv, kind, w, p, cap, slope = CASES[case]
+    _run(synth.case_seed(9, 900 + case), lq, lk, H, dqk, dv, kind, w, p, cap, slope, backward=True)

@@ -37,3 +37,18 @@ def test_each_sequence_is_its_own_problem():
             continue
         ob, lb = oracle.forward(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], mask=m)
         assert np.array_equal(o[qs:qe], ob[0]) and np.array_equal(lse[:, qs:qe], lb[0])
+
+
+@pytest.mark.parametrize("kind", ["causal", "sliding_window"])
+def test_backward_equal_lengths_equal_the_batched_backward(kind):
+    rng = np.random.default_rng(9)
+    B, Nq, Nk, H, D = 2, 6, 5, 2, 3
+    q, k, v, do = (rng.standard_normal(s) for s in ((B, Nq, H, D), (B, Nk, H, D), (B, Nk, H, D), (B, Nq, H, D)))
+    m = oracle.MaskSpec(kind, window=2)
+    ref = oracle.backward(q, k, v, do, mask=m, bias_slope=0.05)
+    cu_q, cu_k = np.arange(B + 1) * Nq, np.arange(B + 1) * Nk
+    got = oracle.backward_varlen(q.reshape(-1, H, D), k.reshape(-1, H, D), v.reshape(-1, H, D),
+                                 do.reshape(-1, H, D), cu_q, cu_k, mask=m, bias_slope=0.05)
+    for g, r in zip(got[:4], ref[:4]):
+        assert np.array_equal(g, r.reshape(g.shape))
+    assert np.array_equal(got[4], ref[4].transpose(1, 0, 2).reshape(H, B * Nq))
