@@ -312,7 +312,13 @@ def all_configs_report():
     f = 2.0 * hh * 256 * visible_pairs("block_diagonal", n, 0, 0, docs)
     log(workload="fwd_bf16_varlen_documents", N=n, B=bsz, H=hh, D=128, sequences=len(lens), ms=round(ms, 4),
         tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
-    del q, k, v, qp, kp, vp
+    out, lse = fa.fmha_fwd_varlen(qp, kp, vp, cu, cu, max(lens), max(lens), bias_slope=-0.01)
+    dop = torch.randn_like(qp)
+    ms = timeit(lambda: fa.fmha_bwd_varlen(qp, kp, vp, out, lse, dop, cu, cu, max(lens), max(lens), bias_slope=-0.01))
+    fb = 2.0 * hh * (3 * 128 + 2 * 128) * visible_pairs("block_diagonal", n, 0, 0, docs)
+    log(workload="bwd_bf16_varlen_documents", N=n, B=bsz, H=hh, D=128, sequences=len(lens), ms=round(ms, 4),
+        tflops=round(fb / ms / 1e9, 1), frac=round(fb / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+    del q, k, v, qp, kp, vp, out, lse, dop
     # backward workloads (causal, B=1 H=16), incl. the MLA-shaped head Dqk=192 Dv=128
     for n, dqk, dv in ((4096, 64, 64), (4096, 128, 128), (16384, 64, 64), (8192, 192, 128)):
         q = torch.randn(1, n, 16, dqk, device=dev).bfloat16()
