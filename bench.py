@@ -366,7 +366,7 @@ def main():
                          "(counter calibration), and exit without the JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+        sys.stderr.write("bench.py measures one GPU only: the library has no multi-GPU path "
                          "(heads or key ranges would be sharded across GPUs; not built). Use --gpus 1.\n")
         sys.exit(2)
 

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   FMHA_OK = 0,
   FMHA_ERR_INVALID_ARG = -1,   /* null pointer, bad shape/stride/size, inconsistent lists */
-  FMHA_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement, or not gfx950 */
+  FMHA_ERR_UNSUPPORTED = -2,   /* valid request the library does not implement, or not gfx950 */
   FMHA_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
   FMHA_ERR_WORKSPACE = -4      /* workspace missing or smaller than the *_workspace_size */
 } fmha_status;
