@@ -174,6 +174,7 @@ AttnParams attn_params(const fmha_fwd_args* a) {
   p.mask = mask_params(a->mask);
   // longest-first query-tile order pays off when tiles carry different key counts
   p.longest_first = (a->mask.kind == FMHA_MASK_CAUSAL || a->mask.kind == FMHA_MASK_PREFIX_LM) ? 1 : 0;
+  p.group = a->kv_heads > 0 ? a->H / a->kv_heads : 1;
   return p;
 }
 
@@ -237,7 +238,6 @@ const char* fmha_status_string(int status) {
 int fmha_fwd(const fmha_fwd_args* a, void* stream) {
   int rc = validate_fwd(a);
   if (rc != FMHA_OK) return rc;
-  if (!multi_head(a)) return FMHA_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->H * a->Nq == 0) return FMHA_OK;
   if (a->block_sparse) {
     if (a->dtype != FMHA_BF16) return FMHA_ERR_UNSUPPORTED;
@@ -263,7 +263,7 @@ int fmha_fwd_varlen(const fmha_fwd_args* a, const fmha_varlen* vl, void* stream)
   int rc = validate_fwd(a);
   if (rc != FMHA_OK) return rc;
   if (vl->reserved != 0 || vl->total_q < 0 || !vl->cu_seqlens_q || !vl->cu_seqlens_k) return FMHA_ERR_INVALID_ARG;
-  if (a->dtype != FMHA_BF16 || !multi_head(a) || a->block_sparse != nullptr || a->mask.kind == FMHA_MASK_BLOCK_DIAGONAL)
+  if (a->dtype != FMHA_BF16 || a->block_sparse != nullptr || a->mask.kind == FMHA_MASK_BLOCK_DIAGONAL)
     return FMHA_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->H * a->Nq == 0 || vl->total_q == 0) return FMHA_OK;
   rc = check_device();

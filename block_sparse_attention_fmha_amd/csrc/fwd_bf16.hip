@@ -119,8 +119,8 @@ void fwd_bf16_kernel(const AttnParams p) {
   const int delta = Nk - Nq;
 
   const __bf16* Qg = (const __bf16*)p.q + q_off + h * p.qs_h;
-  const __bf16* Kg = (const __bf16*)p.k + k_off + h * p.ks_h;
-  const __bf16* Vg = (const __bf16*)p.v + v_off + h * p.vs_h;
+  const __bf16* Kg = (const __bf16*)p.k + k_off + kv_head(p, h) * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + v_off + kv_head(p, h) * p.vs_h;
 
   // ---- tile sequence
   TileSeq<kBN> seq;

@@ -71,8 +71,8 @@ void fwd_f32_kernel(const AttnParams p) {
   const int dsl = w * DW;
 
   const float* Qg = (const float*)p.q + b * p.qs_b + h * p.qs_h;
-  const float* Kg = (const float*)p.k + b * p.ks_b + h * p.ks_h + dsl + 4 * g;
-  const float* Vg = (const float*)p.v + b * p.vs_b + h * p.vs_h + dsl;
+  const float* Kg = (const float*)p.k + b * p.ks_b + kv_head(p, h) * p.ks_h + dsl + 4 * g;
+  const float* Vg = (const float*)p.v + b * p.vs_b + kv_head(p, h) * p.vs_h + dsl;
   char* vslice = smem + w * SM::VSLICE;
   float* red = (float*)(smem + NW * SM::VSLICE);
 

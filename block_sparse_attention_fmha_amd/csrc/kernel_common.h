@@ -94,7 +94,12 @@ struct AttnParams {
   const int* cu_q;
   const int* cu_k;
   int64_t lse_total;
+  int group;          // query heads per K/V head (0 or 1: one K/V head per query head)
 };
+
+// K/V head read by query head h (grouped-query attention: consecutive groups of
+// p.group query heads share one K/V head)
+__device__ __forceinline__ int kv_head(const AttnParams& p, int h) { return p.group > 1 ? h / p.group : h; }
 
 struct BwdParams {
   AttnParams a;       // q, k, v, o (forward output), lse (forward LSE)

@@ -132,9 +132,9 @@ typedef struct {
                           attention: query head h reads K/V head h / (H / Hkv) (the grouping
                           of the reference call with enable_gqa in "Enable 2CTA for SM100
                           block-sparse backward", section "Testing Testing Testing").
-                          Only fmha_fwd_splitkv accepts Hkv != H; fmha_fwd and fmha_bwd
-                          return FMHA_ERR_UNSUPPORTED for it. Not dividing H, or negative:
-                          FMHA_ERR_INVALID_ARG. */
+                          The forward entry points accept Hkv != H (fmha_fwd, fmha_fwd_varlen,
+                          fmha_fwd_splitkv); the backward ones return FMHA_ERR_UNSUPPORTED
+                          for it. Not dividing H, or negative: FMHA_ERR_INVALID_ARG. */
   const void* q;
   const void* k;
   const void* v;

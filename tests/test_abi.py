@@ -78,7 +78,6 @@ def _args(**kw):
     ({"dtype": 7}, fa.FMHA_ERR_INVALID_ARG),
     ({"kv_heads": -1}, fa.FMHA_ERR_INVALID_ARG),
     ({"kv_heads": 3}, fa.FMHA_ERR_INVALID_ARG),           # does not divide H = 2
-    ({"kv_heads": 1}, fa.FMHA_ERR_UNSUPPORTED),           # grouped heads: split-KV only
     ({"reserved2": 1}, fa.FMHA_ERR_INVALID_ARG),
     ({"Nq": -1}, fa.FMHA_ERR_INVALID_ARG),
     ({"dtype": fa.FMHA_FP32, "Dqk": 1024, "Dv": 1024, "softcap": 30.0}, fa.FMHA_ERR_UNSUPPORTED),
@@ -238,7 +237,7 @@ def test_varlen_argument_checks(lib):
     assert lib.fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(bad), None) == fa.FMHA_ERR_INVALID_ARG
     bad.total_q, bad.reserved = 64, 1
     assert lib.fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(bad), None) == fa.FMHA_ERR_INVALID_ARG
-    for kw in ({"dtype": fa.FMHA_FP32}, {"kv_heads": 1}):
+    for kw in ({"dtype": fa.FMHA_FP32},):
         b = _args(**kw)
         assert lib.fmha_fwd_varlen(ctypes.byref(b), ctypes.byref(vl), None) == fa.FMHA_ERR_UNSUPPORTED
     b = _args()
@@ -261,3 +260,13 @@ def test_varlen_struct_layout(tmp_path):
     subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [fa.CVarlen.total_q.offset, fa.CVarlen.reserved.offset, ctypes.sizeof(fa.CVarlen)]
+
+
+def test_backward_rejects_grouped_heads(lib):
+    a = _args(kv_heads=1)
+    g = fa.CBwdArgs()
+    assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_UNSUPPORTED
+    vl = fa.CVarlen()
+    vl.cu_seqlens_q = vl.cu_seqlens_k = 0x200000
+    vl.total_q = 64
+    assert lib.fmha_bwd_varlen(ctypes.byref(a), ctypes.byref(g), ctypes.byref(vl), None) == fa.FMHA_ERR_UNSUPPORTED
