@@ -286,7 +286,9 @@ size_t fmha_bwd_workspace_size(int32_t B, int32_t H, int32_t Nq) {
 static int bwd_impl(const fmha_fwd_args* a, const fmha_bwd_args* g, const fmha_varlen* vl, void* stream) {
   int rc = validate_fwd(a);
   if (rc != FMHA_OK) return rc;
-  if (!multi_head(a)) return FMHA_ERR_UNSUPPORTED;
+  // grouped K/V heads walk every query head of a group in one dK/dV workgroup, which can
+  // only follow one list row: head-broadcast lists only
+  if (!multi_head(a) && a->block_sparse != nullptr && a->block_sparse->heads != 1) return FMHA_ERR_UNSUPPORTED;
   if (g == nullptr) return FMHA_ERR_INVALID_ARG;
   if (vl != nullptr) {
     if (vl->reserved != 0 || vl->total_q < 0 || !vl->cu_seqlens_q || !vl->cu_seqlens_k) return FMHA_ERR_INVALID_ARG;

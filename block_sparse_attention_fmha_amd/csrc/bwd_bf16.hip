@@ -125,9 +125,15 @@ void bwd_dkdv_kernel(const BwdParams bp) {
 
   const int bid = xcd_remap(blockIdx.x, bp.grid_padded_kv);
   if (bid >= bp.total_work_kv) return;
-  const int bh = bid / bp.n_kv_tiles;
-  const int kt = bid - bh * bp.n_kv_tiles;   // ascending: under causal masks the first key
-  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;   // tiles see the most queries
+  // work item: (batch b, K/V head hk, key tile kt); with grouped K/V heads the group's
+  // query heads h0 .. h0 + G - 1 are walked one after the other (a fixed order: the dK / dV
+  // sums stay deterministic)
+  const int G = p.group > 1 ? p.group : 1;
+  const int Hkv = p.H / G;
+  const int bhk = bid / bp.n_kv_tiles;
+  const int kt = bid - bhk * bp.n_kv_tiles;   // ascending: under causal masks the first key
+  const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;   // tiles see the most queries
+  const int h0 = hk * G;
   const int k0 = kt * kKB;
 
   const int tid = threadIdx.x;
@@ -141,11 +147,11 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   const int kw = k0 + 32 * pair;
   const int key = kw + lq;
 
-  const __bf16* Qg = (const __bf16*)p.q + row_base(sq, true, b, p.qs_b, p.qs_s) + h * p.qs_h;
-  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + h * p.ks_h;
-  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + h * p.vs_h;
-  const __bf16* DOg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h * bp.dos_h;
-  const char* WSg = (const char*)(bp.ws + (int64_t)bh * bp.n_qblk * 128);
+  const __bf16* Qg = (const __bf16*)p.q + row_base(sq, true, b, p.qs_b, p.qs_s) + h0 * p.qs_h;
+  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + hk * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + hk * p.vs_h;
+  const __bf16* DOg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h0 * bp.dos_h;
+  const char* WSg = (const char*)(bp.ws + ((int64_t)b * p.H + h0) * bp.n_qblk * 128);
 
   // ---- query-step sequence
   TileSeq<kQS> seq;
@@ -162,7 +168,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     seq.count = max(0, (hi + kQS - 1) / kQS - seq.t_lo);
   } else {
     const ListParams& L = p.lists;   // transposed lists: rows = key tiles
-    const int64_t row = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h)) * L.n_rows + k0 / L.tile_rows;
+    // (grouped K/V heads take head-broadcast lists only, so h0 stands for every head)
+    const int64_t row = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h0)) * L.n_rows + k0 / L.tile_rows;
     seq.count = build_tile_sequence<kThreads, kQS>(L, row, -1, Nq, smem + SM::BYTES, tid);
   }
 
@@ -210,15 +217,27 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   constexpr int ld_wave = 7;   // a wave with the fewest tile blocks issues the lse2 / D load
   const int per_step = qdma.count() + odma.count() + (w == ld_wave ? 1 : 0);
   zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // defensive: every slot is loaded before it is read
+  // step t walks query step tq of group head gi (t = gi * Tq + tq)
+  const int Tq = seq.count;
+  auto head_step = [&](int t, int& gi) {
+    if (G == 1) {
+      gi = 0;
+      return t;
+    }
+    gi = t / Tq;
+    return t - gi * Tq;
+  };
   auto issue_step = [&](int t) {
-    const int i0 = seq.start(t, LISTS);
+    int gi;
+    const int i0 = seq.start(head_step(t, gi), LISTS);
     char* st = smem + (t % SM::NST) * SM::STAGE;
-    qdma.issue(Qg, p.qs_s, i0, Nq, st);
-    odma.issue(DOg, bp.dos_s, i0, Nq, st + SM::QB);
-    if (w == ld_wave) dma_16b(WSg, (uint32_t)(i0 / 64) * 512u + 16u * l, st + SM::QB + SM::OB);
+    qdma.issue(Qg + (int64_t)gi * p.qs_h, p.qs_s, i0, Nq, st);
+    odma.issue(DOg + (int64_t)gi * bp.dos_h, bp.dos_s, i0, Nq, st + SM::QB);
+    if (w == ld_wave)
+      dma_16b(WSg + (int64_t)gi * bp.n_qblk * 512, (uint32_t)(i0 / 64) * 512u + 16u * l, st + SM::QB + SM::OB);
   };
 
-  const int T = seq.count;
+  const int T = G * Tq;
   for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_step(t);
   wait_all_vmem();
   __syncthreads();
@@ -251,10 +270,12 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   // P wave: P_ts = exp2(s * scale_log2 - lse2) (score transform and element mask applied),
   // register r of block kb holding query i0 + 32 kb + 16 (r / 8) + 8 g + r % 8
   auto p_vector = [&](int ts) {
-    const int i0 = seq.start(ts, LISTS);
+    int gi;
+    const int tq = head_step(ts, gi);
+    const int i0 = seq.start(tq, LISTS);
     const float* LD = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB);
     bool need;
-    if constexpr (LISTS) need = seq.cls(ts, 0, true) != 2u;
+    if constexpr (LISTS) need = seq.cls(tq, 0, true) != 2u;
     else need = i0 < need_below || i0 > need_above;
     auto body = [&](auto test_c) {
       constexpr int TEST = decltype(test_c)::value;
@@ -355,8 +376,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   // each role's own path, so registers only one role uses are not kept live by the other.
   auto store = [&](bool isk) {
     if (key >= Nk) return;
-    __bf16* dst = isk ? (__bf16*)bp.dk + row_base(sq, false, b, bp.dks_b, bp.dks_s) + h * bp.dks_h + (int64_t)key * bp.dks_s
-                      : (__bf16*)bp.dv + row_base(sq, false, b, bp.dvs_b, bp.dvs_s) + h * bp.dvs_h + (int64_t)key * bp.dvs_s;
+    __bf16* dst = isk ? (__bf16*)bp.dk + row_base(sq, false, b, bp.dks_b, bp.dks_s) + hk * bp.dks_h + (int64_t)key * bp.dks_s
+                      : (__bf16*)bp.dv + row_base(sq, false, b, bp.dvs_b, bp.dvs_s) + hk * bp.dvs_h + (int64_t)key * bp.dvs_s;
     const float sc = isk ? p.scale : 1.0f;
     const int dw = isk ? DQK : DV;
 #pragma unroll
@@ -461,8 +482,8 @@ void bwd_dq_kernel(const BwdParams bp) {
   const int qrow = qw + lq;
 
   const __bf16* Qg = (const __bf16*)p.q + row_base(sq, true, b, p.qs_b, p.qs_s) + h * p.qs_h;
-  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + h * p.ks_h;
-  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + h * p.vs_h;
+  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + kv_head(p, h) * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + kv_head(p, h) * p.vs_h;
   const __bf16* DOg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h * bp.dos_h;
 
   // ---- key-tile sequence (same bands / lists as the forward)
@@ -774,7 +795,7 @@ hipError_t launch_bwd_bf16(BwdParams bp, int dqk, int dv, hipStream_t st) {
   p.total_work = p.B * p.H * p.n_tiles;
   p.grid_padded = (p.total_work + 7) / 8 * 8;
   bp.n_kv_tiles = (p.Nk + kKB - 1) / kKB;
-  bp.total_work_kv = p.B * p.H * bp.n_kv_tiles;
+  bp.total_work_kv = p.B * (p.H / (p.group > 1 ? p.group : 1)) * bp.n_kv_tiles;   // per K/V head
   bp.grid_padded_kv = (bp.total_work_kv + 7) / 8 * 8;
   bp.n_qblk = (p.Nq + 63) / 64;
 

@@ -208,13 +208,24 @@ def backward_bh(q, k, v, do, b, h, *, scale, softcap=0.0, bias_slope=0.0,
 
 def backward(q, k, v, do, *, scale=None, softcap=0.0, bias_slope=0.0,
              mask: MaskSpec = MaskSpec(), lists=None, heads=None):
-    """Full backward: returns dQ, dK, dV (BSHD, fp64), O and LSE of the oracle forward.
+    """Full backward: returns dQ, dK, dV (BSHD, fp64), O and LSE of the oracle forward;
+    K / V may have fewer heads than Q (see kv_head).
     ``heads`` restricts the computation (other heads are NaN)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, nq, H, dqk = q.shape
     nk, dv_ = k.shape[1], v.shape[3]
-    if k.shape[2] != H or v.shape[2] != H:
-        raise ValueError("the backward oracle covers multi-head attention only (Hkv = H)")
+    hkv = k.shape[2]
+    if hkv != H:
+        # grouped K/V heads (see kv_head): the forward is the multi-head forward on K/V
+        # repeated H / Hkv times along the head axis, so a shared head's gradient is the
+        # sum of its copies' gradients
+        kv_head(0, H, hkv)   # validates the grouping
+        G = H // hkv
+        dq, dkr, dvr, o, lse = backward(q, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2), do, scale=scale,
+                                        softcap=softcap, bias_slope=bias_slope, mask=mask, lists=lists,
+                                        heads=heads)
+        return (dq, dkr.reshape(B, nk, hkv, G, dqk).sum(axis=3), dvr.reshape(B, nk, hkv, G, dv_).sum(axis=3),
+                o, lse)
     scale = default_scale(dqk) if scale is None else scale
     heads = range(H) if heads is None else heads
     dq = np.full(q.shape, np.nan)

@@ -262,11 +262,11 @@ def test_varlen_struct_layout(tmp_path):
     assert got == [fa.CVarlen.total_q.offset, fa.CVarlen.reserved.offset, ctypes.sizeof(fa.CVarlen)]
 
 
-def test_backward_rejects_grouped_heads(lib):
+def test_backward_rejects_grouped_heads_with_per_head_lists(lib):
+    # grouped K/V heads walk a whole group in one dK/dV workgroup: head-broadcast lists only
     a = _args(kv_heads=1)
+    bs = fa.CBlockSparse()
+    bs.tile_m, bs.tile_n, bs.n_q_tiles, bs.n_kv_tiles, bs.heads = 128, 128, 1, 1, 2
+    a.block_sparse = ctypes.pointer(bs)
     g = fa.CBwdArgs()
     assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_UNSUPPORTED
-    vl = fa.CVarlen()
-    vl.cu_seqlens_q = vl.cu_seqlens_k = 0x200000
-    vl.total_q = 64
-    assert lib.fmha_bwd_varlen(ctypes.byref(a), ctypes.byref(g), ctypes.byref(vl), None) == fa.FMHA_ERR_UNSUPPORTED

@@ -52,3 +52,28 @@ def test_gqa_split_partials_combine_to_the_forward():
     for splits in (1, 3, 5):
         o, lse = oracle.combine_partials(oracle.split_partials(q, k, v, splits, 64))
         assert np.allclose(o, o_ref, atol=1e-12) and np.allclose(lse, lse_ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["none", "causal"])
+def test_gqa_backward_matches_finite_differences(kind):
+    # central differences of the grouped-head forward (fp64) for dQ, dK and dV
+    rng = np.random.default_rng(21)
+    B, Nq, Nk, H, Hkv, D = 1, 3, 4, 4, 2, 2
+    q, k, v, do = (rng.standard_normal(s) for s in ((B, Nq, H, D), (B, Nk, Hkv, D), (B, Nk, Hkv, D), (B, Nq, H, D)))
+    m = oracle.MaskSpec(kind)
+    dq, dk, dv, _, _ = oracle.backward(q, k, v, do, mask=m, bias_slope=0.1)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.forward(q_, k_, v_, mask=m, bias_slope=0.1)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.abs(num - grad).max() <= 1e-6 * max(1.0, np.abs(num).max())
