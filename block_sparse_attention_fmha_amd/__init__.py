@@ -337,8 +337,8 @@ def fmha_fwd_splitkv(q, k, v, num_splits: int, *, scale=None, mask: Mask | None 
 def fmha_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
                     scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | None = None, out=None, lse=None,
                     stream=None):
-    """Forward over packed variable-length sequences. q [total_q, H, Dqk], k [total_k, H, Dqk],
-    v [total_k, H, Dv] (bf16); cu_seqlens_q / cu_seqlens_k: contiguous int32 device tensors
+    """Forward over packed variable-length sequences. q [total_q, H, Dqk], k [total_k, Hkv, Dqk],
+    v [total_k, Hkv, Dv] (bf16; Hkv divides H); cu_seqlens_q / cu_seqlens_k: contiguous int32 device tensors
     [B + 1] of ascending row offsets starting at 0; max_seqlen_q / max_seqlen_k bound every
     sequence's length (the offsets are not read on the host). Returns (out [total_q, H, Dv],
     lse [H, total_q] fp32)."""
