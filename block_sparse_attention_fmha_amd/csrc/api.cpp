@@ -293,12 +293,14 @@ static int bwd_impl(const fmha_fwd_args* a, const fmha_bwd_args* g, const fmha_v
   if (vl != nullptr) {
     if (vl->reserved != 0 || vl->total_q < 0 || !vl->cu_seqlens_q || !vl->cu_seqlens_k) return FMHA_ERR_INVALID_ARG;
     if (a->block_sparse != nullptr || a->mask.kind == FMHA_MASK_BLOCK_DIAGONAL) return FMHA_ERR_UNSUPPORTED;
-    if (vl->total_q == 0) return FMHA_OK;
   }
   if (a->dtype != FMHA_BF16) return FMHA_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->H * a->Nq == 0 && (int64_t)a->B * a->H * a->Nk == 0) return FMHA_OK;
-  if (a->Nq == 0 || a->Nk == 0) return FMHA_ERR_UNSUPPORTED;  // empty side: nothing sensible to launch
-  if (!g->dout || !g->dq || !g->dk || !g->dv || !a->k || !a->v) return FMHA_ERR_INVALID_ARG;
+  // one side may be empty: no keys gives dQ = 0, no queries dK = dV = 0 (the kernels of
+  // the other side see no steps and store zeros); only the non-empty side's buffers are used
+  const bool has_q = a->Nq > 0, has_k = a->Nk > 0;
+  if ((has_q && (!g->dout || !g->dq)) || (has_k && (!g->dk || !g->dv || !a->k || !a->v)))
+    return FMHA_ERR_INVALID_ARG;
   if (!aligned16(g->dout) || !aligned16(g->dq) || !aligned16(g->dk) || !aligned16(g->dv))
     return FMHA_ERR_INVALID_ARG;
   if (!strides_ok(g->do_stride, 2) || !strides_ok(g->dq_stride, 2) || !strides_ok(g->dk_stride, 2) ||

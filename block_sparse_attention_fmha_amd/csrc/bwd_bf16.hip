@@ -734,9 +734,11 @@ hipError_t launch_passes(const BwdParams& bp, hipStream_t st) {
     const int bytes = DkdvSmem<DQK, DV>::BYTES + list_bytes(kv.a.lists, kQS);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(bp.grid_padded_kv), dim3(kThreads), bytes, st, kv);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (bp.grid_padded_kv > 0) {   // no keys: no dK / dV to write
+      hipLaunchKernelGGL(kern, dim3(bp.grid_padded_kv), dim3(kThreads), bytes, st, kv);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   {
     auto kern = bwd_dq_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
@@ -745,9 +747,11 @@ hipError_t launch_passes(const BwdParams& bp, hipStream_t st) {
     if (e != hipSuccess) return e;
     e = record_stage(bp, 2, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(bp.a.grid_padded), dim3(kThreads), bytes, st, bp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (bp.a.grid_padded > 0) {   // no queries: no dQ to write
+      hipLaunchKernelGGL(kern, dim3(bp.a.grid_padded), dim3(kThreads), bytes, st, bp);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     return record_stage(bp, 3, st);
   }
 }
@@ -806,9 +810,10 @@ hipError_t launch_bwd_bf16(BwdParams bp, int dqk, int dv, hipStream_t st) {
     const int64_t rows = (int64_t)p.B * p.H * bp.n_qblk * 64;
     const int rows_per_blk = kPreThreads / lpk;
     const unsigned nblk = (unsigned)((rows + rows_per_blk - 1) / rows_per_blk);
-    if (dv == 128) hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(nblk), dim3(kPreThreads), 0, st, bp);
-    else if (dv == 64) hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(nblk), dim3(kPreThreads), 0, st, bp);
-    else return hipErrorInvalidValue;
+    if (dv != 128 && dv != 64) return hipErrorInvalidValue;
+    if (nblk == 0) {}   // no queries: nothing to preprocess
+    else if (dv == 128) hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(nblk), dim3(kPreThreads), 0, st, bp);
+    else hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(nblk), dim3(kPreThreads), 0, st, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

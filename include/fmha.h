@@ -132,9 +132,10 @@ typedef struct {
                           attention: query head h reads K/V head h / (H / Hkv) (the grouping
                           of the reference call with enable_gqa in "Enable 2CTA for SM100
                           block-sparse backward", section "Testing Testing Testing").
-                          The forward entry points accept Hkv != H (fmha_fwd, fmha_fwd_varlen,
-                          fmha_fwd_splitkv); the backward ones return FMHA_ERR_UNSUPPORTED
-                          for it. Not dividing H, or negative: FMHA_ERR_INVALID_ARG. */
+                          Every entry point accepts Hkv != H; the backward then sums each
+                          group's query heads into dK / dV in a fixed order, and takes
+                          block-sparse lists only with heads == 1 (FMHA_ERR_UNSUPPORTED
+                          otherwise). Not dividing H, or negative: FMHA_ERR_INVALID_ARG. */
   const void* q;
   const void* k;
   const void* v;
@@ -180,7 +181,9 @@ int fmha_fwd(const fmha_fwd_args* args, void* stream);
 /* Backward from the saved LSE: reads args->q, k, v, o, lse and bwd->dout; writes dQ,
  * dK, dV. bf16 only. Deterministic: no atomics; every gradient element has a single
  * writer and a fixed summation order, so repeated calls give bitwise-identical
- * results. With block-sparse lists the transposed lists drive the dK/dV pass. */
+ * results. With block-sparse lists the transposed lists drive the dK/dV pass.
+ * One empty side is allowed: Nk == 0 writes dQ = 0, Nq == 0 writes dK = dV = 0 (the
+ * empty side's pointers may then be NULL). */
 size_t fmha_bwd_workspace_size(int32_t B, int32_t H, int32_t Nq);
 int fmha_bwd(const fmha_fwd_args* args, const fmha_bwd_args* bwd, void* stream);
 
@@ -223,7 +226,9 @@ int fmha_fwd_varlen(const fmha_fwd_args* args, const fmha_varlen* varlen, void* 
 /* Backward over packed variable-length sequences: as fmha_bwd, with the sequences, masks
  * and LSE layout of fmha_fwd_varlen (dO, dQ, dK, dV are packed like O, Q, K, V). The
  * workspace is fmha_bwd_workspace_size(B, H, args->Nq) with args->Nq the longest query
- * sequence. Block-diagonal masks and block-sparse lists: FMHA_ERR_UNSUPPORTED. */
+ * sequence. Keys of a sequence without queries get dK = dV = 0, queries of a sequence
+ * without keys dQ = 0 (also when total_q is 0). Block-diagonal masks and block-sparse
+ * lists: FMHA_ERR_UNSUPPORTED. */
 int fmha_bwd_varlen(const fmha_fwd_args* args, const fmha_bwd_args* bwd, const fmha_varlen* varlen,
                     void* stream);
 

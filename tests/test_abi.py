@@ -270,3 +270,19 @@ def test_backward_rejects_grouped_heads_with_per_head_lists(lib):
     a.block_sparse = ctypes.pointer(bs)
     g = fa.CBwdArgs()
     assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_UNSUPPORTED
+
+
+def test_backward_one_empty_side_checks_only_that_sides_buffers(lib):
+    # Nk = 0: dQ (written as 0) and dO must be given, K / V / dK / dV may be NULL;
+    # Nq = 0: dK / dV (written as 0) must be given. Both rejections precede any device use.
+    fake = 0x100000
+    a = _args(Nk=0, k=None, v=None)
+    g = fa.CBwdArgs()
+    g.dout = fake
+    assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_INVALID_ARG   # no dQ
+    a = _args(Nq=0, q=None, o=None, lse=None)
+    g = fa.CBwdArgs()
+    g.dk = fake
+    assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_INVALID_ARG   # no dV
+    a = _args(Nq=0, Nk=0)
+    assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(fa.CBwdArgs()), None) == fa.FMHA_OK   # nothing to write

@@ -81,6 +81,31 @@ def test_bwd_block_sparse_full_size(kind):
           lists=(128, 128))
 
 
+@pytest.mark.parametrize("kind", ["none", "causal"])
+def test_bwd_one_empty_side(kind):
+    # no keys: every query's output is 0 and so is dQ; no queries: dK = dV = 0. The
+    # gradient buffers start as NaN, so every element must be written.
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    dev = torch.device("cuda:0")
+    gm = fa.Mask(kind)
+    q, k, v, do = (to_dev(x) for x in synth.attention_inputs(synth.case_seed(4, 90), 2, 300, 300, 3, 128, 128,
+                                                               "bf16", with_dout=True))
+    none = torch.empty(2, 0, 3, 128, device=dev, dtype=torch.bfloat16)
+    announce(f"bwd Nk=0 B=2 Nq=300 H=3 D=128 mask={kind}")
+    out, lse = fa.fmha_fwd(q, none, none, mask=gm)
+    dq = torch.full_like(q, float("nan"))
+    dq, dk, dv = fa.fmha_bwd(q, none, none, out, lse, do, mask=gm, dq=dq)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
+    lse0 = torch.empty(2, 3, 0, device=dev, dtype=torch.float32)
+    announce(f"bwd Nq=0 B=2 Nk=300 H=3 D=128 mask={kind}")
+    dk, dv = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    dq, dk, dv = fa.fmha_bwd(none, k, v, none, lse0, none, mask=gm, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+
+
 def test_bwd_deterministic():
     import torch
     q, k, v, do = synth.attention_inputs(synth.case_seed(9, 400), 1, 1024, 1024, 4, 128, 128, "bf16",

@@ -72,3 +72,23 @@ def test_varlen_documents_of_the_block_sparse_workload():
 def test_varlen_backward(case):
     lq, lk, H, dqk, dv, kind, w, p, cap, slope = CASES[case]
     _run(synth.case_seed(9, 900 + case), lq, lk, H, dqk, dv, kind, w, p, cap, slope, backward=True)
+
+
+def test_varlen_backward_without_queries():
+    # total_q = 0 while the sequences hold keys: every dK / dV row is 0 (the buffers start
+    # as NaN, so each must be written)
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    dev = torch.device("cuda:0")
+    _, k, v = synth.attention_inputs(synth.case_seed(9, 899), 1, 1, 300, 2, 128, 128, "bf16")
+    tk, tv = (x.to_torch(dev)[0] for x in (k, v))
+    none = torch.empty(0, 2, 128, device=dev, dtype=torch.bfloat16)
+    cu_q = torch.tensor([0, 0, 0], dtype=torch.int32, device=dev)
+    cu_k = torch.tensor([0, 100, 300], dtype=torch.int32, device=dev)
+    lse = torch.empty(2, 0, device=dev, dtype=torch.float32)
+    dk, dv = torch.full_like(tk, float("nan")), torch.full_like(tv, float("nan"))
+    announce("varlen bwd total_q=0 total_k=300 H=2 D=128 causal")
+    dq, dk, dv = fa.fmha_bwd_varlen(none, tk, tv, none, lse, none, cu_q, cu_k, 0, 200, mask=fa.Mask("causal"),
+                                    dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
