@@ -306,6 +306,180 @@ void splitkv_grouped_kernel(const SplitParams sp) {
   }
 }
 
+// Large groups on the matrix cores. When one K/V head serves G >= 8 query heads, the
+// G x Nq query rows of a (batch, K/V head) are a 32-row matrix, so the scores of a
+// 32-key block are one product S^T = K Q^T (K rows in the permuted order of the bf16
+// forward: each lane's accumulator then holds 8 consecutive keys of its row per 16-key
+// group, which is the B operand of O^T += V^T P^T as is) and V^T comes from transposed
+// LDS reads of the block staged in a wave-private region. Each K/V row is read from
+// memory once per workgroup for the whole group. One workgroup per (batch, K/V head,
+// split); its 4 waves take the split's 32-key blocks round robin, each with its own
+// online softmax per row (lanes l and l ^ 32 hold the two halves of a row's 32 keys), and
+// are merged at the end through LDS. Rows past G x Nq carry zero queries and are not
+// stored. The partials use the layout of the other partial kernels.
+constexpr int kMfmaBlock = 32;    // keys per block and wave
+constexpr int kVRowBytes = 320;   // staged V row pitch: the transposed reads of 4 rows hit disjoint banks
+constexpr int kVStage = kMfmaBlock * kVRowBytes;       // 10 KiB per wave
+constexpr int kMergeO = kMfmaBlock * 128 * 4;           // one wave's O^T, fp32: 16 KiB
+
+__global__ __launch_bounds__(kThreads, 1)
+void splitkv_mfma_kernel(const SplitParams sp) {
+  constexpr int D = 128;
+  const AttnParams& p = sp.a;
+  // V staging during the key walk; afterwards the O^T of waves 1-3 for the merge
+  __shared__ __attribute__((aligned(16))) char lds[3 * kMergeO];
+  __shared__ float stats[4][2][kMfmaBlock];
+  static_assert(4 * kVStage <= 3 * kMergeO, "V staging fits the merge buffer");
+
+  const int G = sp.group;
+  const int Hkv = p.H / G;
+  const int s = blockIdx.x % sp.splits;
+  const int bk = blockIdx.x / sp.splits;
+  const int b = bk / Hkv, hk = bk - (bk / Hkv) * Hkv;
+  const int h0 = hk * G;
+  const int R = G * p.Nq;                       // rows in use (<= 32, checked on the host)
+  const int k_lo = min(p.Nk, s * sp.per_split);
+  const int k_hi = min(p.Nk, k_lo + sp.per_split);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 5, lq = l & 31;
+
+  // B operand Q^T: lane row lq = (query head h0 + lq / Nq, query lq % Nq)
+  const int gi = lq / p.Nq, qi = lq - (lq / p.Nq) * p.Nq;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = (lq < R) ? *(const bf16x8*)((const __bf16*)p.q + b * p.qs_b + (h0 + gi) * p.qs_h +
+                                         (int64_t)qi * p.qs_s + 16 * ks + 8 * g)
+                      : bf16x8{};
+
+  const __bf16* Kg = (const __bf16*)p.k + b * p.ks_b + hk * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + b * p.vs_b + hk * p.vs_h;
+  const int prow = swap_bits23(lq);
+  const int trow = 8 * g + ((l & 15) >> 2);
+  const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  char* vst = lds + w * kVStage;
+  const bool masked = p.mask.kind != kMaskNone;
+
+  float m_run = kNegInf, l_run = 0.0f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+
+  // this wave's blocks start at k_lo + 32 (w + 4 i); rows past k_hi read row k_hi - 1
+  // (in bounds, masked out)
+  bf16x8 ka[D / 16];
+  u32x4 vr[8];
+  auto load = [&](int blk) {
+    const int kr = min(blk + prow, k_hi - 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) ka[ks] = *(const bf16x8*)(Kg + (int64_t)kr * p.ks_s + 16 * ks + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int vrow = min(blk + (l >> 4) + 4 * i, k_hi - 1);
+      vr[i] = *(const u32x4*)(Vg + (int64_t)vrow * p.vs_s + 8 * (l & 15));
+    }
+  };
+  int blk = k_lo + kMfmaBlock * w;
+  if (blk < k_hi) load(blk);
+  for (; blk < k_hi; blk += 4 * kMfmaBlock) {
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sc, 0, 0, 0);
+    // stage V rows (l >> 4) + 4 i; the previous block's transposed reads were issued
+    // before these writes by the same wave, and LDS operations of a wave run in order
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(u32x4*)(vst + ((l >> 4) + 4 * i) * kVRowBytes + 16 * (l & 15)) = vr[i];
+    const int next = blk + 4 * kMfmaBlock;
+    if (next < k_hi) load(next);   // in flight during the softmax and P V of this block
+    // reg r holds key blk + 16 (r / 8) + 8 g + r % 8 of row lq
+    float x[16];
+    float mt = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = blk + 16 * (r >> 3) + 8 * g + (r & 7);
+      bool vis = key < k_hi;
+      if (masked && vis) vis = mask_visible(p.mask, b, qi, key, p.Nq, p.Nk);
+      x[r] = vis ? sc[r] * p.scale_log2 : kNegInf;
+      mt = fmaxf(mt, x[r]);
+    }
+    const float mn = fmaxf(m_run, pair_max(mt));
+    const float mu = (mn == kNegInf) ? 0.0f : mn;
+    const float alpha = fast_exp2(m_run - mu);
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+    m_run = mn;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(x[8 * hh + 2 * e] - mu), p1 = fast_exp2(x[8 * hh + 2 * e + 1] - mu);
+        l_run += p0 + p1;
+        pk[e] = pack_bf16x2(p0, p1);
+      }
+      pb[hh] = __builtin_bit_cast(bf16x8, pk);
+    }
+    // O^T += V^T P^T: A = V^T (32 head-dim rows x 16 keys) from transposed reads
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const char* tp = vst + (trow + 16 * hh) * kVRowBytes + tcol * 2 + 64 * db;
+        const bf16x8 va = join_bf16x8(lds_read_tr(tp), lds_read_tr(tp + 4 * kVRowBytes));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hh], o[db], 0, 0, 0);
+      }
+  }
+  l_run = pair_sum(l_run);
+
+  // merge the 4 waves: waves 1-3 leave (m, l) and O^T in LDS, wave 0 combines and stores;
+  // lane (lq, g) holds O^T[d][lq] for d = 32 db + 8 (r / 4) + 4 g + r % 4
+  __syncthreads();   // every wave is done with its V staging region
+  if (g == 0) {
+    stats[w][0][lq] = m_run;
+    stats[w][1][lq] = l_run;
+  }
+  if (w > 0) {
+    float* ob = (float*)(lds + (w - 1) * kMergeO) + lq * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(f32x4*)(ob + 32 * db + 8 * q4 + 4 * g) = f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (w != 0 || lq >= R) return;
+  float mx = m_run;
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) mx = fmaxf(mx, stats[ww][0][lq]);
+  const float mu = (mx == kNegInf) ? 0.0f : mx;
+  float c[4];
+  c[0] = fast_exp2(m_run - mu);
+  float tot = l_run * c[0];
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) {
+    c[ww] = fast_exp2(stats[ww][0][lq] - mu);
+    tot += stats[ww][1][lq] * c[ww];
+  }
+  const bool empty = !(tot > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / tot;
+  const int64_t row = ((int64_t)(b * p.H + h0 + gi) * sp.splits + s) * p.Nq + qi;
+  float* po = sp.part_o + row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * g;
+      f32x4 acc = f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]} * c[0];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) acc += *(const f32x4*)((const float*)(lds + (ww - 1) * kMergeO) + lq * D + d) * c[ww];
+      *(f32x4*)(po + d) = acc * inv;
+    }
+  if (g == 0) sp.part_lse[row] = empty ? kNegInf : (mx + fast_log2(tot)) * kLn2;
+}
+
 // One workgroup of D threads per (b, h, query row): LSE-weighted merge of the partials.
 template <int D>
 __global__ __launch_bounds__(D)
@@ -357,9 +531,14 @@ hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* 
   const unsigned nblk = (unsigned)(p.B * (p.H / gc) * p.Nq * splits);
   const unsigned nrow = (unsigned)(p.B * p.H * p.Nq);
   if (d != 64 && d != 128) return hipErrorInvalidValue;
+  // a group of 8 or more query heads whose rows fit one 32-row product: matrix cores
+  const bool mfma = d == 128 && group >= 8 && group * p.Nq <= kMfmaBlock;
   auto partial = [&](auto d_c) {
     constexpr int DD = decltype(d_c)::value;
-    if (gc == 4) hipLaunchKernelGGL((splitkv_grouped_kernel<DD, 4>), dim3(nblk), dim3(kThreads), 0, st, sp);
+    if (DD == 128 && mfma)
+      hipLaunchKernelGGL(splitkv_mfma_kernel, dim3((unsigned)(p.B * (p.H / group) * splits)), dim3(kThreads), 0,
+                         st, sp);
+    else if (gc == 4) hipLaunchKernelGGL((splitkv_grouped_kernel<DD, 4>), dim3(nblk), dim3(kThreads), 0, st, sp);
     else if (gc == 2) hipLaunchKernelGGL((splitkv_grouped_kernel<DD, 2>), dim3(nblk), dim3(kThreads), 0, st, sp);
     else hipLaunchKernelGGL(splitkv_partial_kernel<DD>, dim3(nblk), dim3(kThreads), 0, st, sp);
     hipError_t e = hipGetLastError();

@@ -94,18 +94,18 @@ def test_splitkv_grouped_heads_full_size(Hkv, splits):
         check_bf16(f"LSE[{b},{h}]", l[b, h], l_ref)
 
 
-@pytest.mark.parametrize("Hkv", [4, 2, 1])
+@pytest.mark.parametrize("Hkv", [8, 2, 1])
 def test_splitkv_no_keys(Hkv):
     # an empty K / V cache: every split is empty, so O = 0 and LSE = -inf (the combine of
     # empty partials); output buffers start as NaN
     import torch
     import block_sparse_attention_fmha_amd as fa
     dev = torch.device("cuda:0")
-    q = synth.attention_inputs(synth.case_seed(9, 990 + Hkv), 2, 1, 1, 4, 128, 128, "bf16")[0]
+    q = synth.attention_inputs(synth.case_seed(9, 990 + Hkv), 2, 1, 1, 8, 128, 128, "bf16")[0]
     none = torch.empty(2, 0, Hkv, 128, device=dev, dtype=torch.bfloat16)
-    out = torch.full((2, 1, 4, 128), float("nan"), device=dev, dtype=torch.bfloat16)
-    lse = torch.full((2, 4, 1), float("nan"), device=dev, dtype=torch.float32)
-    announce(f"splitkv Nk=0 B=2 H=4 Hkv={Hkv} splits=8")
+    out = torch.full((2, 1, 8, 128), float("nan"), device=dev, dtype=torch.bfloat16)
+    lse = torch.full((2, 8, 1), float("nan"), device=dev, dtype=torch.float32)
+    announce(f"splitkv Nk=0 B=2 H=8 Hkv={Hkv} splits=8")
     out, lse = fa.fmha_fwd_splitkv(to_dev(q), none, none, 8, out=out, lse=lse)
     torch.cuda.synchronize()
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
