@@ -6,8 +6,8 @@
 // bound. The split partials are merged with the two-chunk online-softmax rule of the
 // POPCORNBENCH transcript "Kimi-K2.6 l1 p97" (running max, rescaled sums and outputs).
 //
-// On CDNA4 this path is HBM-bound (every K/V byte is used for one query row), so it
-// does not use MFMA: with one query there is no matrix to multiply. Each workgroup
+// With one query row per K/V head this path is HBM-bound (every K/V byte is used for one
+// query row), so it does not use MFMA: there is no matrix to multiply. Each workgroup
 // (one query row of one (batch, head), one split) streams its key range once:
 //   * D/8 lanes cooperate on one key (16 bytes of the K row each), so a wavefront reads
 //     64/(D/8) whole, contiguous K rows per load instruction (fully coalesced);
@@ -24,7 +24,10 @@
 // are packed bf16 dot products (v_dot2: the product of two bf16 values is exact in
 // fp32) on the bf16 Q and K, and the V slice is converted to fp32 once for the GC heads,
 // so the group's K/V bytes cross HBM once and the per-(head, key) VALU work drops. An odd
-// group size runs the one-head kernel with the head mapping.
+// group size runs the one-head kernel with the head mapping. Groups of 8 or more query
+// heads whose G x Nq rows fit 32 run on the matrix cores instead (splitkv_mfma_kernel):
+// there the rows do form a matrix, and the VALU kernels' per-(head, key) work would
+// dominate.
 // The combine kernel then computes LSE = ln sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s per row (empty splits carry LSE_s = -inf).
 #include "kernel_common.h"
