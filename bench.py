@@ -145,7 +145,7 @@ def gpu_step_timing(steps: int, warmup: int):
 def profile_other_rows(reps: int):
     """For rocprofv3 runs: `reps` launches each of the split-KV decode (B=8 H=32 Nq=1
     Nk=32768 D=128, 16 splits; partial + combine kernels), the same with 8 grouped K/V
-    heads, the fp32 wide-head forward
+    heads and with one (multi-query), the fp32 wide-head forward
     (B=4 H=8 N=512 D=1024) and the block-sparse causal forward (B=2 H=8 N=8192 D=128,
     128 x 128 tiles, relative bias) with its block-mask build."""
     import torch
@@ -160,6 +160,12 @@ def profile_other_rows(reps: int):
     del k, v
     k = torch.randn(8, 32768, 8, 128, device=dev).bfloat16()   # 8 K/V heads for the 32 query heads
     v = torch.randn(8, 32768, 8, 128, device=dev).bfloat16()
+    for _ in range(reps):
+        fa.fmha_fwd_splitkv(q, k, v, 16)
+    torch.cuda.synchronize()
+    del k, v
+    k = torch.randn(8, 32768, 1, 128, device=dev).bfloat16()   # one K/V head (multi-query)
+    v = torch.randn(8, 32768, 1, 128, device=dev).bfloat16()
     for _ in range(reps):
         fa.fmha_fwd_splitkv(q, k, v, 16)
     torch.cuda.synchronize()
