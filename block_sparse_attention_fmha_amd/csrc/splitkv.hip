@@ -24,7 +24,7 @@
 // are packed bf16 dot products (v_dot2: the product of two bf16 values is exact in
 // fp32) on the bf16 Q and K, and the V slice is converted to fp32 once for the GC heads,
 // so the group's K/V bytes cross HBM once and the per-(head, key) VALU work drops. An odd
-// group size runs the one-head kernel with the head mapping. Groups of 8 or more query
+// group size runs the one-head kernel with the head mapping. Groups of 4 or more query
 // heads whose G x Nq rows fit 32 run on the matrix cores instead (splitkv_mfma_kernel):
 // there the rows do form a matrix, and the VALU kernels' per-(head, key) work would
 // dominate.
@@ -309,7 +309,7 @@ void splitkv_grouped_kernel(const SplitParams sp) {
   }
 }
 
-// Large groups on the matrix cores. When one K/V head serves G >= 8 query heads, the
+// Groups on the matrix cores. When one K/V head serves G >= 4 query heads, the
 // G x Nq query rows of a (batch, K/V head) are a 32-row matrix, so the scores of a
 // 32-key block are one product S^T = K Q^T (K rows in the permuted order of the bf16
 // forward: each lane's accumulator then holds 8 consecutive keys of its row per 16-key
@@ -534,8 +534,11 @@ hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* 
   const unsigned nblk = (unsigned)(p.B * (p.H / gc) * p.Nq * splits);
   const unsigned nrow = (unsigned)(p.B * p.H * p.Nq);
   if (d != 64 && d != 128) return hipErrorInvalidValue;
-  // a group of 8 or more query heads whose rows fit one 32-row product: matrix cores
-  const bool mfma = d == 128 && group >= 8 && group * p.Nq <= kMfmaBlock;
+  // a group whose rows fit one 32-row product runs on the matrix cores when it has 8 or
+  // more query heads, or 4-7 with at least 1024 keys per split (measured at B=8 H=32
+  // Nk=32768: G = 4 is equal or faster down to 1024 keys per split, slower at 512; G = 1
+  // is slower)
+  const bool mfma = d == 128 && group * p.Nq <= kMfmaBlock && (group >= 8 || (group >= 4 && sp.per_split >= 1024));
   auto partial = [&](auto d_c) {
     constexpr int DD = decltype(d_c)::value;
     if (DD == 128 && mfma)

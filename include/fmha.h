@@ -193,7 +193,8 @@ int fmha_bwd(const fmha_fwd_args* args, const fmha_bwd_args* bwd, void* stream);
  * combine kernel merges them: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
  * bf16 only, no block-sparse lists, 1 <= num_splits <= 64. Accepts grouped K/V heads
  * (args->kv_heads): the query heads of one group (up to 4 per workgroup, or the whole group
- * as the rows of one matrix product when it has 8 or more heads and heads x Nq <= 32)
+ * as the rows of one matrix product when heads x Nq <= 32 and it has 8 or more heads, or
+ * 4-7 with at least 1024 keys per split)
  * stream each K/V row of the group once from memory. The workspace is sized by query heads H. */
 size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t Dv,
                                        int32_t num_splits);
