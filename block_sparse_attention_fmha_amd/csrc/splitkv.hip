@@ -321,13 +321,20 @@ void splitkv_grouped_kernel(const SplitParams sp) {
 // are merged at the end through LDS. Rows past G x Nq carry zero queries and are not
 // stored. The partials use the layout of the other partial kernels.
 constexpr int kMfmaBlock = 32;    // keys per block and wave
-constexpr int kVRowBytes = 320;   // staged V row pitch: the transposed reads of 4 rows hit disjoint banks
-constexpr int kVStage = kMfmaBlock * kVRowBytes;       // 10 KiB per wave
-constexpr int kMergeO = kMfmaBlock * 128 * 4;           // one wave's O^T, fp32: 16 KiB
 
+// Staged V row pitch in bytes: the transposed reads of 4 rows then hit disjoint banks
+// (an odd multiple of 64 bytes modulo 256, as in the bf16 forward).
+template <int D> struct DecodeVPitch { static constexpr int value = (D == 64) ? 192 : 320; };
+
+template <int D>
 __global__ __launch_bounds__(kThreads, 1)
 void splitkv_mfma_kernel(const SplitParams sp) {
-  constexpr int D = 128;
+  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  constexpr int kVRowBytes = DecodeVPitch<D>::value;
+  constexpr int kVStage = kMfmaBlock * kVRowBytes;      // per wave
+  constexpr int kMergeO = kMfmaBlock * D * 4;           // one wave's O^T, fp32
+  constexpr int CH = D / 8;                             // 16-byte chunks per V row
+  constexpr int NV = kMfmaBlock * CH / 64;              // V loads per lane and block
   const AttnParams& p = sp.a;
   // V staging during the key walk; afterwards the O^T of waves 1-3 for the merge
   __shared__ __attribute__((aligned(16))) char lds[3 * kMergeO];
@@ -372,15 +379,15 @@ void splitkv_mfma_kernel(const SplitParams sp) {
   // this wave's blocks start at k_lo + 32 (w + 4 i); rows past k_hi read row k_hi - 1
   // (in bounds, masked out)
   bf16x8 ka[D / 16];
-  u32x4 vr[8];
+  u32x4 vr[NV];   // lane l: V rows l / CH + (64 / CH) i, 16-byte chunk l % CH
   auto load = [&](int blk) {
     const int kr = min(blk + prow, k_hi - 1);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) ka[ks] = *(const bf16x8*)(Kg + (int64_t)kr * p.ks_s + 16 * ks + 8 * g);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int vrow = min(blk + (l >> 4) + 4 * i, k_hi - 1);
-      vr[i] = *(const u32x4*)(Vg + (int64_t)vrow * p.vs_s + 8 * (l & 15));
+    for (int i = 0; i < NV; ++i) {
+      const int vrow = min(blk + l / CH + (64 / CH) * i, k_hi - 1);
+      vr[i] = *(const u32x4*)(Vg + (int64_t)vrow * p.vs_s + 8 * (l % CH));
     }
   };
   int blk = k_lo + kMfmaBlock * w;
@@ -389,10 +396,10 @@ void splitkv_mfma_kernel(const SplitParams sp) {
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sc, 0, 0, 0);
-    // stage V rows (l >> 4) + 4 i; the previous block's transposed reads were issued
-    // before these writes by the same wave, and LDS operations of a wave run in order
+    // stage the block's V rows; the previous block's transposed reads were issued before
+    // these writes by the same wave, and LDS operations of a wave run in order
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4*)(vst + ((l >> 4) + 4 * i) * kVRowBytes + 16 * (l & 15)) = vr[i];
+    for (int i = 0; i < NV; ++i) *(u32x4*)(vst + (l / CH + (64 / CH) * i) * kVRowBytes + 16 * (l % CH)) = vr[i];
     const int next = blk + 4 * kMfmaBlock;
     if (next < k_hi) load(next);   // in flight during the softmax and P V of this block
     // reg r holds key blk + 16 (r / 8) + 8 g + r % 8 of row lq
@@ -538,12 +545,12 @@ hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* 
   // more query heads, or 4-7 with at least 1024 keys per split (measured at B=8 H=32
   // Nk=32768: G = 4 is equal or faster down to 1024 keys per split, slower at 512; G = 1
   // is slower)
-  const bool mfma = d == 128 && group * p.Nq <= kMfmaBlock && (group >= 8 || (group >= 4 && sp.per_split >= 1024));
+  const bool mfma = group * p.Nq <= kMfmaBlock && (group >= 8 || (group >= 4 && sp.per_split >= 1024));
   auto partial = [&](auto d_c) {
     constexpr int DD = decltype(d_c)::value;
-    if (DD == 128 && mfma)
-      hipLaunchKernelGGL(splitkv_mfma_kernel, dim3((unsigned)(p.B * (p.H / group) * splits)), dim3(kThreads), 0,
-                         st, sp);
+    if (mfma)
+      hipLaunchKernelGGL(splitkv_mfma_kernel<DD>, dim3((unsigned)(p.B * (p.H / group) * splits)), dim3(kThreads),
+                         0, st, sp);
     else if (gc == 4) hipLaunchKernelGGL((splitkv_grouped_kernel<DD, 4>), dim3(nblk), dim3(kThreads), 0, st, sp);
     else if (gc == 2) hipLaunchKernelGGL((splitkv_grouped_kernel<DD, 2>), dim3(nblk), dim3(kThreads), 0, st, sp);
     else hipLaunchKernelGGL(splitkv_partial_kernel<DD>, dim3(nblk), dim3(kThreads), 0, st, sp);

@@ -109,3 +109,18 @@ def test_splitkv_no_keys(Hkv):
     out, lse = fa.fmha_fwd_splitkv(to_dev(q), none, none, 8, out=out, lse=lse)
     torch.cuda.synchronize()
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("H,Hkv,nq,kind,splits", [(16, 2, 1, "none", 4), (16, 1, 2, "sliding_window", 3),
+                                                  (8, 2, 1, "causal", 2), (8, 2, 3, "none", 1)])
+def test_splitkv_grouped_heads_d64(H, Hkv, nq, kind, splits):
+    # head dim 64 with groups of 4 (>= 1024 keys per split), 8 and 16 query heads per K/V
+    # head: the matrix-core decode path at D = 64, against the oracle element-wise
+    seed = synth.case_seed(9, 900 + 10 * H + Hkv + nq)
+    q, k, v = _gqa_inputs(seed, 2, nq, 5000, H, Hkv, 64)
+    om, gm = mask_pair(kind, 2, nq, 5000, window=700)
+    announce(f"splitkv grouped heads D=64 seed={seed} H={H} Hkv={Hkv} Nq={nq} Nk=5000 mask={kind} splits={splits}")
+    out, lse = run_split(to_dev(q), to_dev(k), to_dev(v), splits, gm)
+    o_ref, l_ref = oracle.forward(q.values, k.values, v.values, mask=om)
+    check_bf16("O", host(out), o_ref)
+    check_bf16("LSE", host(lse), l_ref)
