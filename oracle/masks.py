@@ -67,21 +67,36 @@ def allowed(mask: MaskSpec, b: int, qidx, kidx, nq: int, nk: int) -> np.ndarray:
     raise AssertionError(mask.kind)
 
 
-def block_sparse_allowed(lists, mask: MaskSpec, b: int, h: int, qidx, kidx,
-                         nq: int, nk: int) -> np.ndarray:
-    """Element visibility under block-sparse index lists (forward lists of ``lists``):
-    full tiles are visible everywhere, partial tiles apply ``mask``, others are skipped."""
-    hm = h if lists.partial_cnt.shape[1] > 1 else 0
-    qt = np.asarray(qidx, dtype=np.int64) // lists.tile_m
-    kt = np.asarray(kidx, dtype=np.int64) // lists.tile_n
+def tile_sets(lists, b: int, hm: int):
+    """The listed tiles of mask head ``hm`` as two boolean [nQt, nKt] sets (full,
+    partial). Each row holds ``cnt`` entries (a count below 0 reads as 0, above the
+    row length as the whole row); an entry is a key-tile index, and an index outside
+    [0, nKt) names no tile, so it adds nothing. Membership is set membership: an entry
+    given twice is one entry."""
     n_qt, n_kt = lists.partial_idx.shape[2], lists.partial_idx.shape[3]
     is_full = np.zeros((n_qt, n_kt), dtype=bool)
     is_part = np.zeros((n_qt, n_kt), dtype=bool)
-    for r in range(n_qt):
-        for c in lists.full_idx[b, hm, r, : lists.full_cnt[b, hm, r]]:
-            is_full[r, c] = True
-        for c in lists.partial_idx[b, hm, r, : lists.partial_cnt[b, hm, r]]:
-            is_part[r, c] = True
+    for dst, cnt, idx in ((is_full, lists.full_cnt, lists.full_idx),
+                          (is_part, lists.partial_cnt, lists.partial_idx)):
+        for r in range(n_qt):
+            c = min(max(int(cnt[b, hm, r]), 0), n_kt)
+            for t in idx[b, hm, r, :c]:
+                if 0 <= t < n_kt:
+                    dst[r, t] = True
+    return is_full, is_part
+
+
+def block_sparse_allowed(lists, mask: MaskSpec, b: int, h: int, qidx, kidx,
+                         nq: int, nk: int) -> np.ndarray:
+    """Element visibility under block-sparse index lists (forward lists of ``lists``):
+    full tiles are visible everywhere, partial tiles apply ``mask``, others are skipped.
+    A tile listed both as full and as partial is full (its full listing makes every
+    element visible; the partial listing only adds elements the mask allows). Lists
+    with one mask head serve every attention head; otherwise head h reads mask head h."""
+    hm = h if lists.partial_cnt.shape[1] > 1 else 0
+    qt = np.asarray(qidx, dtype=np.int64) // lists.tile_m
+    kt = np.asarray(kidx, dtype=np.int64) // lists.tile_n
+    is_full, is_part = tile_sets(lists, b, hm)
     full = is_full[qt[:, None], kt[None, :]]
     part = is_part[qt[:, None], kt[None, :]]
     return full | (part & allowed(mask, b, qidx, kidx, nq, nk))
