@@ -94,8 +94,11 @@ bool supported_dims(int dtype, int dqk, int dv) {
   return false;
 }
 
-// Shape / pointer / stride / option checks shared by every entry point.
-int validate_fwd(const fmha_fwd_args* a) {
+// Shape / pointer / stride / option checks shared by every entry point. Q / O / LSE are
+// checked whenever there are queries; K / V whenever there are keys and something reads
+// them: the forward only with queries, the backward (kv_read_alone) also without, since its
+// dK / dV pass then still runs over the keys and writes zeros.
+int validate_fwd(const fmha_fwd_args* a, bool kv_read_alone = false) {
   if (a == nullptr) return FMHA_ERR_INVALID_ARG;
   if (a->B < 0 || a->H < 0 || a->Nq < 0 || a->Nk < 0) return FMHA_ERR_INVALID_ARG;
   if (a->reserved2 != 0) return FMHA_ERR_INVALID_ARG;
@@ -109,20 +112,23 @@ int validate_fwd(const fmha_fwd_args* a) {
   if (rc != FMHA_OK) return rc;
   if (a->dtype == FMHA_FP32 && (a->softcap != 0.0f || a->bias_slope != 0.0f || a->block_sparse != nullptr))
     return FMHA_ERR_UNSUPPORTED;
-  const int64_t work = (int64_t)a->B * a->H * ceil_div(a->Nq, 32);
+  const int64_t work = (int64_t)a->B * a->H * ceil_div(a->Nq > a->Nk ? a->Nq : a->Nk, 32);
   if (work > (int64_t)1 << 30) return FMHA_ERR_UNSUPPORTED;
-  if ((int64_t)a->B * a->H * a->Nq == 0) return FMHA_OK;  // nothing to compute
-  if (!a->q || !a->o || !a->lse) return FMHA_ERR_INVALID_ARG;
-  if (a->Nk > 0 && (!a->k || !a->v)) return FMHA_ERR_INVALID_ARG;
+  const bool has_q = (int64_t)a->B * a->H * a->Nq > 0;
+  const bool has_k = (int64_t)a->B * a->H * a->Nk > 0 && (has_q || kv_read_alone);
   const int es = a->dtype == FMHA_BF16 ? 2 : 4;
-  if (!aligned16(a->q) || !aligned16(a->o) || (a->Nk > 0 && (!aligned16(a->k) || !aligned16(a->v))))
-    return FMHA_ERR_INVALID_ARG;
-  if (!strides_ok(a->q_stride, es) || !strides_ok(a->k_stride, es) || !strides_ok(a->v_stride, es) ||
-      !strides_ok(a->o_stride, es))
-    return FMHA_ERR_INVALID_ARG;
-  if (!seq_stride_fits(a->q_stride, es) || !seq_stride_fits(a->k_stride, es) || !seq_stride_fits(a->v_stride, es) ||
-      !seq_stride_fits(a->o_stride, es))
-    return FMHA_ERR_UNSUPPORTED;
+  if (has_q) {
+    if (!a->q || !a->o || !a->lse) return FMHA_ERR_INVALID_ARG;
+    if (!aligned16(a->q) || !aligned16(a->o)) return FMHA_ERR_INVALID_ARG;
+    if (!strides_ok(a->q_stride, es) || !strides_ok(a->o_stride, es)) return FMHA_ERR_INVALID_ARG;
+    if (!seq_stride_fits(a->q_stride, es) || !seq_stride_fits(a->o_stride, es)) return FMHA_ERR_UNSUPPORTED;
+  }
+  if (has_k) {
+    if (!a->k || !a->v) return FMHA_ERR_INVALID_ARG;
+    if (!aligned16(a->k) || !aligned16(a->v)) return FMHA_ERR_INVALID_ARG;
+    if (!strides_ok(a->k_stride, es) || !strides_ok(a->v_stride, es)) return FMHA_ERR_INVALID_ARG;
+    if (!seq_stride_fits(a->k_stride, es) || !seq_stride_fits(a->v_stride, es)) return FMHA_ERR_UNSUPPORTED;
+  }
   return FMHA_OK;
 }
 
@@ -284,7 +290,7 @@ size_t fmha_bwd_workspace_size(int32_t B, int32_t H, int32_t Nq) {
 
 // fmha_bwd and fmha_bwd_varlen (vl != nullptr: packed variable-length sequences)
 static int bwd_impl(const fmha_fwd_args* a, const fmha_bwd_args* g, const fmha_varlen* vl, void* stream) {
-  int rc = validate_fwd(a);
+  int rc = validate_fwd(a, true);
   if (rc != FMHA_OK) return rc;
   // grouped K/V heads walk every query head of a group in one dK/dV workgroup, which can
   // only follow one list row: head-broadcast lists only

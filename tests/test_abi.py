@@ -286,3 +286,25 @@ def test_backward_one_empty_side_checks_only_that_sides_buffers(lib):
     assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_INVALID_ARG   # no dV
     a = _args(Nq=0, Nk=0)
     assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(fa.CBwdArgs()), None) == fa.FMHA_OK   # nothing to write
+
+
+@pytest.mark.parametrize("bad", ["neg_stride", "odd_stride", "misaligned_k", "null_v"])
+def test_backward_without_queries_still_validates_keys(lib, bad):
+    # Nq = 0, Nk > 0: the dK / dV pass still reads K and V (and writes zeros), so their
+    # pointers and strides are checked before anything is launched
+    fake = 0x100000
+    a = _args(Nq=0, q=None, o=None, lse=None)
+    if bad == "neg_stride":
+        a.k_stride[1] = -2 * 128
+    elif bad == "odd_stride":
+        a.v_stride[1] = 2 * 128 + 2
+    elif bad == "misaligned_k":
+        a.k = fake + 8
+    else:
+        a.v = None
+    g = fa.CBwdArgs()
+    g.dk = g.dv = fake
+    for s in (g.do_stride, g.dq_stride, g.dk_stride, g.dv_stride):
+        s[0], s[1], s[2] = 64 * 2 * 128, 2 * 128, 128
+    g.workspace, g.workspace_bytes = 0x200000, lib.fmha_bwd_workspace_size(1, 2, 0)
+    assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_INVALID_ARG
