@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(HERE, "libfmha.so")
 FMHA_OK, FMHA_ERR_INVALID_ARG, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP, FMHA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 FMHA_BF16, FMHA_FP32 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding_window": 2, "block_diagonal": 3, "prefix_lm": 4}
+ABI_VERSION = 3   # the struct layouts below (fmha_abi_version of include/fmha.h)
 ENTRY_POINTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_splitkv",
                 "fmha_fwd_splitkv_workspace_size", "fmha_fwd_varlen", "fmha_bwd_varlen", "build_block_mask",
                 "fmha_status_string", "fmha_abi_version")
@@ -72,7 +73,8 @@ class CFwdArgs(ctypes.Structure):
 
 class CVarlen(ctypes.Structure):
     _fields_ = [("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
-                ("total_q", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("total_q", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("seqused_q", ctypes.c_void_p), ("seqused_k", ctypes.c_void_p)]
 
 
 class CBwdArgs(ctypes.Structure):
@@ -124,6 +126,9 @@ def load_library():
     lib.fmha_status_string.restype = ctypes.c_char_p
     lib.fmha_abi_version.argtypes = []
     lib.fmha_abi_version.restype = ctypes.c_int
+    if lib.fmha_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.fmha_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild it with `python -m block_sparse_attention_fmha_amd.build`")
     _LIB = lib
     return lib
 
@@ -334,14 +339,33 @@ def fmha_fwd_splitkv(q, k, v, num_splits: int, *, scale=None, mask: Mask | None 
     return out, lse
 
 
+def _varlen(cu_seqlens_q, cu_seqlens_k, total_q, seqused_q, seqused_k):
+    """The fmha_varlen descriptor (offsets and used lengths stay on the device)."""
+    B = cu_seqlens_q.numel() - 1
+    for t, n in ((seqused_q, "seqused_q"), (seqused_k, "seqused_k")):
+        if t is None:
+            continue
+        _need_device(t, n)
+        if str(t.dtype) != "torch.int32" or not t.is_contiguous() or t.dim() != 1 or t.numel() != B:
+            raise ValueError(f"{n} must be a contiguous int32 [B] device tensor")
+    vl = CVarlen()
+    vl.cu_seqlens_q, vl.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    vl.total_q, vl.reserved = total_q, 0
+    vl.seqused_q = None if seqused_q is None else seqused_q.data_ptr()
+    vl.seqused_k = None if seqused_k is None else seqused_k.data_ptr()
+    return vl
+
+
 def fmha_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
                     scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | None = None, out=None, lse=None,
-                    stream=None):
+                    seqused_q=None, seqused_k=None, stream=None):
     """Forward over packed variable-length sequences. q [total_q, H, Dqk], k [total_k, Hkv, Dqk],
     v [total_k, Hkv, Dv] (bf16; Hkv divides H); cu_seqlens_q / cu_seqlens_k: contiguous int32 device tensors
     [B + 1] of ascending row offsets starting at 0; max_seqlen_q / max_seqlen_k bound every
-    sequence's length (the offsets are not read on the host). Returns (out [total_q, H, Dv],
-    lse [H, total_q] fp32)."""
+    sequence's length (the offsets are not read on the host). seqused_q / seqused_k: optional
+    contiguous int32 device tensors [B]; only the first seqused[b] rows of each sequence take
+    part and rows past them are left as they were in ``out`` / ``lse``. Returns
+    (out [total_q, H, Dv], lse [H, total_q] fp32)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
         _need_device(t, n)
@@ -365,18 +389,17 @@ def fmha_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
                          lse.view(1, H, total_q), scale, softcap, bias_slope, mask, None)
     a.B = cu_seqlens_q.numel() - 1
     a.Nq, a.Nk = int(max_seqlen_q), int(max_seqlen_k)
-    vl = CVarlen()
-    vl.cu_seqlens_q, vl.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
-    vl.total_q, vl.reserved = total_q, 0
+    vl = _varlen(cu_seqlens_q, cu_seqlens_k, total_q, seqused_q, seqused_k)
     _check(load_library().fmha_fwd_varlen(ctypes.byref(a), ctypes.byref(vl), _stream(stream)), "fmha_fwd_varlen")
     return out, lse
 
 
 def fmha_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
                     scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | None = None, dq=None, dk=None,
-                    dv=None, workspace=None, stream=None):
-    """Backward over packed variable-length sequences (layouts of fmha_fwd_varlen): returns
-    (dq [total_q, H, Dqk], dk, dv [total_k, H, D]) in bf16."""
+                    dv=None, workspace=None, seqused_q=None, seqused_k=None, stream=None):
+    """Backward over packed variable-length sequences (layouts and seqused of
+    fmha_fwd_varlen): returns (dq [total_q, H, Dqk], dk, dv [total_k, H, D]) in bf16; rows past
+    a sequence's used length keep what the given dq / dk / dv held."""
     import torch
     lib = load_library()
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or out.dim() != 3 or dout.dim() != 3:
@@ -410,9 +433,7 @@ def fmha_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seq
     g.do_stride, g.dq_stride, g.dk_stride, g.dv_stride = (_strides(t.unsqueeze(0)) for t in (dout, dq, dk, dv))
     g.workspace = workspace.data_ptr()
     g.workspace_bytes = workspace.numel() * workspace.element_size()
-    vl = CVarlen()
-    vl.cu_seqlens_q, vl.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
-    vl.total_q, vl.reserved = total_q, 0
+    vl = _varlen(cu_seqlens_q, cu_seqlens_k, total_q, seqused_q, seqused_k)
     _check(lib.fmha_bwd_varlen(ctypes.byref(a), ctypes.byref(g), ctypes.byref(vl), _stream(stream)),
            "fmha_bwd_varlen")
     return dq, dk, dv

@@ -228,7 +228,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 extern "C" {
 
-int fmha_abi_version(void) { return 2; }
+int fmha_abi_version(void) { return 3; }
 
 const char* fmha_status_string(int status) {
   switch (status) {
@@ -277,6 +277,8 @@ int fmha_fwd_varlen(const fmha_fwd_args* a, const fmha_varlen* vl, void* stream)
   AttnParams p = attn_params(a);
   p.cu_q = vl->cu_seqlens_q;
   p.cu_k = vl->cu_seqlens_k;
+  p.used_q = vl->seqused_q;
+  p.used_k = vl->seqused_k;
   p.lse_total = vl->total_q;
   FMHA_LOG("fwd varlen bf16 B=%d H=%d maxNq=%d maxNk=%d total_q=%d Dqk=%d Dv=%d mask=%d", a->B, a->H, a->Nq, a->Nk,
            vl->total_q, a->Dqk, a->Dv, a->mask.kind);
@@ -340,6 +342,8 @@ static int bwd_impl(const fmha_fwd_args* a, const fmha_bwd_args* g, const fmha_v
   if (vl != nullptr) {
     bp.a.cu_q = vl->cu_seqlens_q;
     bp.a.cu_k = vl->cu_seqlens_k;
+    bp.a.used_q = vl->seqused_q;
+    bp.a.used_k = vl->seqused_k;
     bp.a.lse_total = vl->total_q;
   }
   FMHA_LOG("bwd bf16 B=%d H=%d Nq=%d Nk=%d Dqk=%d Dv=%d mask=%d lists=%d varlen=%d", a->B, a->H, a->Nq, a->Nk,

@@ -102,20 +102,13 @@ void fwd_bf16_kernel(const AttnParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so per-wave tests branch on scalars
   const int l = tid & 63, g = l >> 5, lq = l & 31;
   // sequence b: its lengths, the offsets of its first query / key row and of its LSE row
-  int Nq = p.Nq, Nk = p.Nk;
-  int64_t q_off = b * p.qs_b, k_off = b * p.ks_b, v_off = b * p.vs_b, o_off = b * p.os_b;
-  int64_t lse_off = ((int64_t)b * p.H + h) * Nq;
-  if (p.cu_q != nullptr) {   // packed variable-length sequences (the grid covers the longest)
-    const int qs = p.cu_q[b], ks = p.cu_k[b];
-    Nq = p.cu_q[b + 1] - qs;
-    Nk = p.cu_k[b + 1] - ks;
-    if (q0 >= Nq) return;    // whole workgroup, before any barrier
-    q_off = (int64_t)qs * p.qs_s;
-    k_off = (int64_t)ks * p.ks_s;
-    v_off = (int64_t)ks * p.vs_s;
-    o_off = (int64_t)qs * p.os_s;
-    lse_off = (int64_t)h * p.lse_total + qs;
-  }
+  // (packed variable-length sequences: the grid covers the longest)
+  const SeqInfo sq = seq_info(p, b);
+  const int Nq = sq.nq, Nk = sq.nk;
+  if (q0 >= Nq) return;      // whole workgroup, before any barrier
+  const int64_t q_off = row_base(sq, true, b, p.qs_b, p.qs_s), o_off = row_base(sq, true, b, p.os_b, p.os_s);
+  const int64_t k_off = row_base(sq, false, b, p.ks_b, p.ks_s), v_off = row_base(sq, false, b, p.vs_b, p.vs_s);
+  const int64_t lse_off = lse_base(p, sq, b, h);
   const int delta = Nk - Nq;
 
   const __bf16* Qg = (const __bf16*)p.q + q_off + h * p.qs_h;

@@ -93,6 +93,10 @@ struct AttnParams {
   // sequence axis (the batch strides are unused); LSE is [H, lse_total]
   const int* cu_q;
   const int* cu_k;
+  // optional used lengths [B] (nullptr = the whole span): only the first used_q[b] queries
+  // and used_k[b] keys of sequence b take part; rows past them are neither read nor written
+  const int* used_q;
+  const int* used_k;
   int64_t lse_total;
   int group;          // query heads per K/V head (0 or 1: one K/V head per query head)
 };
@@ -127,6 +131,7 @@ struct SeqInfo {
   int nq, nk, qs, ks;
   bool packed;
 };
+// A used length outside [0, span] is clamped to it (the lengths are read on the device only).
 __device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int b) {
   SeqInfo s{p.Nq, p.Nk, 0, 0, false};
   if (p.cu_q != nullptr) {
@@ -134,6 +139,8 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int b) {
     s.ks = p.cu_k[b];
     s.nq = p.cu_q[b + 1] - s.qs;
     s.nk = p.cu_k[b + 1] - s.ks;
+    if (p.used_q != nullptr) s.nq = min(max(p.used_q[b], 0), s.nq);
+    if (p.used_k != nullptr) s.nk = min(max(p.used_k[b], 0), s.nk);
     s.packed = true;
   }
   return s;

@@ -202,20 +202,30 @@ int fmha_fwd_splitkv(const fmha_fwd_args* args, int32_t num_splits, void* worksp
                      size_t workspace_bytes, void* stream);
 
 /* Packed variable-length sequences ("Enable 2CTA for SM100 block-sparse backward",
- * section "Testing Testing Testing": the forward's cu_seqlens_q / cu_seqlens_k and
- * seqused arguments). Sequence b (0 <= b < args->B) owns query rows
- * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b], cu_seqlens_k[b+1])
- * of Q [total_q, H, Dqk], K / V [total_k, H, D*] and O [total_q, H, Dv], addressed with
- * the seq and head strides of fmha_fwd_args (its batch strides are ignored). The offset
- * arrays are device int32 [B + 1], ascending, starting at 0; they are read on the device
- * only, so the caller guarantees that every query length is <= args->Nq, every key length
- * <= args->Nk, and every row lies inside the tensors. Masks apply within each sequence
- * (delta = that sequence's key length minus its query length). LSE is fp32 [H, total_q]. */
+ * section "Testing Testing Testing": the forward call's cu_seqlens_q / cu_seqlens_k and
+ * seqused_q / seqused_k arguments). Sequence b (0 <= b < args->B) owns the span of query
+ * rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b], cu_seqlens_k[b+1])
+ * of Q [total_q, H, Dqk], K / V [total_k, Hkv, D*] and O [total_q, H, Dv], addressed with the
+ * seq and head strides of fmha_fwd_args (its batch strides are ignored). The offset arrays
+ * are device int32 [B + 1], ascending, starting at 0.
+ * seqused_q / seqused_k (device int32 [B], or NULL = the whole span): only the first
+ * seqused_q[b] query rows and seqused_k[b] key rows of each span take part; the sequence is
+ * then the problem of those lengths (masks and positions as below), and rows of a span past
+ * its used length are neither read nor written (their O / LSE / dQ / dK / dV keep whatever
+ * the caller's buffers held). The pages pass these arguments without defining them; this is
+ * the plain reading of "used" lengths. A used length outside [0, span] is clamped to it.
+ * Every array here is read on the device only, so the caller guarantees that every used
+ * query length (the span, or seqused_q[b]) is <= args->Nq, every used key length is
+ * <= args->Nk, and every row lies inside the tensors.
+ * Masks apply within each sequence (delta = that sequence's key length minus its query
+ * length, after seqused). LSE is fp32 [H, total_q]. */
 typedef struct {
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_k;
   int32_t total_q;     /* cu_seqlens_q[B] */
   int32_t reserved;    /* must be 0 */
+  const int32_t* seqused_q;   /* [B] or NULL */
+  const int32_t* seqused_k;   /* [B] or NULL */
 } fmha_varlen;
 
 /* Forward over packed variable-length sequences: as fmha_fwd with args->B sequences of at
@@ -247,7 +257,7 @@ int build_block_mask(const fmha_mask* mask, int32_t B, int32_t Hm, int32_t Nq, i
 const char* fmha_status_string(int status);
 
 /* ABI version: bumped whenever a struct layout changes. */
-int fmha_abi_version(void);   /* 2: kv_heads, fmha_fwd_varlen, fmha_bwd_varlen */
+int fmha_abi_version(void);   /* 3: fmha_varlen.seqused_q / seqused_k (2: kv_heads, varlen entry points) */
 
 #ifdef __cplusplus
 }

@@ -133,13 +133,29 @@ def forward(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: MaskSpec 
     return o, lse
 
 
+def used_rows(cu, seqused, b: int) -> int:
+    """Rows of sequence b that take part: its whole span cu[b]:cu[b+1], or the first
+    seqused[b] of them (the forward's seqused_q / seqused_k arguments of "Enable 2CTA for
+    SM100 block-sparse backward", section "Testing Testing Testing", passed there without a
+    definition; read here as the used prefix of each span)."""
+    span = int(cu[b + 1]) - int(cu[b])
+    if seqused is None:
+        return span
+    u = int(seqused[b])
+    if not 0 <= u <= span:
+        raise ValueError(f"seqused[{b}] = {u} outside [0, {span}]")
+    return u
+
+
 def forward_varlen(q, k, v, cu_q, cu_k, *, scale=None, softcap=0.0, bias_slope=0.0,
-                   mask: MaskSpec = MaskSpec()):
+                   mask: MaskSpec = MaskSpec(), seqused_q=None, seqused_k=None):
     """Packed variable-length sequences (the forward's cu_seqlens arguments of "Enable 2CTA
     for SM100 block-sparse backward", section "Testing Testing Testing"): q [total_q,H,Dqk],
     k [total_k,H,Dqk], v [total_k,H,Dv]; sequence b is query rows cu_q[b]:cu_q[b+1] and key
     rows cu_k[b]:cu_k[b+1], attended as its own batch entry (positions, masks and the
-    relative bias are sequence-local). Returns o [total_q,H,Dv], lse [H,total_q]."""
+    relative bias are sequence-local). With seqused_q / seqused_k only the first rows of
+    each span take part (see used_rows); rows past them are not part of the result and
+    come back as NaN. Returns o [total_q,H,Dv], lse [H,total_q]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     total_q, H, dqk = q.shape
     dv = v.shape[2]
@@ -147,7 +163,10 @@ def forward_varlen(q, k, v, cu_q, cu_k, *, scale=None, softcap=0.0, bias_slope=0
     o = np.zeros((total_q, H, dv))
     lse = np.full((H, total_q), -np.inf)
     for b in range(len(cu_q) - 1):
-        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        qs, ks = int(cu_q[b]), int(cu_k[b])
+        qe, ke = qs + used_rows(cu_q, seqused_q, b), ks + used_rows(cu_k, seqused_k, b)
+        o[qe:int(cu_q[b + 1])] = np.nan
+        lse[:, qe:int(cu_q[b + 1])] = np.nan
         if qe == qs:
             continue
         if ke == ks:   # no keys: every row is fully masked
@@ -160,10 +179,11 @@ def forward_varlen(q, k, v, cu_q, cu_k, *, scale=None, softcap=0.0, bias_slope=0
 
 
 def backward_varlen(q, k, v, do, cu_q, cu_k, *, scale=None, softcap=0.0, bias_slope=0.0,
-                    mask: MaskSpec = MaskSpec()):
+                    mask: MaskSpec = MaskSpec(), seqused_q=None, seqused_k=None):
     """Backward of forward_varlen: each sequence as its own batch entry (the batched
-    backward on its rows). Returns dq [total_q,H,Dqk], dk, dv [total_k,H,D], o, lse
-    [H,total_q]; rows of sequences without keys get zero gradients."""
+    backward on its used rows). Returns dq [total_q,H,Dqk], dk, dv [total_k,H,D], o, lse
+    [H,total_q]; rows of sequences without keys (or queries) get zero gradients, rows past
+    a used length are NaN (not part of the result)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     total_q, H, dqk = q.shape
     scale = default_scale(dqk) if scale is None else scale
@@ -171,7 +191,13 @@ def backward_varlen(q, k, v, do, cu_q, cu_k, *, scale=None, softcap=0.0, bias_sl
     o = np.zeros((total_q, H, v.shape[2]))
     lse = np.full((H, total_q), -np.inf)
     for b in range(len(cu_q) - 1):
-        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        qs, ks = int(cu_q[b]), int(cu_k[b])
+        qe, ke = qs + used_rows(cu_q, seqused_q, b), ks + used_rows(cu_k, seqused_k, b)
+        for arr in (dq, o):
+            arr[qe:int(cu_q[b + 1])] = np.nan
+        lse[:, qe:int(cu_q[b + 1])] = np.nan
+        dk[ke:int(cu_k[b + 1])] = np.nan
+        dv[ke:int(cu_k[b + 1])] = np.nan
         if qe == qs or ke == ks:
             continue
         gq, gk, gv, ob, lb = backward(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke], do[None, qs:qe], scale=scale,

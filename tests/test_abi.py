@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fmha_abi_version() == 2
+    assert lib.fmha_abi_version() == fa.ABI_VERSION == 3
     assert fa.status_string(0) == "FMHA_OK"
     assert fa.status_string(-4) == "FMHA_ERR_WORKSPACE"
     assert fa.status_string(12345) == "FMHA_ERR_UNKNOWN"
@@ -254,12 +254,14 @@ def test_varlen_struct_layout(tmp_path):
         pytest.skip("no host C compiler")
     src = tmp_path / "vl.c"
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fmha.h"\n'
-                   'int main(void) { printf("%zu %zu %zu\\n", offsetof(fmha_varlen, total_q),'
-                   ' offsetof(fmha_varlen, reserved), sizeof(fmha_varlen)); return 0; }\n')
+                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", offsetof(fmha_varlen, total_q),'
+                   ' offsetof(fmha_varlen, reserved), offsetof(fmha_varlen, seqused_q),'
+                   ' offsetof(fmha_varlen, seqused_k), sizeof(fmha_varlen)); return 0; }\n')
     exe = tmp_path / "vl"
     subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    assert got == [fa.CVarlen.total_q.offset, fa.CVarlen.reserved.offset, ctypes.sizeof(fa.CVarlen)]
+    assert got == [fa.CVarlen.total_q.offset, fa.CVarlen.reserved.offset, fa.CVarlen.seqused_q.offset,
+                   fa.CVarlen.seqused_k.offset, ctypes.sizeof(fa.CVarlen)]
 
 
 def test_backward_rejects_grouped_heads_with_per_head_lists(lib):

@@ -92,3 +92,56 @@ def test_varlen_backward_without_queries():
                                     dk=dk, dv=dv)
     torch.cuda.synchronize()
     assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+SEQUSED_CASES = [
+    # (span lengths q, span lengths k, used q, used k, H, Dqk, Dv, mask, window, slope)
+    ([300, 129, 700], [300, 129, 700], [300, 100, 513], [257, 129, 1], 2, 128, 128, "causal", 0, 0.0),
+    ([256, 640, 64], [512, 640, 300], [0, 640, 17], [400, 333, 300], 2, 128, 128, "none", 0, -0.01),
+    ([385, 200], [385, 200], [385, 1], [130, 0], 2, 64, 64, "sliding_window", 70, 0.0),
+    ([255, 385], [385, 255], [200, 385], [385, 128], 2, 192, 128, "prefix_lm", 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SEQUSED_CASES)))
+def test_varlen_seqused(case):
+    # only the used prefix of each span takes part: used rows match the oracle on the
+    # truncated problem, and every row past a used length keeps the NaN it started with
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    lq, lk, uq, uk, H, dqk, dv, kind, w, slope = SEQUSED_CASES[case]
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    seed = synth.case_seed(9, 870 + case)
+    x = synth.attention_inputs(seed, 1, int(cu_q[-1]), int(cu_k[-1]), H, dqk, dv, "bf16", with_dout=True)
+    qv, kv, vv, dov = (t.values[0] for t in x)
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdo = (t.to_torch(dev)[0] for t in x)
+    dt = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)
+    gm, om = fa.Mask(kind, window=w), oracle.MaskSpec(kind, window=w)
+    out = torch.full((int(cu_q[-1]), H, dv), float("nan"), device=dev, dtype=torch.bfloat16)
+    lse = torch.full((H, int(cu_q[-1])), float("nan"), device=dev, dtype=torch.float32)
+    announce(f"varlen seqused fwd+bwd case={case} spans q={lq} k={lk} used q={uq} k={uk} D={dqk}/{dv} mask={kind}")
+    fa.fmha_fwd_varlen(tq, tk, tv, dt(cu_q), dt(cu_k), max(uq), max(uk), mask=gm, bias_slope=slope, out=out,
+                       lse=lse, seqused_q=dt(uq), seqused_k=dt(uk))
+    dq = torch.full_like(tq, float("nan"))
+    dk, dv_ = torch.full_like(tk, float("nan")), torch.full_like(tv, float("nan"))
+    fa.fmha_bwd_varlen(tq, tk, tv, out, lse, tdo, dt(cu_q), dt(cu_k), max(uq), max(uk), mask=gm,
+                       bias_slope=slope, dq=dq, dk=dk, dv=dv_, seqused_q=dt(uq), seqused_k=dt(uk))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.forward_varlen(qv, kv, vv, cu_q, cu_k, mask=om, bias_slope=slope,
+                                         seqused_q=np.array(uq), seqused_k=np.array(uk))
+    g_ref = oracle.backward_varlen(qv, kv, vv, dov, cu_q, cu_k, mask=om, bias_slope=slope,
+                                   seqused_q=np.array(uq), seqused_k=np.array(uk))
+    used_q = ~np.isnan(o_ref[:, 0, 0])
+    used_k = ~np.isnan(g_ref[1][:, 0, 0])
+    o, l = host(out), host(lse)
+    check_bf16("O", o[used_q], o_ref[used_q])
+    check_bf16("LSE", l[:, used_q], l_ref[:, used_q])
+    assert np.all(np.isnan(o[~used_q])) and np.all(np.isnan(l[:, ~used_q])), "rows past seqused_q were written"
+    gq, gk, gv = host(dq), host(dk), host(dv_)
+    check_grad("dQ", gq[used_q], g_ref[0][used_q])
+    check_grad("dK", gk[used_k], g_ref[1][used_k])
+    check_grad("dV", gv[used_k], g_ref[2][used_k])
+    assert np.all(np.isnan(gq[~used_q])), "dQ rows past seqused_q were written"
+    assert np.all(np.isnan(gk[~used_k])) and np.all(np.isnan(gv[~used_k])), "dK / dV rows past seqused_k were written"

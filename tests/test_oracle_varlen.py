@@ -52,3 +52,59 @@ def test_backward_equal_lengths_equal_the_batched_backward(kind):
     for g, r in zip(got[:4], ref[:4]):
         assert np.array_equal(g, r.reshape(g.shape))
     assert np.array_equal(got[4], ref[4].transpose(1, 0, 2).reshape(H, B * Nq))
+
+
+def _packed(rng, lq, lk, H=2, D=4):
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q, k, v, do = (rng.standard_normal((n, H, D)) for n in (cu_q[-1], cu_k[-1], cu_k[-1], cu_q[-1]))
+    return cu_q, cu_k, q, k, v, do
+
+
+@pytest.mark.parametrize("kind", ["causal", "sliding_window", "prefix_lm"])
+def test_seqused_equal_to_the_span_changes_nothing(kind):
+    rng = np.random.default_rng(21)
+    lq, lk = [5, 0, 3, 7], [6, 2, 0, 7]
+    cu_q, cu_k, q, k, v, do = _packed(rng, lq, lk)
+    m = oracle.MaskSpec(kind, window=2, prefix=2)
+    a = oracle.forward_varlen(q, k, v, cu_q, cu_k, mask=m, bias_slope=0.1)
+    b = oracle.forward_varlen(q, k, v, cu_q, cu_k, mask=m, bias_slope=0.1, seqused_q=np.array(lq),
+                              seqused_k=np.array(lk))
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    a = oracle.backward_varlen(q, k, v, do, cu_q, cu_k, mask=m, softcap=1.5)
+    b = oracle.backward_varlen(q, k, v, do, cu_q, cu_k, mask=m, softcap=1.5, seqused_q=np.array(lq),
+                               seqused_k=np.array(lk))
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("kind", ["none", "causal", "sliding_window"])
+def test_seqused_shorter_than_the_span_equals_the_truncated_sequences(kind):
+    # used prefixes of each span vs. a packing that holds only those prefixes: the used rows
+    # must agree exactly and every row past a used length is left out (NaN)
+    rng = np.random.default_rng(22)
+    lq, lk = [6, 4, 5, 3], [7, 5, 4, 3]
+    uq, uk = [4, 0, 5, 2], [7, 3, 0, 1]
+    cu_q, cu_k, q, k, v, do = _packed(rng, lq, lk)
+    m = oracle.MaskSpec(kind, window=1)
+    rows_q = np.concatenate([np.arange(cu_q[b], cu_q[b] + uq[b]) for b in range(4)]).astype(int)
+    rows_k = np.concatenate([np.arange(cu_k[b], cu_k[b] + uk[b]) for b in range(4)]).astype(int)
+    tcu_q, tcu_k = np.concatenate([[0], np.cumsum(uq)]), np.concatenate([[0], np.cumsum(uk)])
+    o, lse = oracle.forward_varlen(q, k, v, cu_q, cu_k, mask=m, seqused_q=np.array(uq), seqused_k=np.array(uk))
+    to, tl = oracle.forward_varlen(q[rows_q], k[rows_k], v[rows_k], tcu_q, tcu_k, mask=m)
+    assert np.array_equal(o[rows_q], to) and np.array_equal(lse[:, rows_q], tl)
+    rest_q = np.setdiff1d(np.arange(cu_q[-1]), rows_q)
+    assert np.all(np.isnan(o[rest_q])) and np.all(np.isnan(lse[:, rest_q]))
+    g = oracle.backward_varlen(q, k, v, do, cu_q, cu_k, mask=m, seqused_q=np.array(uq), seqused_k=np.array(uk))
+    t = oracle.backward_varlen(q[rows_q], k[rows_k], v[rows_k], do[rows_q], tcu_q, tcu_k, mask=m)
+    assert np.array_equal(g[0][rows_q], t[0])
+    assert np.array_equal(g[1][rows_k], t[1]) and np.array_equal(g[2][rows_k], t[2])
+    rest_k = np.setdiff1d(np.arange(cu_k[-1]), rows_k)
+    assert np.all(np.isnan(g[0][rest_q])) and np.all(np.isnan(g[1][rest_k])) and np.all(np.isnan(g[2][rest_k]))
+
+
+def test_seqused_outside_the_span_is_rejected():
+    rng = np.random.default_rng(23)
+    cu_q, cu_k, q, k, v, _ = _packed(rng, [3, 2], [3, 2])
+    with pytest.raises(ValueError):
+        oracle.forward_varlen(q, k, v, cu_q, cu_k, seqused_q=np.array([4, 2]))
+    with pytest.raises(ValueError):
+        oracle.forward_varlen(q, k, v, cu_q, cu_k, seqused_k=np.array([1, -1]))
