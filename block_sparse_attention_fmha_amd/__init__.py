@@ -102,6 +102,10 @@ def load_library():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m block_sparse_attention_fmha_amd.build` (no fallback path exists)")
+    # torch first: its HIP runtime is then the one the library's HIP calls resolve to (loading
+    # the library alone first would bring in a second runtime copy that sees no device once
+    # torch has set up its own)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     lib.fmha_fwd.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.c_void_p]
     lib.fmha_fwd.restype = ctypes.c_int

@@ -41,7 +41,11 @@ std::mutex g_arch_mu;
 
 int check_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FMHA_ERR_HIP;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) {
+    FMHA_LOG("hipGetDevice failed: %s", hipGetErrorString(ge));
+    return FMHA_ERR_HIP;
+  }
   if (dev < 0 || dev >= kMaxDevices) return FMHA_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_arch_mu);
   if (g_arch_ok[dev] == 0) {
