@@ -24,12 +24,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfmha.so")
 
 FMHA_OK, FMHA_ERR_INVALID_ARG, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP, FMHA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+FMHA_ERR_SCRATCH_TOO_SMALL = -5
 FMHA_BF16, FMHA_FP32 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding_window": 2, "block_diagonal": 3, "prefix_lm": 4}
 ABI_VERSION = 3   # the struct layouts below (fmha_abi_version of include/fmha.h)
 ENTRY_POINTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_splitkv",
-                "fmha_fwd_splitkv_workspace_size", "fmha_fwd_varlen", "fmha_bwd_varlen", "build_block_mask",
-                "fmha_status_string", "fmha_abi_version")
+                "fmha_fwd_splitkv_workspace_size", "fmha_fwd_splitkv_noalloc", "fmha_fwd_splitkv_noalloc_max_bytes",
+                "fmha_fwd_varlen", "fmha_bwd_varlen", "build_block_mask", "fmha_status_string", "fmha_abi_version")
 
 
 class FmhaError(RuntimeError):
@@ -121,6 +122,10 @@ def load_library():
     lib.fmha_bwd_varlen.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.POINTER(CBwdArgs), ctypes.POINTER(CVarlen),
                                     ctypes.c_void_p]
     lib.fmha_bwd_varlen.restype = ctypes.c_int
+    lib.fmha_fwd_splitkv_noalloc.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.c_int32, ctypes.c_void_p]
+    lib.fmha_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.fmha_fwd_splitkv_noalloc_max_bytes.argtypes = []
+    lib.fmha_fwd_splitkv_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.fmha_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.build_block_mask.argtypes = [ctypes.POINTER(CMask)] + [ctypes.c_int32] * 6 + [
@@ -340,6 +345,25 @@ def fmha_fwd_splitkv(q, k, v, num_splits: int, *, scale=None, mask: Mask | None 
     _check(lib.fmha_fwd_splitkv(ctypes.byref(a), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
                                 workspace.numel() * workspace.element_size(), _stream(stream)),
            "fmha_fwd_splitkv")
+    return out, lse
+
+
+def fmha_fwd_splitkv_noalloc(q, k, v, num_splits: int, *, scale=None, mask: Mask | None = None,
+                             out=None, lse=None, stream=None):
+    """fmha_fwd_splitkv with the partials in the library's own fixed device scratch (no
+    workspace, no allocation inside the call when out / lse are given): returns (out, lse).
+    Calls that overlap on one GPU race on that scratch."""
+    import torch
+    lib = load_library()
+    B, Nq, H, _ = q.shape
+    Dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, Nq, H, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    a, _keep = _fwd_args(q, k, v, out, lse, scale, 0.0, 0.0, mask, None)
+    _check(lib.fmha_fwd_splitkv_noalloc(ctypes.byref(a), int(num_splits), _stream(stream)),
+           "fmha_fwd_splitkv_noalloc")
     return out, lse
 
 

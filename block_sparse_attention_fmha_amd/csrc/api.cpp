@@ -220,6 +220,37 @@ ListParams bwd_lists(const fmha_block_sparse* bs) {
   return l;
 }
 
+// Library-owned scratch of fmha_fwd_splitkv_noalloc: one array per GPU the library runs on,
+// held until the process ends. Host code must never pass the array's own name to a kernel or
+// copy (on the host it is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) {
+    FMHA_LOG("hipGetDevice failed: %s", hipGetErrorString(ge));
+    return FMHA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FMHA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      FMHA_LOG("hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return FMHA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FMHA_OK;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return FMHA_OK;
   FMHA_LOG("HIP error: %s", hipGetErrorString(e));
@@ -241,6 +272,7 @@ const char* fmha_status_string(int status) {
     case FMHA_ERR_UNSUPPORTED: return "FMHA_ERR_UNSUPPORTED";
     case FMHA_ERR_HIP: return "FMHA_ERR_HIP";
     case FMHA_ERR_WORKSPACE: return "FMHA_ERR_WORKSPACE";
+    case FMHA_ERR_SCRATCH_TOO_SMALL: return "FMHA_ERR_SCRATCH_TOO_SMALL";
     default: return "FMHA_ERR_UNKNOWN";
   }
 }
@@ -365,6 +397,28 @@ int fmha_bwd_varlen(const fmha_fwd_args* a, const fmha_bwd_args* g, const fmha_v
 size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t Dv, int32_t num_splits) {
   if (B < 0 || H < 0 || Nq < 0 || Dv <= 0 || num_splits < 1) return 0;
   return fmha::splitkv_workspace_bytes(B, H, Nq, Dv, num_splits);
+}
+
+size_t fmha_fwd_splitkv_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int fmha_fwd_splitkv_noalloc(const fmha_fwd_args* a, int32_t num_splits, void* stream) {
+  // the size check comes first: it needs no device
+  if (a != nullptr && a->B >= 0 && a->H >= 0 && a->Nq >= 0 && a->Dv > 0 && num_splits >= 1 &&
+      fmha::splitkv_workspace_bytes(a->B, a->H, a->Nq, a->Dv, num_splits) > kScratchBytes) {
+    FMHA_LOG("fmha_fwd_splitkv_noalloc: %zu partial bytes exceed the %zu-byte scratch",
+             fmha::splitkv_workspace_bytes(a->B, a->H, a->Nq, a->Dv, num_splits), kScratchBytes);
+    return FMHA_ERR_SCRATCH_TOO_SMALL;
+  }
+  int rc = validate_fwd(a);
+  if (rc != FMHA_OK) return rc;
+  if (num_splits < 1 || num_splits > 64) return FMHA_ERR_INVALID_ARG;
+  if ((int64_t)a->B * a->H * a->Nq == 0) return FMHA_OK;
+  rc = check_device();
+  if (rc != FMHA_OK) return rc;
+  void* ptr = nullptr;
+  rc = scratch_address(&ptr);
+  if (rc != FMHA_OK) return rc;
+  return fmha_fwd_splitkv(a, num_splits, ptr, kScratchBytes, stream);
 }
 
 int fmha_fwd_splitkv(const fmha_fwd_args* a, int32_t num_splits, void* workspace, size_t workspace_bytes,

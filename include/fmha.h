@@ -64,7 +64,9 @@ typedef enum {
   FMHA_ERR_INVALID_ARG = -1,   /* null pointer, bad shape/stride/size, inconsistent lists */
   FMHA_ERR_UNSUPPORTED = -2,   /* valid request the library does not implement, or not gfx950 */
   FMHA_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
-  FMHA_ERR_WORKSPACE = -4      /* workspace missing or smaller than the *_workspace_size */
+  FMHA_ERR_WORKSPACE = -4,     /* workspace missing or smaller than the *_workspace_size */
+  FMHA_ERR_SCRATCH_TOO_SMALL = -5  /* request needs more than the library-owned scratch of a
+                                      no-allocation entry point */
 } fmha_status;
 
 typedef enum { FMHA_BF16 = 0, FMHA_FP32 = 1 } fmha_dtype;
@@ -200,6 +202,21 @@ size_t fmha_fwd_splitkv_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t
                                        int32_t num_splits);
 int fmha_fwd_splitkv(const fmha_fwd_args* args, int32_t num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): fmha_fwd_splitkv with its partials in
+ * a library-owned device buffer instead of a caller workspace. The buffer is a fixed
+ * fmha_fwd_splitkv_noalloc_max_bytes() (16 MiB) per GPU, held from the first call on that
+ * GPU until the process ends; requests whose partials need more
+ * (fmha_fwd_splitkv_workspace_size(B, H, Nq, Dv, num_splits) bytes) return
+ * FMHA_ERR_SCRATCH_TOO_SMALL before anything is launched. Nothing is allocated by the call.
+ * Every call on one GPU uses the same buffer: calls whose executions overlap on one GPU
+ * (different streams, or different host threads without ordering) race and must not be
+ * issued; calls ordered on one stream are safe. The buffer keeps the last call's partials;
+ * each call writes every entry it reads, so nothing needs clearing. Arguments and results
+ * otherwise as fmha_fwd_splitkv. */
+size_t fmha_fwd_splitkv_noalloc_max_bytes(void);
+int fmha_fwd_splitkv_noalloc(const fmha_fwd_args* args, int32_t num_splits, void* stream);
 
 /* Packed variable-length sequences ("Enable 2CTA for SM100 block-sparse backward",
  * section "Testing Testing Testing": the forward call's cu_seqlens_q / cu_seqlens_k and

@@ -310,3 +310,15 @@ def test_backward_without_queries_still_validates_keys(lib, bad):
         s[0], s[1], s[2] = 64 * 2 * 128, 2 * 128, 128
     g.workspace, g.workspace_bytes = 0x200000, lib.fmha_bwd_workspace_size(1, 2, 0)
     assert lib.fmha_bwd(ctypes.byref(a), ctypes.byref(g), None) == fa.FMHA_ERR_INVALID_ARG
+
+
+def test_noalloc_splitkv_rejects_requests_beyond_its_scratch(lib):
+    # the size check needs no device: partials of B*H*Nq*splits rows of (Dv + 1) fp32
+    cap = lib.fmha_fwd_splitkv_noalloc_max_bytes()
+    assert cap == 16 << 20
+    a = _args(B=64, H=64, Nq=1, Nk=4096)
+    need = lib.fmha_fwd_splitkv_workspace_size(64, 64, 1, 128, 16)
+    assert need > cap
+    assert lib.fmha_fwd_splitkv_noalloc(ctypes.byref(a), 16, None) == fa.FMHA_ERR_SCRATCH_TOO_SMALL
+    assert fa.status_string(fa.FMHA_ERR_SCRATCH_TOO_SMALL) == "FMHA_ERR_SCRATCH_TOO_SMALL"
+    assert lib.fmha_fwd_splitkv_noalloc(ctypes.byref(a), 0, None) == fa.FMHA_ERR_INVALID_ARG
