@@ -25,10 +25,12 @@
 //      register group, which is the B operand of the dV / dK products as is; dO^T / Q^T
 //      come from transposed LDS reads;
 //   3. dQ pass: a workgroup owns 128 queries and walks 64-key tiles of K / V (direct
-//      global->LDS loads, 3-4 stages), again in wave pairs sharing 32 queries: the "S wave"
-//      holds Q, computes S^T = K Q^T and P and hands P over; the "dQ wave" holds dO,
-//      computes dP^T = V dO^T and dS, and accumulates dQ^T += K^T dS^T (K^T from
-//      transposed LDS reads). Lane = query in both, as in the forward.
+//      global->LDS loads, 3-4 stages), again in wave pairs sharing 32 queries, but here
+//      the pair splits each tile's keys: both waves hold Q and dO, and each computes
+//      S^T = K Q^T, dP^T = V dO^T, P and dS for its 32 keys and accumulates its own
+//      partial dQ^T += K^T dS^T (K^T from transposed LDS reads), one phase apart so the
+//      MFMAs of one overlap the exp / dS arithmetic of the other. The two partials are
+//      added once at the end in a fixed order. Lane = query, as in the forward.
 // The dQ pass recomputes S and dP (7 matrix products instead of 5): that is the price
 // of determinism without atomics.
 //
@@ -353,13 +355,16 @@ void bwd_dkdv_kernel(const BwdParams bp) {
       }
   };
 
+  // Step t refills the stage of step t - 2 (read up to step t - 1) with step t + NST - 2;
+  // each wave issues its share at the start of its vector phase, where the time the
+  // vector-memory path takes to accept the loads is hidden under the partner's MFMAs (as
+  // in the forward). The hand-over of step t is written in its second phase and read in
+  // the first phase of step t + 1, so with a double-buffered hand-over the end-of-step
+  // barrier alone orders every LDS reuse; otherwise a barrier also separates the two
+  // phases.
   auto step_begin = [&](int t) {
     if (t + SM::NST - 2 < T) issue_step(t + SM::NST - 2);
   };
-  // Stages are refilled only at the start of a step and the hand-over of step t is
-  // written in its second phase and read in the first phase of step t + 1, so with a
-  // double-buffered hand-over the end-of-step barrier alone orders every LDS reuse;
-  // otherwise a barrier also separates the two phases.
   auto mid = [&]() {
     if (!SM::DBLX) __syncthreads();
   };
@@ -395,19 +400,18 @@ void bwd_dkdv_kernel(const BwdParams bp) {
 
   if (role == 0) {
     if (T > 0) {
-      step_begin(0);
       matrix(IntC<0>{}, 0, false, true);
       mid();
+      step_begin(0);
       p_vector(0);
       step_end(0);
       for (int t = 1; t < T; ++t) {
-        step_begin(t);
         matrix(IntC<0>{}, t, true, true);
         mid();
+        step_begin(t);
         p_vector(t);
         step_end(t);
       }
-      step_begin(T);
       matrix(IntC<0>{}, T, true, false);
       mid();
       step_end(T);
@@ -426,7 +430,6 @@ void bwd_dkdv_kernel(const BwdParams bp) {
         matrix(IntC<1>{}, t, true, true);
         step_end(t);
       }
-      step_begin(T);
       ds_vector(T - 1);
       mid();
       matrix(IntC<1>{}, T, true, false);
@@ -436,9 +439,14 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   }
 }
 
-// ------------------------------------------------------------------------------- dQ
+// ------------------------------------------------------------------------------- dQ, DQK != DV
+// Used where the head dims differ (192 / 128): with Q, dO and the wider dQ^T accumulator
+// all held by each wave, the key-split pass below would exceed the register budget of two
+// waves per SIMD. Here the pair splits the work by role instead: the "S wave" holds Q,
+// computes S^T = K Q^T and P and hands P over through LDS; the "dQ wave" holds dO,
+// computes dP^T = V dO^T and dS, and accumulates dQ^T += K^T dS^T.
 template <int DQK, int DV, bool LISTS>
-struct DqSmem {
+struct DqRolesSmem {
   static constexpr int KPC = DualPitch<DQK>::value, VPC = RowPitch<DV>::value;
   static constexpr int KP = KPC * 16, VP = VPC * 16;
   static constexpr int KB = kKN * KP, VB = kKN * VP;
@@ -456,8 +464,8 @@ struct DqSmem {
 
 template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1)
-void bwd_dq_kernel(const BwdParams bp) {
-  using SM = DqSmem<DQK, DV, LISTS>;
+void bwd_dq_roles_kernel(const BwdParams bp) {
+  using SM = DqRolesSmem<DQK, DV, LISTS>;
   constexpr int DM = DQK > DV ? DQK : DV;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnParams& p = bp.a;
@@ -716,6 +724,320 @@ void bwd_dq_kernel(const BwdParams bp) {
   }
 }
 
+// ------------------------------------------------------------------------------- dQ
+template <int DQK, int DV, bool LISTS>
+struct DqSmem {
+  static constexpr int KPC = DualPitch<DQK>::value, VPC = RowPitch<DV>::value;
+  static constexpr int KP = KPC * 16, VP = VPC * 16;
+  static constexpr int KB = kKN * KP, VB = kKN * VP;
+  static constexpr int STAGE = KB + VB;
+  static constexpr int NST = (4 * STAGE <= (LISTS ? 148 : 160) * 1024) ? 4 : 3;
+  static constexpr int BYTES = NST * STAGE;
+  // closing exchange of partial dQ^T: 8 waves x DQK / 64 accumulator blocks x 4 KiB
+  static constexpr int XBYTES = 8 * (DQK / 64) * 4096;
+  static_assert(XBYTES <= BYTES, "the closing exchange reuses the K / V stages");
+};
+
+// One matrix phase of the dQ pass as a software pipeline over single-MFMA items:
+//   NT items acc[i / 2] += K^T dS^T (A from two transposed 8-byte reads of the K tile at
+//      t0, keys + 16 (i % 2), head dims + 32 (i / 2); B = ds[i % 2]),
+//   NK items s += K Q^T (A = 16-byte K row read at k0 + 32 ks; B = qf[ks]),
+//   NV items dp += V dO^T (A = 16-byte V row read at v0 + 32 ks; B = of[ks]).
+// The read of item i + AHEAD is issued right after item i's MFMA and the scheduler is
+// fenced per item, so reads stay in flight across the MFMAs (as in pipelined_matrix).
+template <int NT, int NK, int NV, int KP, int AHEAD, int NACC>
+__device__ __forceinline__ void dq_matrix(const char* t0, const char* k0, const char* v0, bool do_t, bool do_s,
+                                          f32x16 (&acc)[NACC], const bf16x8 (&ds)[2], f32x16& s, f32x16& dp,
+                                          const bf16x8 (&qf)[NK], const bf16x8 (&of)[NV]) {
+  constexpr int N = NT + NK + NV;
+  auto load = [&](int i) -> bf16x8 {
+    if (i < NT) {
+      const char* tp = t0 + 16 * (i & 1) * KP + 64 * (i >> 1);
+      return join_bf16x8(lds_read_tr(tp), lds_read_tr(tp + 4 * KP));
+    }
+    if (i < NT + NK) return *(const bf16x8*)(k0 + 32 * (i - NT));
+    return *(const bf16x8*)(v0 + 32 * (i - NT - NK));
+  };
+  auto run = [&](int i, const bf16x8& a) {
+    if (i < NT) acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ds[i & 1], acc[i >> 1], 0, 0, 0);
+    else if (i < NT + NK) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i - NT], s, 0, 0, 0);
+    else dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[i - NT - NK], dp, 0, 0, 0);
+  };
+  const int first = do_t ? 0 : NT, last = do_s ? N : NT;
+  if (do_s) {
+    s = f32x16{};
+    dp = f32x16{};
+  }
+  bf16x8 ring[AHEAD];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i >= first && i < first + AHEAD && i < last) ring[i % AHEAD] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < first || i >= last) continue;
+    __builtin_amdgcn_sched_barrier(0);
+    run(i, ring[i % AHEAD]);
+    if (i + AHEAD < last) ring[i % AHEAD] = load(i + AHEAD);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
+__global__ __launch_bounds__(kThreads, 1)
+void bwd_dq_kernel(const BwdParams bp) {
+  using SM = DqSmem<DQK, DV, LISTS>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const AttnParams& p = bp.a;
+
+  const int bid = xcd_remap(blockIdx.x, p.grid_padded);
+  if (bid >= p.total_work) return;
+  const int bh = bid / p.n_tiles;
+  const int t = bid - bh * p.n_tiles;
+  const int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int q0 = qt * kQM;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 5, lq = l & 31;
+  const int half = w >> 2;     // keys 32 half .. 32 half + 31 of every tile
+  const int pair = w & 3;      // waves w and w + 4 share a SIMD and the same 32 queries
+  const SeqInfo sq = seq_info(p, b);
+  const int Nq = sq.nq, Nk = sq.nk, delta = Nk - Nq;
+  if (q0 >= Nq) return;        // packed sequences: past this one's queries (whole workgroup, no barrier yet)
+  const int qw = q0 + 32 * pair;
+  const int qrow = qw + lq;
+
+  const __bf16* Qg = (const __bf16*)p.q + row_base(sq, true, b, p.qs_b, p.qs_s) + h * p.qs_h;
+  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + kv_head(p, h) * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + kv_head(p, h) * p.vs_h;
+  const __bf16* DOg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h * bp.dos_h;
+
+  // ---- key-tile sequence (same bands / lists as the forward)
+  TileSeq<kKN> seq;
+  seq.t_lo = 0;
+  seq.ent = (const uint32_t*)(smem + SM::BYTES + 16);
+  const int mk = p.mask.kind;
+  if constexpr (!LISTS) {
+    int lo = 0, hi = Nk;
+    if (mk == kMaskCausal || mk == kMaskWindow) hi = min(Nk, q0 + kQM + delta);
+    if (mk == kMaskPrefix) hi = min(Nk, max(p.mask.prefix, q0 + kQM + delta));
+    if (mk == kMaskWindow) lo = max(0, q0 + delta - p.mask.window);
+    hi = max(hi, 0);
+    seq.t_lo = lo / kKN;
+    seq.count = max(0, (hi + kKN - 1) / kKN - seq.t_lo);
+  } else {
+    const ListParams& L = p.lists;   // the workgroup's 128 queries lie in one sparse row
+    const int64_t row = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h)) * L.n_rows + q0 / L.tile_rows;
+    seq.count = build_tile_sequence<kThreads, kKN>(L, row, -1, Nk, smem + SM::BYTES, tid);
+  }
+
+  // ---- B operands of S^T (Q) and dP^T (dO): the lane's query, k-slot = head dim
+  bf16x8 qf[DQK / 16], of[DV / 16];
+#pragma unroll
+  for (int ks = 0; ks < DQK / 16; ++ks)
+    qf[ks] = qrow < Nq ? *(const bf16x8*)(Qg + (int64_t)qrow * p.qs_s + 16 * ks + 8 * g) : bf16x8{};
+#pragma unroll
+  for (int ks = 0; ks < DV / 16; ++ks)
+    of[ks] = qrow < Nq ? *(const bf16x8*)(DOg + (int64_t)qrow * bp.dos_s + 16 * ks + 8 * g) : bf16x8{};
+  // lse2 and D of the lane's query; rows past Nq carry lse2 = +inf, so their P is 0
+  float lse2 = __builtin_huge_valf(), dsum = 0.0f;
+  if (qrow < Nq) {
+    const float* wq = bp.ws + ((int64_t)bh * bp.n_qblk + qrow / 64) * 128 + qrow % 64;
+    lse2 = wq[0];
+    dsum = wq[64];
+  }
+  const int dqd = (mk == kMaskBlockDiag && qrow < Nq) ? p.mask.doc_q[(int64_t)b * Nq + qrow] : 0;
+  // element-mask geometry, computed once (as in the forward)
+  int need_above, need_below;
+  key_tile_need(p.mask, qw, Nk, delta, kKN, need_above, need_below);
+  if constexpr (LISTS) need_above = Nk - kKN, need_below = INT32_MIN;   // the list classes decide
+  int band_lo, band_hi;
+  band_interval(p.mask, qrow, Nq, Nk, band_lo, band_hi);
+
+  f32x16 dq[DQK / 32];
+#pragma unroll
+  for (int i = 0; i < DQK / 32; ++i) dq[i] = f32x16{};
+  const int prow = swap_bits23(lq);
+  const int trow = 8 * g + ((l & 15) >> 2);
+  const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const float c_eff = (SOFTCAP || BIAS) ? 1.0f : p.scale_log2;
+
+  LdsDma<kKN, DQK, SM::KPC, kThreads> kdma;
+  LdsDma<kKN, DV, SM::VPC, kThreads> vdma;
+  kdma.init(p.ks_s, tid);
+  vdma.init(p.vs_s, tid);
+  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // defensive: every slot is loaded before it is read
+  auto issue_tile = [&](int t) {
+    const int n0 = seq.start(t, LISTS);
+    char* st = smem + (t % SM::NST) * SM::STAGE;
+    kdma.issue(Kg, p.ks_s, n0, Nk, st);
+    vdma.issue(Vg, p.vs_s, n0, Nk, st + SM::KB);
+  };
+
+  f32x16 s, dp;
+  bf16x8 ds[2];
+  const int T = seq.count;
+  for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_tile(t);
+  wait_all_vmem();
+  __syncthreads();
+
+  // Steps t = 0 .. T, two phases each. Both waves of a pair do the same work on their own
+  // 32 keys of each tile; the half-1 wave runs one phase behind, so one wave's MFMAs
+  // overlap the other's vector work on their shared SIMD:
+  //   half 0, step t: matrix [dQ^T += K^T dS^T of tile t-1; S^T, dP^T of tile t], vector dS of tile t
+  //   half 1, step t: vector dS of tile t-1, matrix [the same as half 0's]
+  // Tile t's stage is read during steps t and t+1. No data passes between the waves until
+  // the closing exchange.
+  auto matrix = [&](int ts, bool do_dq, bool do_s) {
+    const int sp = (ts - 1 + SM::NST) % SM::NST, sc = ts % SM::NST;
+    const char* t0 = smem + opaque_int(sp * SM::STAGE + (32 * half + trow) * SM::KP + tcol * 2);
+    const char* k0 = smem + opaque_int(sc * SM::STAGE + (32 * half + prow) * SM::KP + 16 * g);
+    const char* v0 = smem + opaque_int(sc * SM::STAGE + SM::KB + (32 * half + prow) * SM::VP + 16 * g);
+    dq_matrix<DQK / 16, DQK / 16, DV / 16, SM::KP, 2>(t0, k0, v0, do_dq, do_s, dq, ds, s, dp, qf, of);
+  };
+
+  // dS = P (dP - D) of tile ts (score transform, element mask, exp against the row's lse2)
+  // into ds; reg r of s / dp holds key n0 + 32 half + 16 (r / 8) + 8 g + r % 8, so
+  // ds[hh] (regs 8 hh .. 8 hh + 7) is the B operand of the dQ^T product as is
+  auto vector = [&](int ts) {
+    const int n0 = seq.start(ts, LISTS);
+    bool need = n0 > need_above || n0 < need_below;
+    bool elem = true, hide = false;
+    if constexpr (LISTS) {
+      const uint32_t c = seq.cls(ts, 0, true);
+      hide = c == 0u;
+      elem = c == 1u;
+      need = need || c != 2u;
+    }
+    // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents)
+    const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
+    const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;   // wave-uniform
+    const bool band = elem && mk != kMaskBlockDiag;
+    const int lo = band ? band_lo : 0, hi = hide ? 0 : band ? band_hi : Nk;
+    const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
+    auto body = [&](auto test_c) {
+      constexpr int TEST = decltype(test_c)::value;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int jb = (TEST != kTestNone || BIAS) ? opaque_int(n0 + 32 * half + 16 * hh + 8 * g) : 0;
+        // relative bias alone: i - j = (qrow - jb) - (2 e + z), exact in fp32 (as in the forward)
+        const float dij = (BIAS && !SOFTCAP) ? __int_as_float(opaque_int(__float_as_int((float)(qrow - jb)))) : 0.0f;
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float dv[2];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int r = 8 * hh + 2 * e + z;
+            const int j = jb + 2 * e + z;
+            float dcap = 1.0f, u = s[r];
+            if constexpr (BIAS && !SOFTCAP)
+              u = __builtin_fmaf(u, p.scale_log2, p.bias_log2 * __builtin_fabsf(dij - (float)(2 * e + z)));
+            else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
+            if constexpr (TEST != kTestNone) {
+              bool vis = (unsigned)(j - lo) < span;
+              if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
+              if (!vis) u = kNegInf;
+            }
+            float pv = fast_exp2(__builtin_fmaf(u, c_eff, -lse2));
+            if constexpr (SOFTCAP) pv *= dcap;
+            dv[z] = pv * (dp[r] - dsum);
+          }
+          pk[e] = pack_bf16x2(dv[0], dv[1]);
+        }
+        ds[hh] = __builtin_bit_cast(bf16x8, pk);
+      }
+    };
+    if (!need) body(IntC<kTestNone>{});
+    else if (!bdw) body(IntC<kTestBand>{});
+    else body(IntC<kTestDoc>{});
+  };
+
+  // End of step t: tile t + 1 (read from the next step on) must have landed; the loads of
+  // the NST - 3 tiles issued after it may stay in flight.
+  auto step_end = [&](int t) {
+    const int later = min(SM::NST - 3, max(0, T - 2 - t));
+    if (later > 0) kdma.wait_leaving(vdma, later);
+    else wait_lds_dma();
+    __syncthreads();
+  };
+
+  // Step t refills the stage of tile t - 2 (read up to step t - 1) with tile t + NST - 2;
+  // each wave issues its share at the start of its vector phase, where the time the
+  // vector-memory path takes to accept the loads is hidden under the partner's MFMAs (as
+  // in the forward). The half-1 waves have no vector phase in step 0 and issue first.
+  auto step_begin = [&](int t) {
+    if (t + SM::NST - 2 < T) issue_tile(t + SM::NST - 2);
+  };
+
+  if (T > 0) {
+    if (half == 0) {
+      matrix(0, false, true);
+      step_begin(0);
+      vector(0);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        matrix(t, true, true);
+        step_begin(t);
+        vector(t);
+        step_end(t);
+      }
+      matrix(T, true, false);
+      step_end(T);
+    } else {
+      step_begin(0);
+      matrix(0, false, true);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        vector(t - 1);
+        matrix(t, true, true);
+        step_end(t);
+      }
+      vector(T - 1);
+      matrix(T, true, false);
+      step_end(T);
+    }
+  }
+
+  // ---- closing exchange and epilogue: each wave holds dQ^T over its own keys; it keeps
+  // head-dim blocks [half NB, half NB + NB) and hands the other NB to its partner through
+  // the (now idle) stage memory. Both add own + other, which is the same sum bitwise in
+  // either wave, so the result has one fixed summation order. Lane = query,
+  // reg r of block db <-> d = 32 db + 8 (r / 4) + 4 g + r % 4.
+  constexpr int NB = DQK / 64;
+  auto finish = [&](auto half_c) {
+    constexpr int HF = decltype(half_c)::value;
+    f32x4* xo = (f32x4*)(smem + w * NB * 4096) + l;
+    const f32x4* xi = (const f32x4*)(smem + (w ^ 4) * NB * 4096) + l;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x16& a = dq[(1 - HF) * NB + j];
+        xo[64 * (4 * j + c)] = f32x4{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+      }
+    __syncthreads();
+    if (qrow >= Nq) return;
+    __bf16* dQg = (__bf16*)bp.dq + row_base(sq, true, b, bp.dqs_b, bp.dqs_s) + h * bp.dqs_h + (int64_t)qrow * bp.dqs_s;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int db = HF * NB + j;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 o = xi[64 * (4 * j + c)];
+        u32x2 v;
+        v[0] = pack_bf16x2((dq[db][4 * c] + o[0]) * p.scale, (dq[db][4 * c + 1] + o[1]) * p.scale);
+        v[1] = pack_bf16x2((dq[db][4 * c + 2] + o[2]) * p.scale, (dq[db][4 * c + 3] + o[3]) * p.scale);
+        *(u32x2*)(dQg + 32 * db + 8 * c + 4 * g) = v;
+      }
+    }
+  };
+  if (half == 0) finish(IntC<0>{});
+  else finish(IntC<1>{});
+}
+
 hipError_t record_stage(const BwdParams& bp, int i, hipStream_t st) {
   if (bp.stage_events == nullptr) return hipSuccess;
   return hipEventRecord(static_cast<hipEvent_t>(bp.stage_events[i]), st);
@@ -741,8 +1063,16 @@ hipError_t launch_passes(const BwdParams& bp, hipStream_t st) {
     }
   }
   {
-    auto kern = bwd_dq_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
-    const int bytes = DqSmem<DQK, DV, LISTS>::BYTES + list_bytes(bp.a.lists, kKN);
+    // key-split pass; role-split pass for unequal head dims
+    void (*kern)(const BwdParams);
+    int bytes = list_bytes(bp.a.lists, kKN);
+    if constexpr (DQK == DV) {
+      kern = bwd_dq_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
+      bytes += DqSmem<DQK, DV, LISTS>::BYTES;
+    } else {
+      kern = bwd_dq_roles_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
+      bytes += DqRolesSmem<DQK, DV, LISTS>::BYTES;
+    }
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     e = record_stage(bp, 2, st);
@@ -766,10 +1096,16 @@ hipError_t dispatch(const BwdParams& bp, bool lists, bool softcap, bool bias, hi
   return bias ? launch_passes<DQK, DV, false, false, true>(bp, st) : launch_passes<DQK, DV, false, false, false>(bp, st);
 }
 
+template <int DQK, int DV, bool LISTS>
+constexpr int dq_smem_bytes() {
+  if constexpr (DQK == DV) return DqSmem<DQK, DV, LISTS>::BYTES;
+  else return DqRolesSmem<DQK, DV, LISTS>::BYTES;
+}
+
 template <int DQK, int DV>
 bool lists_fit_dims(const ListParams& fwd, const ListParams& tr) {
   return DkdvSmem<DQK, DV>::BYTES + list_bytes(tr, kQS) <= kMaxLdsBytes &&
-         DqSmem<DQK, DV, true>::BYTES + list_bytes(fwd, kKN) <= kMaxLdsBytes;
+         dq_smem_bytes<DQK, DV, true>() + list_bytes(fwd, kKN) <= kMaxLdsBytes;
 }
 
 }  // namespace

@@ -192,9 +192,14 @@ void fwd_bf16_kernel(const AttnParams p) {
   //                      vector  softmax of S(t) into P (t < T)
   //   waves 4-7, step t: vector  softmax of S(t-1) (t > 0);  matrix as above
   // so the two waves of a SIMD alternate between MFMA and VALU work. Tile t's stage is
-  // busy during phases 2t .. 2t+3; tile t is issued at the start of step t - NST + 2 (the
-  // first NST - 2 tiles before the loop), once the stage's previous tile (t - NST) is
-  // done. Each group runs its own loop with the first and last steps peeled, so nothing
+  // busy during phases 2t .. 2t+3; tile t is issued in step t - NST + 2 (the first NST - 2
+  // tiles before the loop), once the stage's previous tile (t - NST) is done. Each wave
+  // issues its share at the start of its vector phase: issuing a direct-to-LDS load holds
+  // the wave until the vector-memory path takes it (about 1 KiB per 16 clocks per CU), and
+  // there the wait is hidden under the partner wave's MFMAs, and each group of four waves
+  // has the path to itself (issued by all eight waves after the barrier, the loads held
+  // every matrix phase back). Each group runs its own loop with the first and last steps
+  // peeled, so nothing
   // conditional sits between the phases and the loop-carried operands keep their
   // registers.
   // Matrix phase: O += V(ts - 1) P (V read transposed) and S = K Q^T (two accumulation
@@ -285,6 +290,7 @@ void fwd_bf16_kernel(const AttnParams p) {
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
+  // issue tile t + NST - 2 (called at the start of the wave's vector phase of step t)
   auto step_begin = [&](int t) {
     if (t + SM::NST - 2 < T) issue_tile(t + SM::NST - 2);
   };
@@ -303,17 +309,16 @@ void fwd_bf16_kernel(const AttnParams p) {
 
   if (T > 0) {
     if (grp == 0) {
-      step_begin(0);
       matrix(0, false, true);
+      step_begin(0);
       vector(0);
       step_end(0);
       for (int t = 1; t < T; ++t) {
-        step_begin(t);
         matrix(t, true, true);
+        step_begin(t);
         vector(t);
         step_end(t);
       }
-      step_begin(T);
       matrix(T, true, false);
       step_end(T);
     } else {
@@ -326,7 +331,6 @@ void fwd_bf16_kernel(const AttnParams p) {
         matrix(t, true, true);
         step_end(t);
       }
-      step_begin(T);
       vector(T - 1);
       matrix(T, true, false);
       step_end(T);
