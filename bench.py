@@ -19,7 +19,8 @@ Prints ONE JSON line on stdout:
   cpu_baseline the CPU fp64 oracle on one head of the same workload (fwd + bwd), scaled
                to TFLOP/s of useful work
 --all-configs additionally prints per-workload timings of the other configurations to
-stderr (not part of the JSON line).
+stderr (not part of the JSON line), with the CPU oracle's time on each configuration
+(sampled (b, h) pairs, extrapolated; skipped with --no-cpu-baseline).
 """
 from __future__ import annotations
 
@@ -183,28 +184,111 @@ def profile_other_rows(reps: int):
     torch.cuda.synchronize()
 
 
-def cpu_baseline():
-    """The CPU fp64 oracle, as it stands, on one head of the workload (fwd + bwd)."""
-    import numpy as np
-    import oracle
-    from block_sparse_attention_fmha_amd import synth
+def host_info():
+    """The host the CPU oracle runs on: CPU model, logical CPUs, the CPUs this process may
+    use, the thread-count environment and the BLAS thread pools numpy's products use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    env = {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS",
+                                      "BLIS_NUM_THREADS") if k in os.environ}
     try:
         from threadpoolctl import threadpool_info
-        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
     except Exception:
-        cores = os.cpu_count() or 1
+        blas = []
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "thread_env": env, "blas_pools": blas}
+
+
+def oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return max(i.get("num_threads", 1) for i in info) if info else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline():
+    """The CPU fp64 oracle, as it stands, on one head of the workload (fwd + bwd)."""
+    import oracle
+    from block_sparse_attention_fmha_amd import synth
     q, k, v, do = synth.attention_inputs(synth.case_seed(2, 0), B, N, N, H, D, D, "bf16", with_dout=True)
     t0 = time.perf_counter()
     oracle.backward_bh(q.values[0, :, 0], k.values[0, :, 0], v.values[0, :, 0], do.values[0, :, 0], 0, 0,
                        scale=1.0 / math.sqrt(D), mask=oracle.MaskSpec("causal"))
     dt = time.perf_counter() - t0
     f, b = useful_flops(1, 1, causal_pairs(N), D, D)
-    return {"value": round((f + b) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"head 0 of {H} (b=0), full N={N} causal fwd+bwd, {dt:.1f} s wall"}
+    return {"value": round((f + b) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(oracle_threads()),
+            "kind": "oracle",
+            "sample": f"head 0 of {H} (b=0), full N={N} causal fwd+bwd, {dt:.1f} s wall; "
+                      f"the rate of that head is the whole workload's (every head costs the same)",
+            "host": host_info()}
 
 
-def all_configs_report():
-    """Extra timings of the other workloads, to stderr (median of events)."""
+def oracle_config_timings(log):
+    """The CPU oracle beside the other configurations: each timed on a stated sample of
+    (batch, head) pairs and extrapolated linearly to the whole configuration (every pair of
+    a configuration costs the same: the oracle materialises each (b, h) score matrix).
+    About half a minute of CPU work in all."""
+    import numpy as np
+    import oracle
+    from block_sparse_attention_fmha_amd import synth
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def report(config, workload, secs, done, total, unit_desc):
+        log(oracle=config, workload=workload, sample=f"{done} of {total} {unit_desc}",
+            sample_s=round(secs, 3), extrapolated_s=round(secs * total / done, 2), threads=oracle_threads())
+
+    # 1: fp32 forward B=1 H=1 N=128 D=64 causal (whole)
+    q, k, v = synth.attention_inputs(synth.case_seed(1, 0), 1, 128, 128, 1, 64, 64, "fp32")
+    secs = timed(lambda: oracle.forward(q.values, k.values, v.values, mask=oracle.MaskSpec("causal")))
+    report("1", "fwd fp32 B=1 H=1 N=128 D=64 causal", secs, 1, 1, "(b, h)")
+    # 3: block-sparse forward B=2 H=8 N=8192 D=128, relative bias, causal tiles (one head)
+    n = 8192
+    q, k, v = synth.attention_inputs(synth.case_seed(3, 0), 1, n, n, 1, 128, 128, "bf16")
+    idx = np.arange(n)
+    secs = timed(lambda: oracle.forward_bh(q.values[0, :, 0], k.values[0, :, 0], v.values[0, :, 0], idx, 0, 0,
+                                           n, n, scale=1.0 / math.sqrt(128), bias_slope=-0.01,
+                                           mask=oracle.MaskSpec("causal")))
+    report("3", "block-sparse fwd bf16 B=2 H=8 N=8192 D=128 causal, bias -0.01", secs, 1, 16, "(b, h)")
+    # 4: backward B=1 H=16, causal: N=4096 D=128 and the MLA shape N=8192 Dqk=192 Dv=128 (one
+    # head each); N=16384 D=128 is the cpu_baseline line itself
+    for n, dqk, dv in ((4096, 128, 128), (8192, 192, 128)):
+        q, k, v, do = synth.attention_inputs(synth.case_seed(4, n), 1, n, n, 1, dqk, dv, "bf16", with_dout=True)
+        secs = timed(lambda: oracle.backward_bh(q.values[0, :, 0], k.values[0, :, 0], v.values[0, :, 0],
+                                                do.values[0, :, 0], 0, 0, scale=1.0 / math.sqrt(dqk),
+                                                mask=oracle.MaskSpec("causal")))
+        report("4", f"bwd bf16 B=1 H=16 N={n} Dqk={dqk} Dv={dv} causal", secs, 1, 16, "(b, h)")
+    # 5a: split-KV decode B=8 H=32 Nq=1 Nk=32768 D=128, 16 splits + combine (8 (b, h) pairs)
+    nk = 32768
+    q, k, v = synth.attention_inputs(synth.case_seed(5, 0), 1, 1, nk, 8, 128, 128, "bf16")
+    secs = timed(lambda: oracle.combine_partials(oracle.split_partials(q.values, k.values, v.values, 16, 64)))
+    report("5a", "split-KV decode bf16 B=8 H=32 Nq=1 Nk=32768 D=128, 16 splits + combine", secs, 8, 256, "(b, h)")
+    # 5b: fp32 wide head B=4 H=8 N=512 D=1024 (one (b, h))
+    q, k, v = synth.attention_inputs(synth.case_seed(5, 1), 1, 512, 512, 1, 1024, 1024, "fp32")
+    secs = timed(lambda: oracle.forward(q.values, k.values, v.values))
+    report("5b", "fwd fp32 B=4 H=8 N=512 D=1024", secs, 1, 32, "(b, h)")
+
+
+def all_configs_report(oracle_too: bool = True):
+    """Extra timings of the other workloads, to stderr (median of events), and the CPU
+    oracle's time on each configuration (sampled; see oracle_config_timings)."""
     import numpy as np
     import torch
     import block_sparse_attention_fmha_amd as fa
@@ -226,6 +310,9 @@ def all_configs_report():
     def log(**kw):
         sys.stderr.write(json.dumps(kw) + "\n")
         sys.stderr.flush()
+
+    if oracle_too:
+        oracle_config_timings(log)
 
     # forward grid: N x D x mask x softcap (B=1 H=16)
     for n in (1024, 4096, 16384):
@@ -431,7 +518,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     if args.all_configs:
-        all_configs_report()
+        all_configs_report(oracle_too=not args.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 

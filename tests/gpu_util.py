@@ -4,6 +4,12 @@ The tolerances are the ones the workload specification states:
   fp32 O / LSE:   max |x - ref| <= 1e-4
   bf16 O / LSE:   |x - ref| <= 2e-2 + 2e-2 |ref| element-wise (-inf LSE matched exactly)
   bf16 gradients: ||g - ref||_2 / ||ref||_2 <= 1e-2 per tensor
+and, so that one wrong tile cannot hide in a whole-tensor norm, the gradient check also
+applies the 1e-2 bound to every (batch, head) slice and bounds every block of 128 rows
+(tokens) of a slice:
+  ||g_blk - ref_blk|| <= 2e-2 ||ref_blk|| + 2e-3 ||ref_slice|| sqrt(rows_blk / rows_slice)
+(the second term is the block's share of a 2e-3 slice-level floor, for blocks whose
+reference is near zero).
 """
 from __future__ import annotations
 
@@ -18,6 +24,9 @@ FP32_ATOL = 1e-4
 BF16_ATOL = 2e-2
 BF16_RTOL = 2e-2
 GRAD_RTOL = 1e-2
+GRAD_BLOCK_ROWS = 128
+GRAD_BLOCK_RTOL = 2e-2
+GRAD_BLOCK_FLOOR = 2e-3
 
 
 def announce(msg: str):
@@ -75,13 +84,51 @@ def check_fp32(name, got, ref, mask=None):
 
 
 def check_grad(name, got, ref):
+    """Gradient parity: whole tensor, every (batch, head) slice and every 128-row block.
+    Layouts: [B, N, H, D] (batched) or [T, H, D] (packed sequences, checked as one batch)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     den = np.linalg.norm(ref)
     num = np.linalg.norm(got - ref)
     rel = num / den if den > 0 else num
     assert rel <= GRAD_RTOL, f"{name}: norm-relative error {rel:.3e} > {GRAD_RTOL}"
+    check_grad_local(name, got, ref)
+
+
+def grad_local_errors(got, ref):
+    """Per-slice relative errors [B, H] and per-block error / bound ratios [B, H, nblk]."""
+    if ref.ndim == 3:
+        got, ref = got[None], ref[None]
+    B, N, H, D = ref.shape
+    nblk = max(1, -(-N // GRAD_BLOCK_ROWS))
+    pad = nblk * GRAD_BLOCK_ROWS - N
+    diff = got - ref
+    # [B, N, H, D] -> [B, H, nblk, rows, D]
+    def blocks(x):
+        x = np.pad(x, ((0, 0), (0, pad), (0, 0), (0, 0)))
+        return x.reshape(B, nblk, GRAD_BLOCK_ROWS, H, D).transpose(0, 3, 1, 2, 4)
+    e2 = np.sum(blocks(diff) ** 2, axis=(3, 4))          # [B, H, nblk]
+    r2 = np.sum(blocks(ref) ** 2, axis=(3, 4))
+    rows = np.minimum(GRAD_BLOCK_ROWS, N - GRAD_BLOCK_ROWS * np.arange(nblk))   # [nblk]
+    slice_den = np.sqrt(r2.sum(axis=2))                   # [B, H]
+    slice_err = np.sqrt(e2.sum(axis=2))
+    slice_rel = np.where(slice_den > 0, slice_err / np.where(slice_den > 0, slice_den, 1.0), slice_err)
+    bound = GRAD_BLOCK_RTOL * np.sqrt(r2) + GRAD_BLOCK_FLOOR * slice_den[:, :, None] * np.sqrt(rows / N)
+    ratio = np.where(bound > 0, np.sqrt(e2) / np.where(bound > 0, bound, 1.0), np.where(e2 > 0, np.inf, 0.0))
+    return slice_rel, ratio
+
+
+def check_grad_local(name, got, ref):
+    slice_rel, ratio = grad_local_errors(got, ref)
+    b, h = np.unravel_index(np.argmax(slice_rel), slice_rel.shape)
+    assert slice_rel[b, h] <= GRAD_RTOL, \
+        f"{name}: (batch {b}, head {h}) norm-relative error {slice_rel[b, h]:.3e} > {GRAD_RTOL}"
+    b, h, k = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio[b, h, k] <= 1.0, \
+        f"{name}: (batch {b}, head {h}) rows {k * GRAD_BLOCK_ROWS}..{(k + 1) * GRAD_BLOCK_ROWS - 1} " \
+        f"error {ratio[b, h, k]:.2f}x its bound"
 
 
 def mask_pair(kind, B, Nq, Nk, window=0, prefix=0, doc_seed=None):
