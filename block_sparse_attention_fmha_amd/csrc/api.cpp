@@ -180,6 +180,9 @@ AttnParams attn_params(const fmha_fwd_args* a) {
   p.scale = a->scale;
   p.scale_log2 = a->scale * fmha::kLog2e;
   p.softcap = a->softcap;
+  p.cap_k1 = a->softcap > 0.0f ? a->scale * 2.0f * fmha::kLog2e / a->softcap : 0.0f;
+  p.cap_u = a->softcap * fmha::kLog2e;
+  p.cap_fixed = (a->softcap > 0.0f && a->bias_slope == 0.0f && 2.0f * p.cap_u <= 100.0f) ? 1 : 0;
   p.bias_log2 = a->bias_slope * fmha::kLog2e;
   p.mask = mask_params(a->mask);
   // longest-first query-tile order pays off when tiles carry different key counts

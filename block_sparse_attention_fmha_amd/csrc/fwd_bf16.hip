@@ -151,7 +151,7 @@ void fwd_bf16_kernel(const AttnParams p) {
   f32x16 o[DV / 32];
 #pragma unroll
   for (int i = 0; i < DV / 32; ++i) o[i] = f32x16{};
-  float m_run = kNegInf, l_run = 0.0f;
+  float m_run = (SOFTCAP && !BIAS && DQK <= 128 && p.cap_fixed) ? p.cap_u : kNegInf, l_run = 0.0f;
   const float c_eff = (SOFTCAP || BIAS) ? 1.0f : p.scale_log2;
   const int prow = swap_bits23(lq);
   const int qw = q0 + 32 * w;
@@ -210,7 +210,10 @@ void fwd_bf16_kernel(const AttnParams p) {
     pipelined_matrix<4 * (DV / 32), DQK / 16, SM::VP, SM::KP, 2>(v0, k0, do_acc, do_s, o, pb, s, qf);
   };
 
-  auto vector = [&](int ts) {
+  // FIXED: softcap without bias, with the capped score's upper bound cap_u as a fixed
+  // softmax maximum (see cap_fixed): no row max and no rescale, P = exp2(u - cap_u)
+  auto vector_body = [&](auto fixed_c, int ts) __attribute__((always_inline)) {
+    constexpr bool FIXED = decltype(fixed_c)::value;
     const int n0 = seq.start(ts, LISTS);
     bool need = n0 > need_above || n0 < need_below;
     bool elem = true, hide = false;
@@ -233,6 +236,14 @@ void fwd_bf16_kernel(const AttnParams p) {
           const float t = dq - (float)(32 * kb + 16 * (r >> 3) + (r & 7));
           s[kb][r] = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(t));
         }
+    } else if constexpr (FIXED) {
+      // u - cap_u = -2 cap_u r, r = 1 / (exp(2 y) + 1)
+      const float k2 = -2.0f * p.cap_u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = fast_rcp(fast_exp2(s[kb][r] * p.cap_k1) + 1.0f) * k2;
     } else if constexpr (SOFTCAP || BIAS) {
       const int jb = opaque_int(n0 + 8 * g);
 #pragma unroll
@@ -253,20 +264,22 @@ void fwd_bf16_kernel(const AttnParams p) {
     // wave raised its running max. O already holds every P V up to tile ts - 1.
     // row max as a shallow tree (short dependency chains: this phase has one wave per
     // SIMD, so latency, not issue rate, bounds it)
-    float mt = tree_max32(s);
-    mt = pair_max(mt) * c_eff;
-    // lazy rescale: keep a stale running max until some row's max exceeds it by more
-    // than kRescaleLog2, so p = exp2(s - m) <= 2^kRescaleLog2 and the rescale runs only
-    // on large jumps (usually just the first tile); O and l always share the same m
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.0f : m_new));
-      l_run *= alpha;
+    if constexpr (!FIXED) {
+      float mt = tree_max32(s);
+      mt = pair_max(mt) * c_eff;
+      // lazy rescale: keep a stale running max until some row's max exceeds it by more
+      // than kRescaleLog2, so p = exp2(s - m) <= 2^kRescaleLog2 and the rescale runs only
+      // on large jumps (usually just the first tile); O and l always share the same m
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.0f : m_new));
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DV / 32; ++db)
+        for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_new;
+      }
     }
     const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
     // four independent partial row sums of the fp32 probabilities (plain adds: the packed
@@ -279,8 +292,10 @@ void fwd_bf16_kernel(const AttnParams p) {
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
+          const float p0 = FIXED ? fast_exp2(s[kb][8 * hh + 2 * e])
+                                 : fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
+          const float p1 = FIXED ? fast_exp2(s[kb][8 * hh + 2 * e + 1])
+                                 : fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
           pk[e] = pack_bf16x2(p0, p1);
           ls[e] = (kb == 0 && hh == 0) ? p0 + p1 : ls[e] + (p0 + p1);   // no 0 + x: it does not fold
         }
@@ -288,6 +303,16 @@ void fwd_bf16_kernel(const AttnParams p) {
       }
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  constexpr bool CAN_FIX = SOFTCAP && !BIAS && DQK <= 128;   // (the wider head has no registers for a second body)
+  auto vector = [&](int ts) __attribute__((always_inline)) {
+    if constexpr (CAN_FIX) {
+      if (p.cap_fixed) {
+        vector_body(IntC<1>{}, ts);
+        return;
+      }
+    }
+    vector_body(IntC<0>{}, ts);
   };
 
   // issue tile t + NST - 2 (called at the start of the wave's vector phase of step t)

@@ -85,6 +85,10 @@ struct AttnParams {
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   float softcap;      // > 0: tanh softcap
+  float cap_k1;       // softcap: scale * 2 log2(e) / softcap (raw score -> log2 of exp(2 y))
+  float cap_u;        // softcap: softcap * log2(e) (the capped score's log2-unit limit)
+  int cap_fixed;      // softcap without bias and 2 cap_u <= 100: the forward may use cap_u as
+                      // a fixed softmax maximum (every exp2(u - cap_u) lies in [2^-100, 1])
   float bias_log2;    // relative-bias slope * log2(e)
   MaskParams mask;
   ListParams lists;
@@ -283,18 +287,22 @@ __device__ __forceinline__ int list_entry(const int* idx, int e, int n_cols) {
 // Score transform applied to the scaled score x = scale * <q, k> (softcap, then bias).
 // Returns the final score in log2 units; `dcap` receives d(softcap(x))/dx = 1 - tanh^2
 // (1 without softcap), the factor the backward applies to dS.
+// Softcap: with y = x / softcap, tanh(y) = 1 - 2 r, r = 1 / (exp(2 y) + 1), so the capped
+// score in log2 units is softcap log2(e) (1 - 2 r) = cap_u - 2 cap_u r: one multiply, the
+// exp2, an add, the reciprocal and one fma per score, the constants folded on the host
+// (exp(2 y) = inf gives r = 0, tanh = 1; exp(2 y) = 0 gives r = 1, tanh = -1).
 template <bool SOFTCAP, bool BIAS>
 __device__ __forceinline__ float score_log2_d(float raw, const AttnParams& p, int i, int j, float& dcap) {
-  float x = raw * p.scale;
+  float u;
   dcap = 1.0f;
   if constexpr (SOFTCAP) {
-    // tanh(y) = 1 - 2 / (exp(2 y) + 1), y = x / softcap
-    const float e = fast_exp2(x * (2.0f * kLog2e / p.softcap));
-    const float th = 1.0f - 2.0f * fast_rcp(e + 1.0f);
-    x = p.softcap * th;
-    dcap = 1.0f - th * th;
+    const float r = fast_rcp(fast_exp2(raw * p.cap_k1) + 1.0f);
+    u = __builtin_fmaf(r, -2.0f * p.cap_u, p.cap_u);
+    const float th = __builtin_fmaf(r, -2.0f, 1.0f);
+    dcap = __builtin_fmaf(-th, th, 1.0f);
+  } else {
+    u = raw * p.scale_log2;
   }
-  float u = x * kLog2e;
   if constexpr (BIAS) u += p.bias_log2 * (float)abs(i - j);
   return u;
 }

@@ -56,6 +56,8 @@ SMALL = [
     (2, 512, 512, 2, 128, 128, "block_diagonal", 0, 0, 0.0, -0.01),
     (1, 255, 385, 2, 192, 128, "causal", 0, 0, 0.0, 0.0),      # MLA-shaped heads
     (1, 200, 200, 2, 128, 128, "none", 0, 0, 5.0, -0.05),
+    (1, 300, 300, 2, 128, 128, "causal", 0, 0, 30.0, 0.0),     # softcap, fixed softmax maximum
+    (1, 300, 300, 2, 128, 128, "none", 0, 0, 50.0, 0.0),       # softcap above that path's limit
     (1, 1, 1000, 4, 128, 128, "causal", 0, 0, 0.0, 0.0),       # single decode query
     (1, 1000, 1, 2, 64, 64, "none", 0, 0, 0.0, 0.0),
 ]
@@ -65,6 +67,26 @@ SMALL = [
 def test_fwd_bf16_small(case):
     B, Nq, Nk, H, Dqk, Dv, kind, W, P, cap, slope = SMALL[case]
     _case(synth.case_seed(9, case), B, Nq, Nk, H, Dqk, Dv, "bf16", kind, W, P, cap, slope)
+
+
+def test_fwd_bf16_softcap_saturated_rows():
+    """Softcap 30 with every score far below -30 before the cap: each row's capped scores
+    all sit near -30, so every probability is near 2^-86.6 relative to the cap, the
+    smallest the fixed-maximum softmax produces; O must still be the visible keys'
+    weighted mean (nearly the plain mean of V)."""
+    q, k, v = synth.attention_inputs(synth.case_seed(9, 60), 1, 200, 200, 2, 128, 128, "bf16")
+    def shifted(t, shift):
+        x = np.float32(shift) + np.float32(0.25) * t.values
+        bits = synth.bf16_bits(x)
+        return synth.Tensor(synth.bf16_bits_to_f32(bits), bits, "bf16")
+    q, k = shifted(q, 4.0), shifted(k, -4.0)      # raw scores near -128 * 16 = -2048
+    for kind in ("none", "causal"):
+        om, gm = mask_pair(kind, 1, 200, 200)
+        announce(f"fwd bf16 softcap 30 saturated mask={kind}")
+        out, lse = run_fwd(to_dev(q), to_dev(k), to_dev(v), gm, softcap=30.0)
+        o_ref, l_ref = oracle.forward(q.values, k.values, v.values, softcap=30.0, mask=om)
+        check_bf16("O", host(out), o_ref)
+        check_bf16("LSE", host(lse), l_ref)
 
 
 def test_fwd_bf16_empty_keys_and_queries():
