@@ -429,6 +429,216 @@ def all_configs_report(oracle_too: bool = True):
         del q, k, v, do, out, lse, dq, dk, dv_, ws
 
 
+# ---------------------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/*.md) from the databases of the commands below, which
+# `--summarize-profiles DIR` reads from DIR/{trace,fetch,write,sq1,sq2}/run_results.db
+# (and DIR/bench_all.log, the `--all-configs` line of the same box, if present).
+
+PROFILE_CMDS = {
+    "trace": "timeout -k 10 240 rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/trace -o run -- "
+             "python3 $R/bench.py --profile --steps 5 --warmup 2",
+    "fetch": "timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o run -- "
+             "python3 $R/bench.py --profile --steps 2 --warmup 1",
+    "write": "timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o run -- "
+             "python3 $R/bench.py --profile --steps 2 --warmup 1",
+    "sq1": "timeout -s KILL 180 rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+           "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+           "GRBM_GUI_ACTIVE -d $R/gpurun_out/prof/sq1 -o run -- python3 $R/bench.py --profile --steps 1 --warmup 1",
+    "sq2": "timeout -s KILL 180 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 "
+           "SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_LDS_DATA_FIFO_FULL GRBM_GUI_ACTIVE "
+           "-d $R/gpurun_out/prof/sq2 -o run -- python3 $R/bench.py --profile --steps 1 --warmup 1",
+}
+PROFILE_PRE = "R=$PWD; cd /tmp; export TMPDIR=/tmp"
+PROFILE_COPY = "__amd_rocclr_copyBuffer"
+PROFILE_HEAD = ["fwd_bf16_kernel<128, 128, false, false, false>", "bwd_preprocess_kernel<128>",
+                "bwd_dkdv_kernel<128, 128, false, false, false>", "bwd_dq_kernel<128, 128, false, false, false>"]
+# (row label, kernel, which of its dispatches: (part, parts) of them in launch order)
+PROFILE_OTHER = [
+    ("split-KV partial, 32 K/V heads", "splitkv_partial_kernel<128>", (0, 1)),
+    ("split-KV on the matrix cores, 8 K/V heads", "splitkv_mfma_kernel<128>", (0, 2)),
+    ("split-KV on the matrix cores, 1 K/V head", "splitkv_mfma_kernel<128>", (1, 2)),
+    ("split-KV combine (all three)", "splitkv_combine_kernel<128>", (0, 1)),
+    ("fp32 wide-head forward", "fwd_f32_kernel<1024, 128>", (0, 1)),
+    ("block-sparse forward", "fwd_bf16_kernel<128, 128, true, false, true>", (0, 1)),
+    ("block-mask build, forward lists", "classify_kernel<false>", (0, 1)),
+    ("block-mask build, transposed lists", "classify_kernel<true>", (0, 1)),
+]
+
+
+def _short_kernel(name: str) -> str:
+    import re
+    n = re.sub(r"^void ", "", name)
+    n = n.replace("fmha::(anonymous namespace)::", "")
+    return re.sub(r"\([^<>]*\)$", "", n).strip()
+
+
+def _dispatch_part(values_by_dispatch, part, parts, what):
+    """The values of one contiguous part of a kernel's dispatches, in launch order."""
+    keys = sorted(values_by_dispatch)
+    if not keys or len(keys) % parts:
+        raise SystemExit(f"profile summary: {what}: {len(keys)} dispatches, not a multiple of {parts}")
+    n = len(keys) // parts
+    return [values_by_dispatch[k] for k in keys[part * n:(part + 1) * n]]
+
+
+def summarize_profiles(src: str, out_dir: str):
+    import sqlite3
+    need = {k: os.path.join(src, k, "run_results.db") for k in ("trace", "fetch", "write", "sq1", "sq2")}
+    for k, f in need.items():
+        if not os.path.exists(f):
+            raise SystemExit(f"profile summary: missing {f} (the `{k}` pass)")
+
+    con = sqlite3.connect(need["trace"])
+    trace = {}
+    for i, (name, start, end) in enumerate(con.execute("select name, start, end from kernels order by start")):
+        trace.setdefault(_short_kernel(name), {})[i] = (end - start) / 1000.0
+    total_us = sum(sum(v.values()) for v in trace.values())
+
+    def counters(db):
+        c = sqlite3.connect(db)
+        d = {}
+        for k, cn, v, disp in c.execute("select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+            row = d.setdefault(_short_kernel(k), {}).setdefault(cn, {})
+            row[disp] = row.get(disp, 0.0) + v
+        return d
+
+    fetch, write, sq1, sq2 = (counters(need[k]) for k in ("fetch", "write", "sq1", "sq2"))
+
+    def require(table, kernel, what):
+        if kernel not in table:
+            raise SystemExit(f"profile summary: kernel `{kernel}` has no {what} row (names seen: "
+                             f"{', '.join(sorted(table))})")
+        return table[kernel]
+
+    def trace_stats(kernel, part=(0, 1)):
+        v = _dispatch_part(require(trace, kernel, "kernel-trace"), *part, what=kernel)
+        last = v[-5:]
+        return len(v), sum(v) / len(v), sum(last) / len(last), sum(v)
+
+    def counter(table, kernel, cname, part=(0, 1), what="counter"):
+        row = require(table, kernel, what)
+        if cname not in row:
+            raise SystemExit(f"profile summary: `{kernel}` lacks {cname}")
+        v = _dispatch_part(row[cname], *part, what=f"{kernel} {cname}")
+        return sum(v) / len(v)
+
+    fscale = 512 * 1024 / counter(fetch, PROFILE_COPY, "FETCH_SIZE", what="FETCH_SIZE")
+    wscale = 512 * 1024 / counter(write, PROFILE_COPY, "WRITE_SIZE", what="WRITE_SIZE")
+    src_hash = kernel_source_hash()
+    hashline = (f"Kernel sources sha256: `{src_hash}` (the kernels these numbers were taken with; bench.py "
+                f"reports the traffic only while the sources hash to this value).")
+    note = ("`bench.py --profile` runs the warm-up and timed fwd+bwd steps of the causal bf16 B=1 H=16 "
+            "Nq=Nk=16384 D=128 workload, then the same number of launches each of the split-KV decode "
+            "(B=8 H=32 Nq=1 Nk=32768 D=128, 16 splits; with 32, then 8, then 1 K/V heads), the fp32 wide-head "
+            "forward (B=4 H=8 N=512 D=1024) and the block-sparse causal forward (B=2 H=8 N=8192 D=128, "
+            "128x128 tiles, relative bias) with its block-mask build, then one plain 512 MiB device copy.")
+    calib = (f"Calibration: a plain device copy of 512 MiB (`{PROFILE_COPY}`, 512 MiB read + 512 MiB written) "
+             f"reads FETCH_SIZE = {512 * 1024 / fscale:.0f} KiB and WRITE_SIZE = {512 * 1024 / wscale:.0f} KiB, "
+             f"so the scale factors are **fetch x{fscale:.3f}, write x{wscale:.3f}**.")
+    bench_note = ""
+    bl_path = os.path.join(src, "bench_all.log")
+    if os.path.exists(bl_path):
+        lines = [ln for ln in open(bl_path).read().splitlines() if ln.startswith("{\"metric\"")]
+        if lines:
+            bl = json.loads(lines[-1])
+            kk = bl["kernels"]
+            bench_note = (f"Same box, same call, `python3 bench.py --all-configs` (HIP events on the launch stream, "
+                          f"{bl['steps']} timed steps): fwd {kk['fwd_bf16']['ms'] * 1000:.0f} µs, dK/dV "
+                          f"{kk['bwd_dkdv']['ms'] * 1000:.0f} µs, dQ {kk['bwd_dq']['ms'] * 1000:.0f} µs, preprocess "
+                          f"{kk['bwd_preprocess']['ms'] * 1000:.0f} µs per launch; {bl['value']} TFLOP/s for the step.")
+
+    TRH = ["| kernel | calls | avg µs (all) | avg µs (last 5) | total µs | % of traced GPU time |",
+           "|---|---|---|---|---|---|"]
+    HBH = ["| kernel | FETCH_SIZE KiB/dispatch (raw avg) | scaled read MiB | WRITE_SIZE KiB/dispatch | "
+           "scaled write MiB | HBM MiB per launch |", "|---|---|---|---|---|---|"]
+    SQH = ["| kernel | MFMA insts | VALU insts | VALU/MFMA | TRANS/MFMA | SALU/MFMA | LDS insts | MFMA busy | "
+           "LDS bank-conflict cycles / LDS active |", "|---|---|---|---|---|---|---|---|---|"]
+
+    def trace_row(label, kernel, part=(0, 1)):
+        n, avg, last, tot = trace_stats(kernel, part)
+        return f"| `{label}` | {n} | {avg:.1f} | {last:.1f} | {tot:.1f} | {100 * tot / total_us:.1f} |"
+
+    def hbm(kernel, part=(0, 1)):
+        f = counter(fetch, kernel, "FETCH_SIZE", part, "FETCH_SIZE")
+        w = counter(write, kernel, "WRITE_SIZE", part, "WRITE_SIZE")
+        return f, w, (f * fscale + w * wscale) / 1024
+
+    def hbm_row(label, kernel, part=(0, 1)):
+        f, w, t = hbm(kernel, part)
+        return f"| `{label}` | {f:.0f} | {f * fscale / 1024:.1f} | {w:.0f} | {w * wscale / 1024:.1f} | {t:.1f} |"
+
+    def sq_row(label, kernel, part=(0, 1), mfma_cycles=32):
+        c = lambda t, n: counter(t, kernel, n, part, "SQ")
+        mf, va = c(sq2, "SQ_INSTS_MFMA"), c(sq2, "SQ_INSTS_VALU")
+        busy = c(sq1, "SQ_VALU_MFMA_BUSY_CYCLES") / (c(sq1, "GRBM_GUI_ACTIVE") / 8 * 1024)
+        bank = c(sq1, "SQ_LDS_BANK_CONFLICT") / max(1.0, c(sq1, "SQ_LDS_IDX_ACTIVE"))
+        r = lambda x: f"{x / mf:.2f}" if mf else "-"
+        return (f"| `{label}` | {mf:.4g} | {va:.4g} | {r(va)} | {r(c(sq2, 'SQ_INSTS_VALU_TRANS_F32'))} | "
+                f"{r(c(sq2, 'SQ_INSTS_SALU'))} | {c(sq2, 'SQ_INSTS_LDS'):.4g} | {busy:.3f} | {bank:.3f} |")
+
+    os.makedirs(out_dir, exist_ok=True)
+    cmd = lambda *ks: ["```", *(PROFILE_CMDS[k] for k in ks), "```"]
+    head_t = [trace_row(k, k) for k in PROFILE_HEAD] + [trace_row(PROFILE_COPY, PROFILE_COPY)]
+    with open(os.path.join(out_dir, "fwd_bwd_causal_b1h16n16384d128_trace.md"), "w") as fh:
+        fh.write("\n".join([
+            "# Kernel trace: causal bf16 fwd+bwd, B=1 H=16 Nq=Nk=16384 D=128", "",
+            f"Command (on the MI355X box, from the repository root, `{PROFILE_PRE}`); summary written by "
+            f"`python3 bench.py --summarize-profiles gpurun_out/prof`:", "", *cmd("trace"), "",
+            f"{note} {hashline}", "", bench_note, "", *TRH, *head_t, ""]))
+    with open(os.path.join(out_dir, "fwd_bwd_causal_b1h16n16384d128_hbm_counters.md"), "w") as fh:
+        fh.write("\n".join([
+            "# HBM traffic counters: causal bf16 fwd+bwd, B=1 H=16 Nq=Nk=16384 D=128", "",
+            f"Commands (same setup as the kernel trace, `{PROFILE_PRE}`; one counter per pass):", "",
+            *cmd("fetch", "write"), "", hashline, "", calib, "", *HBH, *(hbm_row(k, k) for k in PROFILE_HEAD), ""]))
+    with open(os.path.join(out_dir, "fwd_bwd_causal_b1h16n16384d128_sq_counters.md"), "w") as fh:
+        fh.write("\n".join([
+            "# SQ counters: causal bf16 fwd+bwd, B=1 H=16 Nq=Nk=16384 D=128", "",
+            f"{hashline} Commands (on the MI355X box, from the repository root, `{PROFILE_PRE}`), one pass each:",
+            "", *cmd("sq1", "sq2"), "",
+            "Values are per dispatch (averaged). GRBM_GUI_ACTIVE is summed over the 8 XCDs (per-XCD busy cycles = "
+            "value / 8). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI_ACTIVE / 8 x 1024 SIMDs); one 32x32x16 bf16 "
+            "MFMA counts 32 busy cycles. SQ_INSTS_VALU includes the MFMA instructions.", "",
+            *SQH, *(sq_row(k, k) for k in PROFILE_HEAD), ""]))
+
+    # other workloads: bandwidth / rate lines from the trace (average of the last 5 launches)
+    lines = []
+    for (label, kernel, part), hkv in zip(PROFILE_OTHER[:3], (32, 8, 1)):
+        byts = 2 * 8 * 32768 * hkv * 128 * 2
+        _, _, us, _ = trace_stats(kernel, part)
+        gbs = byts / (us * 1e-6) / 1e9
+        f, w, t = hbm(kernel, part)
+        where = ("" if gbs <= PEAK_HBM_GBS else
+                 " — above the HBM peak: part of the K/V was served from the 256 MB last-level cache, "
+                 "since the same K/V is read on every launch")
+        lines.append(f"- {label}: {byts / 2**20:.0f} MiB of K/V per launch in {us:.1f} µs = **{gbs:.0f} GB/s** "
+                     f"({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s){where}; HBM counters {t:.1f} MiB per launch.")
+    _, _, us, _ = trace_stats("fwd_f32_kernel<1024, 128>")
+    f32 = 2.0 * 4 * 8 * 2048 * 512 * 512
+    lines.append(f"- fp32 wide head: {f32 / 1e9:.1f} GFLOP in {us:.1f} µs = **{f32 / us / 1e6:.1f} TFLOP/s** "
+                 f"({100 * f32 / us / 1e6 / PEAK_FP32_TFLOPS:.1f}% of the {PEAK_FP32_TFLOPS} TFLOP/s fp32 MFMA peak).")
+    other_t = [trace_row(l, k, p) for l, k, p in PROFILE_OTHER]
+    other_h = [hbm_row(l, k, p) for l, k, p in PROFILE_OTHER]
+    other_s = [sq_row(l, k, p) for l, k, p in PROFILE_OTHER]
+    with open(os.path.join(out_dir, "splitkv_fp32wide_blocksparse_kernels.md"), "w") as fh:
+        fh.write("\n".join([
+            "# Kernel trace and counters: split-KV decode (all and grouped K/V heads), fp32 wide-head forward, "
+            "block-sparse forward", "",
+            "Workloads: split-KV decode bf16 B=8 H=32 Nq=1 Nk=32768 D=128, 16 splits (partial + combine) with 32 "
+            "K/V heads, then with 8 K/V heads shared by groups of 4 query heads, then with one K/V head for all 32 "
+            "(multi-query); the grouped launches run `splitkv_mfma_kernel<128>` and are split here by launch order "
+            "(8-head launches first); fp32 forward B=4 H=8 N=512 D=1024, no mask; block-sparse bf16 forward B=2 H=8 "
+            "N=8192 D=128, causal element mask on 128x128 sparse tiles, relative bias -0.01|i-j|, with "
+            "`build_block_mask` (`classify_kernel<false>` forward lists, `<true>` transposed lists).", "",
+            f"Same runs as the fwd+bwd profiles (`{PROFILE_PRE}`), summarised by "
+            f"`python3 bench.py --summarize-profiles gpurun_out/prof`, which stops with an error when a kernel "
+            f"listed here has no row:", "", *cmd("trace", "fetch", "write", "sq1", "sq2"), "",
+            note, "", hashline, "", calib, "", "## Kernel trace", "", *TRH, *other_t, "", *lines, "",
+            "## HBM traffic", "", *HBH, *other_h, "", "## SQ counters", "",
+            "(MFMA busy as in the fwd+bwd SQ summary; the fp32 kernel's 32x32x2 MFMA counts 64 busy cycles, so its "
+            "busy fraction is twice the instruction count's share.)", "", *SQH, *other_s, ""]))
+    print(f"wrote 4 summaries to {out_dir}")
+
+
 def visible_pairs(kind, n, window, prefix, docs):
     """Visible (i, j) pairs summed over the batch rows (Nq = Nk = n)."""
     import numpy as np
@@ -454,10 +664,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write profiles/*.md from the rocprofv3 databases under DIR (no GPU needed)")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3: run --steps hot-path steps, then one plain 512 MiB device copy "
                          "(counter calibration), and exit without the JSON line")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU only: the library has no multi-GPU path "
                          "(heads or key ranges would be sharded across GPUs; not built). Use --gpus 1.\n")
