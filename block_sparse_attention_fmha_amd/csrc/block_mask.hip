@@ -11,13 +11,15 @@
 // counted and compared with the tile's in-bounds size (0 = empty, all = full, else
 // partial). For the band masks (causal, sliding window, prefix-LM: the visible keys of a
 // row are one interval) each thread counts whole tiles in closed form, row by row. For
-// the block-diagonal mask the workgroup stages the document ids of the column axis in
-// LDS (in chunks); every thread takes one row element and a slice of the column tiles,
-// counts the matching ids of each tile, and the counts are summed exactly in one 64-bit
-// LDS counter per tile. The classes go to LDS and one thread compacts them into ascending lists
-// (slots past the count are -1). The transposed lists are produced by the same kernel
-// with the roles of the two axes swapped, so both orientations come from one
-// classification.
+// the block-diagonal mask the visible pairs of a tile are sum over documents d of
+// (row elements in d) x (column elements in d): the workgroup builds its tile row's
+// histogram of document ids in an LDS hash table, then every column element adds its
+// document's row count to its tile's 64-bit LDS counter (integer sums: exact in any
+// order). Tile rows longer than the table holds fall back to comparing every row element
+// with every staged column id. The classes go to LDS and the workgroup compacts them into
+// ascending lists with a prefix sum (slots past the count are -1). The transposed lists
+// are produced by the same kernel with the roles of the two axes swapped, so both
+// orientations come from one classification.
 #include "kernel_common.h"
 #include "launch.h"
 
@@ -27,6 +29,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kIdChunk = 8192;     // document ids staged in LDS at a time
 constexpr int kMaxCounted = 4096;  // tiles per row counted in one pass (one 64-bit LDS counter each)
+// histogram table of a tile row's document ids: 64-bit slots (0 = free, else 2^32 | id) and
+// 32-bit counts, in the id-staging region; at most half full, so probing always ends
+constexpr int kTable = 2048;
+constexpr int kMaxHistRows = kTable / 2;
+static_assert(kTable * 12 <= kIdChunk * 4, "the table lives in the id-staging region");
 
 // dynamic LDS layout: tile classes (n_cols bytes), id chunk, 64-bit counters
 __host__ __device__ constexpr int ids_offset(int n_cols) { return (n_cols + 15) / 16 * 16; }
@@ -61,7 +68,61 @@ void classify_kernel(const MaskParams m, int Hm, int nq, int nk, int tile_m, int
   const int row = blockIdx.x % n_rows;
   const int bhm = blockIdx.x / n_rows;
   const int b = bhm / Hm;
-  if (m.kind == kMaskBlockDiag) {
+  if (m.kind == kMaskBlockDiag && (TRANSPOSED ? min(tile_n, nk - row * tile_n) : min(tile_m, nq - row * tile_m)) <= kMaxHistRows) {
+    // ---- histogram path
+    unsigned long long* slot = (unsigned long long*)(cls + ids_offset(n_cols));
+    int* tcnt = (int*)(slot + kTable);
+    unsigned long long* cnt = (unsigned long long*)(cls + cnt_offset(n_cols));
+    const int* rdoc = TRANSPOSED ? m.doc_k + (int64_t)b * nk : m.doc_q + (int64_t)b * nq;
+    const int* cdoc = TRANSPOSED ? m.doc_q + (int64_t)b * nq : m.doc_k + (int64_t)b * nk;
+    const int rt = TRANSPOSED ? tile_n : tile_m, ct = TRANSPOSED ? tile_m : tile_n;
+    const int rn = TRANSPOSED ? nk : nq, cn = TRANSPOSED ? nq : nk;
+    const int r0 = row * rt, r1 = tile_end(r0, rt, rn), nr = r1 - r0;
+    const int t = threadIdx.x;
+    auto home = [](int id) { return (int)(((uint32_t)id * 0x9E3779B1u) >> 21); };   // 11 bits = kTable
+    for (int e = t; e < kTable; e += kThreads) {
+      slot[e] = 0ull;
+      tcnt[e] = 0;
+    }
+    __syncthreads();
+    for (int i = r0 + t; i < r1; i += kThreads) {
+      const int id = rdoc[i];
+      const unsigned long long tag = (1ull << 32) | (uint32_t)id;
+      int h = home(id);
+      for (;;) {
+        const unsigned long long old = atomicCAS(&slot[h], 0ull, tag);
+        if (old == 0ull || old == tag) break;
+        h = (h + 1) & (kTable - 1);
+      }
+      atomicAdd(&tcnt[h], 1);
+    }
+    for (int g0 = 0; g0 < n_cols; g0 += kMaxCounted) {
+      const int g1 = min(n_cols, g0 + kMaxCounted);
+      __syncthreads();   // table complete / the previous pass's classes written
+      for (int c = t; c < g1 - g0; c += kThreads) cnt[c] = 0;
+      __syncthreads();
+      const int a0 = g0 * ct, a1 = tile_end((g1 - 1) * ct, ct, cn);   // column elements covered
+      for (int j = a0 + t; j < a1; j += kThreads) {
+        const int id = cdoc[j];
+        const unsigned long long tag = (1ull << 32) | (uint32_t)id;
+        int h = home(id), c = 0;
+        for (;;) {
+          const unsigned long long v = slot[h];
+          if (v == tag) { c = tcnt[h]; break; }
+          if (v == 0ull) break;
+          h = (h + 1) & (kTable - 1);
+        }
+        if (c) atomicAdd(&cnt[j / ct - g0], (unsigned long long)c);
+      }
+      __syncthreads();
+      for (int col = g0 + t; col < g1; col += kThreads) {
+        const int c0 = col * ct, c1 = tile_end(c0, ct, cn);
+        const unsigned long long vis = cnt[col - g0];
+        const unsigned long long all = (unsigned long long)nr * (unsigned long long)(c1 - c0);
+        cls[col] = (vis == 0) ? 0 : (vis == all ? 2 : 1);
+      }
+    }
+  } else if (m.kind == kMaskBlockDiag) {
     int* ids = (int*)(cls + ids_offset(n_cols));
     unsigned long long* cnt = (unsigned long long*)(cls + cnt_offset(n_cols));
     // row axis: the grid row's tile; column axis: the tiles being classified
@@ -121,18 +182,50 @@ void classify_kernel(const MaskParams m, int Hm, int nq, int nk, int tile_m, int
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int64_t base = (int64_t)blockIdx.x * n_cols;
+  // ---- compaction: thread t takes the contiguous columns [t per, (t + 1) per), counts its
+  // partial and full tiles, and an exclusive prefix sum over the threads (in thread order,
+  // so the lists stay ascending) gives where its entries go
+  {
+    const int t = threadIdx.x, l = t & 63, w = t >> 6;
+    const int per = (n_cols + kThreads - 1) / kThreads;
+    const int c0 = min(n_cols, t * per), c1 = min(n_cols, c0 + per);
     int np = 0, nf = 0;
-    for (int col = 0; col < n_cols; ++col) {
-      const unsigned char c = cls[col];
-      if (c == 1) pidx[base + np++] = col;
-      else if (c == 2) fidx[base + nf++] = col;
+    for (int col = c0; col < c1; ++col) {
+      np += cls[col] == 1;
+      nf += cls[col] == 2;
     }
-    for (int e = np; e < n_cols; ++e) pidx[base + e] = -1;
-    for (int e = nf; e < n_cols; ++e) fidx[base + e] = -1;
-    pcnt[blockIdx.x] = np;
-    fcnt[blockIdx.x] = nf;
+    // inclusive scan within the wave, then across the four waves through LDS
+    int sp = np, sf = nf;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(sp, d), uf = __shfl_up(sf, d);
+      if (l >= d) sp += up, sf += uf;
+    }
+    int* wsum = (int*)(cls + ids_offset(n_cols));   // the id / table region is free again
+    if (l == 63) {
+      wsum[2 * w] = sp;
+      wsum[2 * w + 1] = sf;
+    }
+    __syncthreads();
+    int op = sp - np, of = sf - nf, tp = 0, tf = 0;
+#pragma unroll
+    for (int v = 0; v < kThreads / 64; ++v) {
+      if (v < w) op += wsum[2 * v], of += wsum[2 * v + 1];
+      tp += wsum[2 * v];
+      tf += wsum[2 * v + 1];
+    }
+    const int64_t base = (int64_t)blockIdx.x * n_cols;
+    for (int col = c0; col < c1; ++col) {
+      const unsigned char c = cls[col];
+      if (c == 1) pidx[base + op++] = col;
+      else if (c == 2) fidx[base + of++] = col;
+    }
+    for (int e = tp + t; e < n_cols; e += kThreads) pidx[base + e] = -1;
+    for (int e = tf + t; e < n_cols; e += kThreads) fidx[base + e] = -1;
+    if (t == 0) {
+      pcnt[blockIdx.x] = tp;
+      fcnt[blockIdx.x] = tf;
+    }
   }
 }
 
