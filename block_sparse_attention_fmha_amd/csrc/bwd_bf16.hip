@@ -439,6 +439,348 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   }
 }
 
+// ------------------------------------------------------------------------------- dK / dV, query split
+// At D = 64 each MFMA carries half the work of D = 128 while the exp / dS work per score
+// is the same, and the role split above leaves every exp of a step on the P wave. There
+// the pair splits each 64-query step instead: both waves hold K and V, and each computes
+// S, dP, P and dS for its own 32 queries and accumulates its own partial dK^T and dV^T
+// (16 MFMAs and 16 exps per lane and step on each side, no P hand-over). At the end the
+// half-0 wave stores dK and the half-1 wave dV, each adding the partner's partial handed
+// over through the idle stage memory (own + other: the same sum bitwise either way).
+// Holding K, V and both accumulators fits two waves per SIMD only at D <= 64.
+template <int DQK, int DV>
+struct DkdvSplitSmem {
+  static constexpr int QPC = DualPitch<DQK>::value, OPC = DualPitch<DV>::value;
+  static constexpr int QP = QPC * 16, OP = OPC * 16;   // bytes
+  static constexpr int QB = kQS * QP, OB = kQS * OP;
+  static constexpr int LB = 1024;                      // lse2[64], D[64], 512 bytes unused
+  static constexpr int STAGE = QB + OB + LB;
+  static constexpr int NST = (4 * STAGE <= 148 * 1024) ? 4 : 3;
+  static constexpr int BYTES = NST * STAGE;
+  // closing exchange: 8 waves x the other wave's accumulator blocks x 4 KiB
+  static constexpr int XBYTES = 8 * ((DQK > DV ? DQK : DV) / 32) * 4096;
+  static_assert(XBYTES <= BYTES, "the closing exchange reuses the stages");
+};
+
+// One matrix phase of the query-split dK / dV pass (items as in dq_matrix):
+//   NDV items dv[i / 2] += dO^T P (A: transposed dO reads at t_o, queries + 16 (i % 2), head
+//     dims + 32 (i / 2); B = pb[i % 2]), NDK items dk[..] += Q^T dS (transposed Q reads at
+//     t_q; B = dsb), NS items s += Q K^T (16-byte Q row reads at r_q + 32 ks; B = kf[ks]),
+//     NP items dp += dO V^T (dO row reads at r_o + 32 ks; B = vf[ks]).
+template <int NDV, int NDK, int NS, int NP, int QP, int OP, int AHEAD>
+__device__ __forceinline__ void dkdv_matrix(const char* t_o, const char* t_q, const char* r_q, const char* r_o,
+                                            bool do_acc, bool do_s, f32x16 (&dv)[NDV / 2], f32x16 (&dk)[NDK / 2],
+                                            const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2], f32x16& s, f32x16& dp,
+                                            const bf16x8 (&kf)[NS], const bf16x8 (&vf)[NP]) {
+  constexpr int NA = NDV + NDK, N = NA + NS + NP;
+  auto load = [&](int i) -> bf16x8 {
+    if (i < NDV) {
+      const char* tp = t_o + 16 * (i & 1) * OP + 64 * (i >> 1);
+      return join_bf16x8(lds_read_tr(tp), lds_read_tr(tp + 4 * OP));
+    }
+    if (i < NA) {
+      const int j = i - NDV;
+      const char* tp = t_q + 16 * (j & 1) * QP + 64 * (j >> 1);
+      return join_bf16x8(lds_read_tr(tp), lds_read_tr(tp + 4 * QP));
+    }
+    if (i < NA + NS) return *(const bf16x8*)(r_q + 32 * (i - NA));
+    return *(const bf16x8*)(r_o + 32 * (i - NA - NS));
+  };
+  auto run = [&](int i, const bf16x8& a) {
+    if (i < NDV) dv[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[i & 1], dv[i >> 1], 0, 0, 0);
+    else if (i < NA) dk[(i - NDV) >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[(i - NDV) & 1], dk[(i - NDV) >> 1], 0, 0, 0);
+    else if (i < NA + NS) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[i - NA], s, 0, 0, 0);
+    else dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[i - NA - NS], dp, 0, 0, 0);
+  };
+  const int first = do_acc ? 0 : NA, last = do_s ? N : NA;
+  if (do_s) {
+    s = f32x16{};
+    dp = f32x16{};
+  }
+  bf16x8 ring[AHEAD];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i >= first && i < first + AHEAD && i < last) ring[i % AHEAD] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < first || i >= last) continue;
+    __builtin_amdgcn_sched_barrier(0);
+    run(i, ring[i % AHEAD]);
+    if (i + AHEAD < last) ring[i % AHEAD] = load(i + AHEAD);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int DQK, int DV, bool LISTS, bool SOFTCAP, bool BIAS>
+__global__ __launch_bounds__(kThreads, 1)
+void bwd_dkdv_split_kernel(const BwdParams bp) {
+  using SM = DkdvSplitSmem<DQK, DV>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const AttnParams& p = bp.a;
+
+  const int bid = xcd_remap(blockIdx.x, bp.grid_padded_kv);
+  if (bid >= bp.total_work_kv) return;
+  // work item: (batch b, K/V head hk, key tile kt); grouped query heads walked in order
+  const int G = p.group > 1 ? p.group : 1;
+  const int Hkv = p.H / G;
+  const int bhk = bid / bp.n_kv_tiles;
+  const int kt = bid - bhk * bp.n_kv_tiles;
+  const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;
+  const int h0 = hk * G;
+  const int k0 = kt * kKB;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 5, lq = l & 31;
+  const int half = w >> 2;     // queries 32 half .. 32 half + 31 of every step
+  const int pair = w & 3;      // waves w and w + 4 share a SIMD and the same 32 keys
+  const SeqInfo sq = seq_info(p, b);
+  const int Nq = sq.nq, Nk = sq.nk, delta = Nk - Nq;
+  if (k0 >= Nk) return;        // packed sequences: past this one's keys (whole workgroup, no barrier yet)
+  const int kw = k0 + 32 * pair;
+  const int key = kw + lq;
+
+  const __bf16* Qg = (const __bf16*)p.q + row_base(sq, true, b, p.qs_b, p.qs_s) + h0 * p.qs_h;
+  const __bf16* Kg = (const __bf16*)p.k + row_base(sq, false, b, p.ks_b, p.ks_s) + hk * p.ks_h;
+  const __bf16* Vg = (const __bf16*)p.v + row_base(sq, false, b, p.vs_b, p.vs_s) + hk * p.vs_h;
+  const __bf16* DOg = (const __bf16*)bp.dout + row_base(sq, true, b, bp.dos_b, bp.dos_s) + h0 * bp.dos_h;
+  const char* WSg = (const char*)(bp.ws + ((int64_t)b * p.H + h0) * bp.n_qblk * 128);
+
+  // ---- query-step sequence (as in the role-split pass)
+  TileSeq<kQS> seq;
+  seq.t_lo = 0;
+  seq.ent = (const uint32_t*)(smem + SM::BYTES + 16);
+  const int mk = p.mask.kind;
+  if constexpr (!LISTS) {
+    int lo = 0, hi = Nq;
+    if (mk == kMaskCausal || mk == kMaskWindow) lo = max(0, k0 - delta);
+    if (mk == kMaskPrefix) lo = (k0 < p.mask.prefix) ? 0 : max(0, k0 - delta);
+    if (mk == kMaskWindow) hi = min(Nq, k0 + kKB - 1 - delta + p.mask.window + 1);
+    lo = min(lo, Nq);
+    seq.t_lo = lo / kQS;
+    seq.count = max(0, (hi + kQS - 1) / kQS - seq.t_lo);
+  } else {
+    const ListParams& L = p.lists;   // transposed lists: rows = key tiles
+    const int64_t row = ((int64_t)b * L.heads + ((L.heads == 1) ? 0 : h0)) * L.n_rows + k0 / L.tile_rows;
+    seq.count = build_tile_sequence<kThreads, kQS>(L, row, -1, Nq, smem + SM::BYTES, tid);
+  }
+
+  // ---- B operands of S (K) and dP (V): the lane's key, k-slot = head dim
+  bf16x8 kf[DQK / 16], vf[DV / 16];
+#pragma unroll
+  for (int ks = 0; ks < DQK / 16; ++ks)
+    kf[ks] = key < Nk ? *(const bf16x8*)(Kg + (int64_t)key * p.ks_s + 16 * ks + 8 * g) : bf16x8{};
+#pragma unroll
+  for (int ks = 0; ks < DV / 16; ++ks)
+    vf[ks] = key < Nk ? *(const bf16x8*)(Vg + (int64_t)key * p.vs_s + 16 * ks + 8 * g) : bf16x8{};
+
+  f32x16 dk[DQK / 32], dv[DV / 32];
+#pragma unroll
+  for (int i = 0; i < DQK / 32; ++i) dk[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < DV / 32; ++i) dv[i] = f32x16{};
+  f32x16 s, dp;
+  bf16x8 pb[2], dsb[2];
+  const int prow = swap_bits23(lq);
+  const int trow = 8 * g + ((l & 15) >> 2);
+  const int tcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+
+  // visible queries of the lane's key under the band masks: qlo <= i <= qhi
+  int qlo = 0, qhi = 0x3fffffff;
+  if (mk == kMaskCausal || mk == kMaskWindow || (mk == kMaskPrefix && key >= p.mask.prefix)) qlo = key - delta;
+  if (mk == kMaskWindow) qhi = key - delta + p.mask.window;
+  const uint32_t qspan = (uint32_t)qhi - (uint32_t)qlo;
+  const int kdoc = (mk == kMaskBlockDiag && key < Nk) ? p.mask.doc_k[(int64_t)b * Nk + key] : 0;
+  int need_below = INT32_MIN, need_above = INT32_MAX;
+  if (mk == kMaskCausal || mk == kMaskWindow || (mk == kMaskPrefix && kw + 31 >= p.mask.prefix))
+    need_below = kw + 31 - delta;
+  if (mk == kMaskWindow) need_above = kw - kQS + 1 - delta + p.mask.window;
+  if (mk == kMaskBlockDiag) need_below = INT32_MAX;
+
+  LdsDma<kQS, DQK, SM::QPC, kThreads> qdma;
+  LdsDma<kQS, DV, SM::OPC, kThreads> odma;
+  qdma.init(p.qs_s, tid);
+  odma.init(bp.dos_s, tid);
+  constexpr int ld_wave = 7;   // a wave with the fewest tile blocks issues the lse2 / D load
+  const int per_step = qdma.count() + odma.count() + (w == ld_wave ? 1 : 0);
+  zero_lds<kThreads>(smem, SM::NST * SM::STAGE, tid);   // defensive: every slot is loaded before it is read
+  const int Tq = seq.count;
+  auto head_step = [&](int t, int& gi) {
+    if (G == 1) {
+      gi = 0;
+      return t;
+    }
+    gi = t / Tq;
+    return t - gi * Tq;
+  };
+  auto issue_step = [&](int t) {
+    int gi;
+    const int i0 = seq.start(head_step(t, gi), LISTS);
+    char* st = smem + (t % SM::NST) * SM::STAGE;
+    qdma.issue(Qg + (int64_t)gi * p.qs_h, p.qs_s, i0, Nq, st);
+    odma.issue(DOg + (int64_t)gi * bp.dos_h, bp.dos_s, i0, Nq, st + SM::QB);
+    if (w == ld_wave)
+      dma_16b(WSg + (int64_t)gi * bp.n_qblk * 512, (uint32_t)(i0 / 64) * 512u + 16u * l, st + SM::QB + SM::OB);
+  };
+
+  const int T = G * Tq;
+  for (int t = 0; t < SM::NST - 2 && t < T; ++t) issue_step(t);
+  wait_all_vmem();
+  __syncthreads();
+
+  // Steps t = 0 .. T, two phases each; the half-1 waves run one phase behind:
+  //   half 0, step t: matrix [dV, dK of step t-1; S, dP of step t], vector P, dS of step t
+  //   half 1, step t: vector P, dS of step t-1, matrix [the same as half 0's]
+  // Stage t is read during steps t and t+1.
+  auto matrix = [&](int ts, bool do_acc, bool do_s) {
+    const int sv = ((ts - 1 + SM::NST) % SM::NST) * SM::STAGE, sc = (ts % SM::NST) * SM::STAGE;
+    const int trq = (32 * half + trow), rrq = 32 * half + prow;
+    const char* t_o = smem + opaque_int(sv + SM::QB + trq * SM::OP + tcol * 2);
+    const char* t_q = smem + opaque_int(sv + trq * SM::QP + tcol * 2);
+    const char* r_q = smem + opaque_int(sc + rrq * SM::QP + 16 * g);
+    const char* r_o = smem + opaque_int(sc + SM::QB + rrq * SM::OP + 16 * g);
+    dkdv_matrix<2 * (DV / 32), 2 * (DQK / 32), DQK / 16, DV / 16, SM::QP, SM::OP, 2>(
+        t_o, t_q, r_q, r_o, do_acc, do_s, dv, dk, pb, dsb, s, dp, kf, vf);
+  };
+
+  // P = exp2(u - lse2) and dS = P (dP - D) [x (1 - tanh^2)] of step ts into pb / dsb;
+  // reg r holds query i0 + 32 half + 16 (r / 8) + 8 g + r % 8 of the lane's key
+  auto vector = [&](int ts) {
+    int gi;
+    const int tq = head_step(ts, gi);
+    const int i0 = seq.start(tq, LISTS);
+    const float* LD = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB);
+    bool need;
+    if constexpr (LISTS) need = seq.cls(tq, 0, true) != 2u;
+    else need = i0 < need_below || i0 > need_above;
+    auto body = [&](auto test_c) {
+      constexpr int TEST = decltype(test_c)::value;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int qi = 32 * half + 16 * hh + 8 * g;
+        const f32x4 la = *(const f32x4*)(LD + qi), lb = *(const f32x4*)(LD + qi + 4);
+        const f32x4 da = *(const f32x4*)(LD + 64 + qi), db4 = *(const f32x4*)(LD + 64 + qi + 4);
+        const int qb = (TEST != kTestNone || BIAS) ? opaque_int(i0 + qi) : 0;
+        const float dij = (BIAS && !SOFTCAP) ? __int_as_float(opaque_int(__float_as_int((float)(i0 + qi - key)))) : 0.0f;
+        u32x4 pk, dk4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv[2], dsv[2];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int ee = 2 * e + z, r = 8 * hh + ee;
+            const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
+            const float dd = ee < 4 ? da[ee] : db4[ee - 4];
+            const int qidx = qb + ee;
+            float dcap = 1.0f, u;
+            if constexpr (BIAS && !SOFTCAP)
+              u = __builtin_fmaf(s[r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee));
+            else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[r], p, qidx, key, dcap);
+            else u = s[r] * p.scale_log2;
+            // rows past Nq carry lse2 = +inf, so their P is 0 whatever the test says
+            if constexpr (TEST == kTestBand) {
+              if ((uint32_t)qidx - (uint32_t)qlo > qspan) u = kNegInf;
+            } else if constexpr (TEST == kTestDoc) {
+              const int dq = p.mask.doc_q[(int64_t)b * Nq + min(qidx, Nq - 1)];
+              if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) u = kNegInf;
+            }
+            pv[z] = fast_exp2(u - lse2);
+            dsv[z] = pv[z] * dcap * (dp[r] - dd);
+          }
+          pk[e] = pack_bf16x2(pv[0], pv[1]);
+          dk4[e] = pack_bf16x2(dsv[0], dsv[1]);
+        }
+        pb[hh] = __builtin_bit_cast(bf16x8, pk);
+        dsb[hh] = __builtin_bit_cast(bf16x8, dk4);
+      }
+    };
+    if (!need) body(IntC<kTestNone>{});
+    else if (mk != kMaskBlockDiag) body(IntC<kTestBand>{});
+    else body(IntC<kTestDoc>{});
+  };
+
+  // Step t refills the stage of step t - 2 (read up to step t - 1) with step t + NST - 2,
+  // each wave's share issued at the start of its vector phase (as in the other passes)
+  auto step_begin = [&](int t) {
+    if (t + SM::NST - 2 < T) issue_step(t + SM::NST - 2);
+  };
+  auto step_end = [&](int t) {
+    const int later = min(SM::NST - 3, max(0, T - 2 - t));
+    if (later > 0) wait_vmcnt_at_most(later * per_step);
+    else wait_lds_dma();
+    __syncthreads();
+  };
+
+  if (T > 0) {
+    if (half == 0) {
+      matrix(0, false, true);
+      step_begin(0);
+      vector(0);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        matrix(t, true, true);
+        step_begin(t);
+        vector(t);
+        step_end(t);
+      }
+      matrix(T, true, false);
+      step_end(T);
+    } else {
+      step_begin(0);
+      matrix(0, false, true);
+      step_end(0);
+      for (int t = 1; t < T; ++t) {
+        step_begin(t);
+        vector(t - 1);
+        matrix(t, true, true);
+        step_end(t);
+      }
+      vector(T - 1);
+      matrix(T, true, false);
+      step_end(T);
+    }
+  }
+
+  // ---- closing exchange and epilogue: half 0 stores dK, half 1 dV; each hands the other
+  // accumulator to its partner through the (idle) stage memory and adds the partner's.
+  // Lane = key, reg r of block db <-> d = 32 db + 8 (r / 4) + 4 g + r % 4.
+  constexpr int NBM = (DQK > DV ? DQK : DV) / 32;
+  auto finish = [&](auto half_c) {
+    constexpr int HF = decltype(half_c)::value;
+    constexpr int NO = HF == 0 ? DV / 32 : DQK / 32;     // blocks handed over
+    constexpr int NK = HF == 0 ? DQK / 32 : DV / 32;     // blocks kept
+    f32x4* xo = (f32x4*)(smem + w * NBM * 4096) + l;
+    const f32x4* xi = (const f32x4*)(smem + (w ^ 4) * NBM * 4096) + l;
+#pragma unroll
+    for (int j = 0; j < NO; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x16& a = HF == 0 ? dv[j] : dk[j];
+        xo[64 * (4 * j + c)] = f32x4{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+      }
+    __syncthreads();
+    if (key >= Nk) return;
+    const bool isk = HF == 0;
+    __bf16* dst = isk ? (__bf16*)bp.dk + row_base(sq, false, b, bp.dks_b, bp.dks_s) + hk * bp.dks_h + (int64_t)key * bp.dks_s
+                      : (__bf16*)bp.dv + row_base(sq, false, b, bp.dvs_b, bp.dvs_s) + hk * bp.dvs_h + (int64_t)key * bp.dvs_s;
+    const float sc = isk ? p.scale : 1.0f;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const f32x16& a = HF == 0 ? dk[j] : dv[j];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 o = xi[64 * (4 * j + c)];
+        u32x2 v;
+        v[0] = pack_bf16x2((a[4 * c] + o[0]) * sc, (a[4 * c + 1] + o[1]) * sc);
+        v[1] = pack_bf16x2((a[4 * c + 2] + o[2]) * sc, (a[4 * c + 3] + o[3]) * sc);
+        *(u32x2*)(dst + 32 * j + 8 * c + 4 * g) = v;
+      }
+    }
+  };
+  if (half == 0) finish(IntC<0>{});
+  else finish(IntC<1>{});
+}
+
 // ------------------------------------------------------------------------------- dQ, DQK != DV
 // Used where the head dims differ (192 / 128): with Q, dO and the wider dQ^T accumulator
 // all held by each wave, the key-split pass below would exceed the register budget of two
@@ -1052,8 +1394,16 @@ hipError_t launch_passes(const BwdParams& bp, hipStream_t st) {
     if (e0 != hipSuccess) return e0;
     BwdParams kv = bp;
     kv.a.lists = bp.tlists;
-    auto kern = bwd_dkdv_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
-    const int bytes = DkdvSmem<DQK, DV>::BYTES + list_bytes(kv.a.lists, kQS);
+    // query-split pass at D <= 64 with equal head dims, role-split pass otherwise
+    void (*kern)(const BwdParams);
+    int bytes = list_bytes(kv.a.lists, kQS);
+    if constexpr (DQK == DV && DQK <= 64) {
+      kern = bwd_dkdv_split_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
+      bytes += DkdvSplitSmem<DQK, DV>::BYTES;
+    } else {
+      kern = bwd_dkdv_kernel<DQK, DV, LISTS, SOFTCAP, BIAS>;
+      bytes += DkdvSmem<DQK, DV>::BYTES;
+    }
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     if (bp.grid_padded_kv > 0) {   // no keys: no dK / dV to write
@@ -1096,6 +1446,12 @@ hipError_t dispatch(const BwdParams& bp, bool lists, bool softcap, bool bias, hi
   return bias ? launch_passes<DQK, DV, false, false, true>(bp, st) : launch_passes<DQK, DV, false, false, false>(bp, st);
 }
 
+template <int DQK, int DV>
+constexpr int dkdv_smem_bytes() {
+  if constexpr (DQK == DV && DQK <= 64) return DkdvSplitSmem<DQK, DV>::BYTES;
+  else return DkdvSmem<DQK, DV>::BYTES;
+}
+
 template <int DQK, int DV, bool LISTS>
 constexpr int dq_smem_bytes() {
   if constexpr (DQK == DV) return DqSmem<DQK, DV, LISTS>::BYTES;
@@ -1104,7 +1460,7 @@ constexpr int dq_smem_bytes() {
 
 template <int DQK, int DV>
 bool lists_fit_dims(const ListParams& fwd, const ListParams& tr) {
-  return DkdvSmem<DQK, DV>::BYTES + list_bytes(tr, kQS) <= kMaxLdsBytes &&
+  return dkdv_smem_bytes<DQK, DV>() + list_bytes(tr, kQS) <= kMaxLdsBytes &&
          dq_smem_bytes<DQK, DV, true>() + list_bytes(fwd, kKN) <= kMaxLdsBytes;
 }
 
