@@ -43,16 +43,40 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+def kernels_using_scratch(remarks: str):
+    """(kernel, what, amount) for every kernel whose resource-usage remarks show scratch
+    memory or spilled VGPRs (SGPR spills go to VGPR lanes and are not counted)."""
+    import re
+    bad, cur = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)", line)
+        if m and cur and int(m.group(2)) > 0:
+            bad.append((cur, m.group(1), int(m.group(2))))
+    return bad
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
+    else:
+        # every kernel must keep its state in registers: a kernel that spills to scratch
+        # runs many times slower, so the build stops on one (see kernels_using_scratch)
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {os.path.basename(src)} failed:\n{r.stdout}\n{r.stderr}")
+    bad = kernels_using_scratch(r.stderr)
+    if bad:
+        lines = "\n".join(f"  {k}: {what} = {n}" for k, what, n in bad)
+        raise RuntimeError(f"{os.path.basename(src)}: kernels use scratch memory:\n{lines}")
     if verbose and r.stderr.strip():
         print(r.stderr, file=sys.stderr)
     return obj
