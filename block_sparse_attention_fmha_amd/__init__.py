@@ -27,8 +27,9 @@ FMHA_OK, FMHA_ERR_INVALID_ARG, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP, FMHA_ERR_WORK
 FMHA_ERR_SCRATCH_TOO_SMALL = -5
 FMHA_BF16, FMHA_FP32 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding_window": 2, "block_diagonal": 3, "prefix_lm": 4}
-ABI_VERSION = 3   # the struct layouts below (fmha_abi_version of include/fmha.h)
-ENTRY_POINTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_splitkv",
+ABI_VERSION = 4   # the struct layouts and entry points below (fmha_abi_version of include/fmha.h)
+ENTRY_POINTS = ("fmha_fwd", "fmha_fwd_workspace_size", "fmha_fwd_with_workspace", "fmha_bwd",
+                "fmha_bwd_workspace_size", "fmha_fwd_splitkv",
                 "fmha_fwd_splitkv_workspace_size", "fmha_fwd_splitkv_noalloc", "fmha_fwd_splitkv_noalloc_max_bytes",
                 "fmha_fwd_varlen", "fmha_bwd_varlen", "build_block_mask", "fmha_status_string", "fmha_abi_version")
 
@@ -110,6 +111,11 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     lib.fmha_fwd.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.c_void_p]
     lib.fmha_fwd.restype = ctypes.c_int
+    lib.fmha_fwd_workspace_size.argtypes = [ctypes.POINTER(CFwdArgs)]
+    lib.fmha_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.fmha_fwd_with_workspace.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]
+    lib.fmha_fwd_with_workspace.restype = ctypes.c_int
     lib.fmha_bwd.argtypes = [ctypes.POINTER(CFwdArgs), ctypes.POINTER(CBwdArgs), ctypes.c_void_p]
     lib.fmha_bwd.restype = ctypes.c_int
     lib.fmha_bwd_workspace_size.argtypes = [ctypes.c_int32] * 3
@@ -269,8 +275,14 @@ def _fwd_args(q, k, v, out, lse, scale, softcap, bias_slope, mask, block_sparse)
 # ------------------------------------------------------------------ entry points
 
 def fmha_fwd(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | None = None,
-             block_sparse: BlockSparse | None = None, out=None, lse=None, stream=None):
-    """Forward: returns (out [B,Nq,H,Dv], lse [B,H,Nq] fp32)."""
+             block_sparse: BlockSparse | None = None, out=None, lse=None, stream=None,
+             key_split: bool = True, workspace=None):
+    """Forward: returns (out [B,Nq,H,Dv], lse [B,H,Nq] fp32).
+
+    With ``key_split`` (the default) a grid too short for the GPU splits the key range
+    (``fmha_fwd_with_workspace``); the workspace is allocated here unless ``workspace`` (a
+    uint8 device tensor of at least ``fmha_fwd_workspace_size`` bytes) is given. With
+    ``key_split=False`` the call is plain ``fmha_fwd``."""
     import torch
     B, Nq, H, _ = q.shape
     Dv = v.shape[3]
@@ -279,8 +291,26 @@ def fmha_fwd(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | N
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     a, _keep = _fwd_args(q, k, v, out, lse, scale, softcap, bias_slope, mask, block_sparse)
-    _check(load_library().fmha_fwd(ctypes.byref(a), _stream(stream)), "fmha_fwd")
+    lib = load_library()
+    need = lib.fmha_fwd_workspace_size(ctypes.byref(a)) if key_split else 0
+    if need == 0:
+        _check(lib.fmha_fwd(ctypes.byref(a), _stream(stream)), "fmha_fwd")
+        return out, lse
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.fmha_fwd_with_workspace(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()), need,
+                                       _stream(stream)), "fmha_fwd_with_workspace")
     return out, lse
+
+
+def fwd_workspace_size(q, k, v, *, mask: Mask | None = None, block_sparse: BlockSparse | None = None) -> int:
+    """Bytes of workspace the key-split forward uses for these shapes (0: no split)."""
+    import torch
+    B, Nq, H, _ = q.shape
+    out = torch.empty((B, Nq, H, v.shape[3]), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    a, _keep = _fwd_args(q, k, v, out, lse, None, 0.0, 0.0, mask, block_sparse)
+    return int(load_library().fmha_fwd_workspace_size(ctypes.byref(a)))
 
 
 def fmha_bwd(q, k, v, out, lse, dout, *, scale=None, softcap=0.0, bias_slope=0.0,

@@ -183,6 +183,9 @@ AttnParams attn_params(const fmha_fwd_args* a) {
   p.cap_k1 = a->softcap > 0.0f ? a->scale * 2.0f * fmha::kLog2e / a->softcap : 0.0f;
   p.cap_u = a->softcap * fmha::kLog2e;
   p.cap_fixed = (a->softcap > 0.0f && a->bias_slope == 0.0f && 2.0f * p.cap_u <= 100.0f) ? 1 : 0;
+  p.kv_splits = 1;
+  p.split_o = nullptr;
+  p.split_lse = nullptr;
   p.bias_log2 = a->bias_slope * fmha::kLog2e;
   p.mask = mask_params(a->mask);
   // longest-first query-tile order pays off when tiles carry different key counts
@@ -266,7 +269,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 extern "C" {
 
-int fmha_abi_version(void) { return 3; }
+int fmha_abi_version(void) { return 4; }
 
 const char* fmha_status_string(int status) {
   switch (status) {
@@ -278,6 +281,42 @@ const char* fmha_status_string(int status) {
     case FMHA_ERR_SCRATCH_TOO_SMALL: return "FMHA_ERR_SCRATCH_TOO_SMALL";
     default: return "FMHA_ERR_UNKNOWN";
   }
+}
+
+// key splits the bf16 forward would use for these arguments (1 = none)
+static int fwd_key_splits(const fmha_fwd_args* a) {
+  if (a->dtype != FMHA_BF16) return 1;
+  return fmha::fwd_bf16_key_splits(a->B, a->H, a->Nq, a->Nk, a->Dqk, a->Dv, a->block_sparse != nullptr);
+}
+
+size_t fmha_fwd_workspace_size(const fmha_fwd_args* a) {
+  if (validate_fwd(a) != FMHA_OK || (int64_t)a->B * a->H * a->Nq == 0) return 0;
+  const int s = fwd_key_splits(a);
+  return s > 1 ? align256(fmha::splitkv_workspace_bytes(a->B, a->H, a->Nq, a->Dv, s)) : 0;
+}
+
+int fmha_fwd_with_workspace(const fmha_fwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_fwd(a);
+  if (rc != FMHA_OK) return rc;
+  if ((int64_t)a->B * a->H * a->Nq == 0) return FMHA_OK;
+  const int s = fwd_key_splits(a);
+  const size_t need = s > 1 ? align256(fmha::splitkv_workspace_bytes(a->B, a->H, a->Nq, a->Dv, s)) : 0;
+  if (need == 0 || workspace == nullptr || workspace_bytes < need) return fmha_fwd(a, stream);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FMHA_ERR_INVALID_ARG;
+  rc = check_device();
+  if (rc != FMHA_OK) return rc;
+  AttnParams p = attn_params(a);
+  p.lists = fwd_lists(nullptr);
+  p.kv_splits = s;
+  const size_t rows = (size_t)a->B * a->H * s * a->Nq;
+  p.split_o = static_cast<float*>(workspace);
+  p.split_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * a->Dv * sizeof(float)));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  FMHA_LOG("fwd bf16 key-split x%d B=%d H=%d Nq=%d Nk=%d D=%d mask=%d", s, a->B, a->H, a->Nq, a->Nk, a->Dv,
+           a->mask.kind);
+  hipError_t e = fmha::launch_fwd_bf16(p, a->Dqk, a->Dv, st);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(fmha::launch_splitkv_combine(p, a->Dv, s, workspace, st));
 }
 
 int fmha_fwd(const fmha_fwd_args* a, void* stream) {

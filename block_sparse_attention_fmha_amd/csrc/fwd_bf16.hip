@@ -90,8 +90,10 @@ void fwd_bf16_kernel(const AttnParams p) {
   using SM = FwdSmem<DQK, DV>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int bid = xcd_remap(blockIdx.x, p.grid_padded);
-  if (bid >= p.total_work) return;
+  const int bid0 = xcd_remap(blockIdx.x, p.grid_padded);
+  if (bid0 >= p.total_work) return;
+  const int ks = p.kv_splits > 1 ? bid0 % p.kv_splits : 0;   // this workgroup's key split
+  const int bid = p.kv_splits > 1 ? bid0 / p.kv_splits : bid0;
   const int bh = bid / p.n_tiles;
   const int t = bid - bh * p.n_tiles;
   const int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
@@ -129,6 +131,12 @@ void fwd_bf16_kernel(const AttnParams p) {
     const int tlo = lo / kBN, thi = (hi + kBN - 1) / kBN;
     seq.t_lo = tlo;
     seq.count = max(0, thi - tlo);
+    if (p.kv_splits > 1) {   // the ks-th of kv_splits contiguous parts of the tile range
+      const int per = (seq.count + p.kv_splits - 1) / p.kv_splits;
+      const int first = min(seq.count, ks * per);
+      seq.t_lo += first;
+      seq.count = min(per, seq.count - first);
+    }
   } else {
     // the two 128-row halves of the workgroup each lie in one sparse row
     const ListParams& L = p.lists;
@@ -366,6 +374,20 @@ void fwd_bf16_kernel(const AttnParams p) {
   const float l_tot = pair_sum(l_run);
   const bool empty = !(l_tot > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l_tot;
+  if (!LISTS && p.kv_splits > 1) {   // partial of this key split, for the combine
+    if (qrow < Nq) {
+      const int64_t prow = ((int64_t)bh * p.kv_splits + ks) * Nq + qrow;
+      float* Po = p.split_o + prow * DV;
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *(f32x4*)(Po + 32 * db + 8 * jj + 4 * g) =
+              f32x4{o[db][4 * jj] * inv, o[db][4 * jj + 1] * inv, o[db][4 * jj + 2] * inv, o[db][4 * jj + 3] * inv};
+      if (g == 0) p.split_lse[prow] = empty ? kNegInf : (m_run + fast_log2(l_tot)) * kLn2;
+    }
+    return;
+  }
   if (qrow < Nq) {
     __bf16* Og = (__bf16*)p.o + o_off + h * p.os_h + (int64_t)qrow * p.os_s;
 #pragma unroll
@@ -429,9 +451,28 @@ bool fwd_bf16_lists_fit(int dqk, int dv, int n_cols, int tile_cols) {
   return bytes <= kMaxLdsBytes;
 }
 
+int fwd_bf16_key_splits(int B, int H, int Nq, int Nk, int dqk, int dv, bool lists) {
+  // Split the key range when the grid is short of the 256 CUs and the key range is long:
+  // then a workgroup's walk over all its key tiles is the critical path of the launch. Each
+  // split writes a 256-row fp32 partial O that the split-KV combine reads back, which only
+  // pays when the split streams much more K / V than that: measured at H = 16, D = 128,
+  // 32 key tiles (2048 keys) per split is the best point (Nq = 256, Nk = 32768: 633 ->
+  // 96 us at 16 splits; Nq = 1024, Nk = 8192: 168 -> 90 us at 4), and any split of a square
+  // N <= 2048 problem is slower than none.
+  if (lists || dqk != dv || (dv != 64 && dv != 128)) return 1;
+  const int64_t work = (int64_t)B * H * ((Nq + kBM - 1) / kBM);
+  if (work <= 0 || work >= 256) return 1;
+  const int key_tiles = (Nk + kBN - 1) / kBN;
+  int s = (int)((256 + work - 1) / work);
+  s = min(s, key_tiles / 32);
+  s = min(s, 16);
+  return s >= 2 ? s : 1;
+}
+
 hipError_t launch_fwd_bf16(AttnParams p, int dqk, int dv, hipStream_t st) {
   p.n_tiles = (p.Nq + kBM - 1) / kBM;
-  p.total_work = p.B * p.H * p.n_tiles;
+  if (p.kv_splits < 1) p.kv_splits = 1;
+  p.total_work = p.B * p.H * p.n_tiles * p.kv_splits;
   p.grid_padded = (p.total_work + 7) / 8 * 8;
   const bool lists = p.lists.pcnt != nullptr;
   const bool softcap = p.softcap > 0.0f;

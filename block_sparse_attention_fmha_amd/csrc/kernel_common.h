@@ -89,6 +89,12 @@ struct AttnParams {
   float cap_u;        // softcap: softcap * log2(e) (the capped score's log2-unit limit)
   int cap_fixed;      // softcap without bias and 2 cap_u <= 100: the forward may use cap_u as
                       // a fixed softmax maximum (every exp2(u - cap_u) lies in [2^-100, 1])
+  // key split of the bf16 forward (1 = off): workgroup (tile, s) walks the s-th of
+  // kv_splits contiguous parts of its tile range and writes its normalised fp32 partial O
+  // [B*H, S, Nq, Dv] and natural-log partial LSE [B*H, S, Nq] for the split-KV combine
+  int kv_splits;
+  float* split_o;
+  float* split_lse;
   float bias_log2;    // relative-bias slope * log2(e)
   MaskParams mask;
   ListParams lists;

@@ -180,6 +180,24 @@ typedef struct {
  * the band edge or is listed as partial. */
 int fmha_fwd(const fmha_fwd_args* args, void* stream);
 
+/* Forward with an optional workspace, for short query sides against long key ranges
+ * (chunked prefill). When the bf16 forward (no block-sparse lists, Dqk == Dv in {64, 128})
+ * would launch fewer workgroups than the GPU has CUs (B * H * ceil(Nq / 256) < 256), it
+ * splits each workgroup's key range into S contiguous parts (S = min(ceil(256 /
+ * workgroups), ceil(Nk / 64) / 32, 16), used when at least 2: every part keeps about 2048
+ * keys or more), computes every part's normalised partial O and LSE in the workspace, and
+ * merges them with the LSE-weighted combine of fmha_fwd_splitkv (the two-chunk online-
+ * softmax merge of the POPCORNBENCH transcript "Kimi-K2.6 l1 p97"). The result is the
+ * same attention as fmha_fwd within the bf16 tolerance, not bit-identical to it.
+ * fmha_fwd_workspace_size returns the bytes this needs for `args` (0 when no split
+ * applies, or for invalid args); with a NULL workspace, or one smaller than that, the call
+ * is exactly fmha_fwd. The workspace is owned by the caller, device memory, 256-byte
+ * aligned (FMHA_ERR_INVALID_ARG otherwise), and must not be used by another call until
+ * this one has finished on `stream`. */
+size_t fmha_fwd_workspace_size(const fmha_fwd_args* args);
+int fmha_fwd_with_workspace(const fmha_fwd_args* args, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Backward from the saved LSE: reads args->q, k, v, o, lse and bwd->dout; writes dQ,
  * dK, dV. bf16 only. Deterministic: no atomics; every gradient element has a single
  * writer and a fixed summation order, so repeated calls give bitwise-identical
@@ -273,8 +291,9 @@ int build_block_mask(const fmha_mask* mask, int32_t B, int32_t Hm, int32_t Nq, i
 /* Human-readable name of a status code (static storage). */
 const char* fmha_status_string(int status);
 
-/* ABI version: bumped whenever a struct layout changes. */
-int fmha_abi_version(void);   /* 3: fmha_varlen.seqused_q / seqused_k (2: kv_heads, varlen entry points) */
+/* ABI version: bumped whenever a struct layout or the set of entry points changes. */
+int fmha_abi_version(void);   /* 4: fmha_fwd_workspace_size / fmha_fwd_with_workspace (3: fmha_varlen.seqused_q /
+                                 seqused_k; 2: kv_heads, varlen entry points) */
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fmha_abi_version() == fa.ABI_VERSION == 3
+    assert lib.fmha_abi_version() == fa.ABI_VERSION == 4
     assert fa.status_string(0) == "FMHA_OK"
     assert fa.status_string(-4) == "FMHA_ERR_WORKSPACE"
     assert fa.status_string(12345) == "FMHA_ERR_UNKNOWN"
@@ -121,6 +121,34 @@ def test_block_sparse_tile_constraints(lib):
     bs.tile_m, bs.n_q_tiles = 128, 1
     bs.n_kv_tiles = 5                                                       # inconsistent with Nk / tile_n
     assert lib.fmha_fwd(ctypes.byref(a), None) == fa.FMHA_ERR_INVALID_ARG
+
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("kw,splits", [
+    ({"H": 16, "Nq": 1024, "Nk": 8192}, 4),      # 64 workgroups, 128 key tiles: 4 splits of 32
+    ({"H": 16, "Nq": 256, "Nk": 32768}, 16),     # short query side, long keys: capped at 16
+    ({"H": 2, "Nq": 129, "Nk": 8000}, 3),        # 125 key tiles: 3 splits
+    ({"H": 16, "Nq": 1024, "Nk": 1024}, 1),      # 16 key tiles: a split would cost more than it saves
+    ({"H": 16, "Nq": 2048, "Nk": 2048}, 1),
+    ({"H": 16, "Nq": 4096, "Nk": 32768}, 1),     # 256 workgroups fill the GPU: no split
+    ({"H": 16, "Nq": 1024, "Nk": 8192, "Dqk": 64, "Dv": 64}, 4),
+    ({"H": 16, "Nq": 1024, "Nk": 8192, "Dqk": 192, "Dv": 128}, 1),
+    ({"H": 16, "Nq": 1024, "Nk": 8192, "dtype": fa.FMHA_FP32}, 1),
+    ({"H": 16, "Nq": 1024, "Nk": 8192, "lse": None}, 0),   # invalid: no workspace
+])
+def test_fwd_workspace_size(lib, kw, splits):
+    a = _args(**kw)
+    for s in (a.q_stride, a.k_stride, a.v_stride, a.o_stride):
+        s[0], s[1] = a.Nq * a.H * 128 * 2 if s is a.q_stride else max(a.Nq, a.Nk) * a.H * 128 * 2, a.H * 128 * 2
+    got = lib.fmha_fwd_workspace_size(ctypes.byref(a))
+    if splits <= 1:
+        assert got == 0
+    else:
+        rows = a.B * a.H * splits * a.Nq
+        assert got == _align256(_align256(rows * a.Dv * 4) + rows * 4)
 
 
 def test_fwd_rejects_sequence_stride_beyond_32bit_tile_offsets(lib):

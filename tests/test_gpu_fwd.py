@@ -170,3 +170,41 @@ def test_fwd_fp32_wide_head_full_size():
                                          np.arange(512), b, h, 512, 512, scale=1 / 32.0)
         check_fp32(f"O[{b},{h}]", o[b, :, h], o_ref)
         check_fp32(f"LSE[{b},{h}]", l[b, h], l_ref)
+
+
+# ------------------------------------------------------------------ key-split forward
+
+KEY_SPLIT = [
+    # (B, Nq, Nk, H, Hkv, D, kind, window, prefix, softcap, slope): short query sides against
+    # long key ranges, so that the forward splits the keys
+    (1, 256, 8192, 16, 16, 128, "none", 0, 0, 0.0, 0.0),
+    (1, 256, 8192, 16, 16, 128, "causal", 0, 0, 0.0, 0.0),
+    (1, 256, 8192, 16, 16, 128, "sliding_window", 300, 0, 0.0, 0.0),
+    (1, 256, 8192, 16, 16, 128, "prefix_lm", 0, 200, 30.0, 0.0),
+    (1, 256, 8192, 16, 16, 64, "causal", 0, 0, 0.0, -0.01),
+    (1, 256, 8192, 16, 4, 128, "causal", 0, 0, 0.0, 0.0),       # grouped K/V heads
+    (2, 300, 5000, 3, 3, 128, "none", 0, 0, 0.0, 0.0),          # ragged rows and keys
+    (1, 129, 8000, 2, 2, 64, "causal", 0, 0, 0.0, 0.0),         # 3 splits of a ragged range
+]
+
+
+@pytest.mark.parametrize("case", range(len(KEY_SPLIT)))
+def test_fwd_bf16_key_split(case):
+    import block_sparse_attention_fmha_amd as fa
+    B, Nq, Nk, H, Hkv, D, kind, W, P, cap, slope = KEY_SPLIT[case]
+    seed = synth.case_seed(9, 300 + case)
+    q, k, v = synth.normal_tensors(seed, [(B, Nq, H, D), (B, Nk, Hkv, D), (B, Nk, Hkv, D)], "bf16")
+    om, gm = mask_pair(kind, B, Nq, Nk, W, P)
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    assert fa.fwd_workspace_size(tq, tk, tv, mask=gm) > 0, "the case should take the key-split path"
+    heads = None if H <= 4 else [0, 7, H - 1]
+    o_ref, l_ref = oracle.forward(q.values, k.values, v.values, softcap=cap, bias_slope=slope, mask=om, heads=heads)
+    hsel = slice(None) if heads is None else np.asarray(heads)
+    for split in (True, False):
+        announce(f"fwd bf16 key_split={split} B={B} Nq={Nq} Nk={Nk} H={H} Hkv={Hkv} D={D} mask={kind} "
+                 f"softcap={cap} bias={slope}")
+        out, lse = fa.fmha_fwd(tq, tk, tv, mask=gm, softcap=cap, bias_slope=slope, key_split=split)
+        import torch
+        torch.cuda.synchronize()
+        check_bf16(f"O split={split}", host(out)[:, :, hsel], o_ref[:, :, hsel])
+        check_bf16(f"LSE split={split}", host(lse)[:, hsel], l_ref[:, hsel])
