@@ -184,6 +184,7 @@ AttnParams attn_params(const fmha_fwd_args* a) {
   p.cap_u = a->softcap * fmha::kLog2e;
   p.cap_fixed = (a->softcap > 0.0f && a->bias_slope == 0.0f && 2.0f * p.cap_u <= 100.0f) ? 1 : 0;
   p.kv_splits = 1;
+  p.split_tiles = 0;
   p.split_o = nullptr;
   p.split_lse = nullptr;
   p.bias_log2 = a->bias_slope * fmha::kLog2e;
@@ -283,40 +284,46 @@ const char* fmha_status_string(int status) {
   }
 }
 
-// key splits the bf16 forward would use for these arguments (1 = none)
-static int fwd_key_splits(const fmha_fwd_args* a) {
-  if (a->dtype != FMHA_BF16) return 1;
-  return fmha::fwd_bf16_key_splits(a->B, a->H, a->Nq, a->Nk, a->Dqk, a->Dv, a->block_sparse != nullptr);
+// key split the bf16 forward would use for these arguments (splits 1 = none)
+static fmha::FwdKeySplit fwd_key_split(const fmha_fwd_args* a) {
+  if (a->dtype != FMHA_BF16) return fmha::FwdKeySplit{1, 0};
+  const AttnParams p = attn_params(a);
+  return fmha::fwd_bf16_key_split(a->B, a->H, a->Nq, a->Nk, p.mask, a->Dqk, a->Dv, a->block_sparse != nullptr);
+}
+
+static size_t fwd_split_bytes(const fmha_fwd_args* a, const fmha::FwdKeySplit& ks) {
+  return ks.splits > 1 ? align256(fmha::fwd_bf16_split_workspace_bytes(a->B, a->H, a->Nq, a->Dv, ks.splits)) : 0;
 }
 
 size_t fmha_fwd_workspace_size(const fmha_fwd_args* a) {
   if (validate_fwd(a) != FMHA_OK || (int64_t)a->B * a->H * a->Nq == 0) return 0;
-  const int s = fwd_key_splits(a);
-  return s > 1 ? align256(fmha::splitkv_workspace_bytes(a->B, a->H, a->Nq, a->Dv, s)) : 0;
+  return fwd_split_bytes(a, fwd_key_split(a));
 }
 
 int fmha_fwd_with_workspace(const fmha_fwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = validate_fwd(a);
   if (rc != FMHA_OK) return rc;
   if ((int64_t)a->B * a->H * a->Nq == 0) return FMHA_OK;
-  const int s = fwd_key_splits(a);
-  const size_t need = s > 1 ? align256(fmha::splitkv_workspace_bytes(a->B, a->H, a->Nq, a->Dv, s)) : 0;
+  const fmha::FwdKeySplit ks = fwd_key_split(a);
+  const size_t need = fwd_split_bytes(a, ks);
   if (need == 0 || workspace == nullptr || workspace_bytes < need) return fmha_fwd(a, stream);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FMHA_ERR_INVALID_ARG;
   rc = check_device();
   if (rc != FMHA_OK) return rc;
   AttnParams p = attn_params(a);
   p.lists = fwd_lists(nullptr);
-  p.kv_splits = s;
-  const size_t rows = (size_t)a->B * a->H * s * a->Nq;
+  p.kv_splits = ks.splits;
+  p.split_tiles = ks.tiles;
+  const size_t rows = (size_t)a->B * a->H * ((a->Nq + fmha::fwd_bf16_block_rows() - 1) / fmha::fwd_bf16_block_rows()) *
+                      ks.splits * fmha::fwd_bf16_block_rows();
   p.split_o = static_cast<float*>(workspace);
   p.split_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * a->Dv * sizeof(float)));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  FMHA_LOG("fwd bf16 key-split x%d B=%d H=%d Nq=%d Nk=%d D=%d mask=%d", s, a->B, a->H, a->Nq, a->Nk, a->Dv,
-           a->mask.kind);
+  FMHA_LOG("fwd bf16 key-split x%d (%d tiles) B=%d H=%d Nq=%d Nk=%d D=%d mask=%d", ks.splits, ks.tiles, a->B, a->H,
+           a->Nq, a->Nk, a->Dv, a->mask.kind);
   hipError_t e = fmha::launch_fwd_bf16(p, a->Dqk, a->Dv, st);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(fmha::launch_splitkv_combine(p, a->Dv, s, workspace, st));
+  return hip_status(fmha::launch_fwd_split_combine(p, a->Dv, st));
 }
 
 int fmha_fwd(const fmha_fwd_args* a, void* stream) {

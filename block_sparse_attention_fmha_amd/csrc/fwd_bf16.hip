@@ -45,6 +45,11 @@ namespace {
 constexpr int kBM = 256;   // query rows per workgroup
 constexpr int kBN = 64;    // keys per tile
 constexpr int kThreads = 512;
+constexpr int kCUs = 256;           // compute units of the GPU the key split balances over
+constexpr int kMaxKeyParts = 16;    // most key parts one query tile is split into
+constexpr int kMinPartTiles = 4;    // shortest key part worth a workgroup of its own
+constexpr double kSplitFixedUs = 5.0;    // key split: combine launch and fixed cost
+constexpr double kSplitUsPerMiB = 0.9;   // key split: per MiB of fp32 partial O
 constexpr float kRescaleLog2 = 8.0f;   // stale-max tolerance of the online softmax (log2 units)
 // LDS stages of (K, V) tiles: tile t is loaded 2 * stages - 4 phases before first use.
 template <int DQK> struct Stages { static constexpr int value = (DQK <= 128) ? 4 : 3; };
@@ -92,7 +97,7 @@ void fwd_bf16_kernel(const AttnParams p) {
 
   const int bid0 = xcd_remap(blockIdx.x, p.grid_padded);
   if (bid0 >= p.total_work) return;
-  const int ks = p.kv_splits > 1 ? bid0 % p.kv_splits : 0;   // this workgroup's key split
+  const int ks = p.kv_splits > 1 ? bid0 % p.kv_splits : 0;   // this workgroup's key part
   const int bid = p.kv_splits > 1 ? bid0 / p.kv_splits : bid0;
   const int bh = bid / p.n_tiles;
   const int t = bid - bh * p.n_tiles;
@@ -122,20 +127,19 @@ void fwd_bf16_kernel(const AttnParams p) {
   seq.t_lo = 0;
   seq.ent = (const uint32_t*)(smem + SM::BYTES + 16);
   const int mk = p.mask.kind;
+  bool part = false;   // one of several key parts of this query tile: writes a partial
   if constexpr (!LISTS) {
-    int lo = 0, hi = Nk;
-    if (mk == kMaskCausal || mk == kMaskWindow) hi = min(Nk, q0 + kBM + delta);
-    if (mk == kMaskPrefix) hi = min(Nk, max(p.mask.prefix, q0 + kBM + delta));
-    if (mk == kMaskWindow) lo = max(0, q0 + delta - p.mask.window);
-    hi = max(hi, 0);
-    const int tlo = lo / kBN, thi = (hi + kBN - 1) / kBN;
-    seq.t_lo = tlo;
-    seq.count = max(0, thi - tlo);
-    if (p.kv_splits > 1) {   // the ks-th of kv_splits contiguous parts of the tile range
-      const int per = (seq.count + p.kv_splits - 1) / p.kv_splits;
-      const int first = min(seq.count, ks * per);
-      seq.t_lo += first;
-      seq.count = min(per, seq.count - first);
+    band_tile_range(p.mask, q0, kBM, Nq, Nk, kBN, &seq.t_lo, &seq.count);
+    if (p.kv_splits > 1) {
+      const int pieces = key_pieces(seq.count, p.kv_splits, p.split_tiles);
+      if (ks >= pieces) return;   // whole workgroup, before any barrier
+      if (pieces > 1) {           // the ks-th of `pieces` contiguous parts of the tile range
+        const int per = (seq.count + pieces - 1) / pieces;
+        const int first = min(seq.count, ks * per);
+        seq.t_lo += first;
+        seq.count = min(per, seq.count - first);
+        part = true;
+      }
     }
   } else {
     // the two 128-row halves of the workgroup each lie in one sparse row
@@ -374,9 +378,9 @@ void fwd_bf16_kernel(const AttnParams p) {
   const float l_tot = pair_sum(l_run);
   const bool empty = !(l_tot > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l_tot;
-  if (!LISTS && p.kv_splits > 1) {   // partial of this key split, for the combine
+  if (!LISTS && part) {   // partial of this key part, for the combine
     if (qrow < Nq) {
-      const int64_t prow = ((int64_t)bh * p.kv_splits + ks) * Nq + qrow;
+      const int64_t prow = (((int64_t)bh * p.n_tiles + qt) * p.kv_splits + ks) * kBM + (qrow - q0);
       float* Po = p.split_o + prow * DV;
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
@@ -451,22 +455,117 @@ bool fwd_bf16_lists_fit(int dqk, int dv, int n_cols, int tile_cols) {
   return bytes <= kMaxLdsBytes;
 }
 
-int fwd_bf16_key_splits(int B, int H, int Nq, int Nk, int dqk, int dv, bool lists) {
-  // Split the key range when the grid is short of the 256 CUs and the key range is long:
-  // then a workgroup's walk over all its key tiles is the critical path of the launch. Each
-  // split writes a 256-row fp32 partial O that the split-KV combine reads back, which only
-  // pays when the split streams much more K / V than that: measured at H = 16, D = 128,
-  // 32 key tiles (2048 keys) per split is the best point (Nq = 256, Nk = 32768: 633 ->
-  // 96 us at 16 splits; Nq = 1024, Nk = 8192: 168 -> 90 us at 4), and any split of a square
-  // N <= 2048 problem is slower than none.
-  if (lists || dqk != dv || (dv != 64 && dv != 128)) return 1;
-  const int64_t work = (int64_t)B * H * ((Nq + kBM - 1) / kBM);
-  if (work <= 0 || work >= 256) return 1;
-  const int key_tiles = (Nk + kBN - 1) / kBN;
-  int s = (int)((256 + work - 1) / work);
-  s = min(s, key_tiles / 32);
-  s = min(s, 16);
-  return s >= 2 ? s : 1;
+// Merge of the key parts of the split query tiles: O = sum_s w_s O_s / sum_s w_s and
+// LSE = mu + ln sum_s w_s with w_s = exp(LSE_s - mu), mu = max_s LSE_s, the parts taken in
+// a fixed order. One workgroup per 256 * 4 / DV rows of a query tile (DV / 4 threads per
+// row, four columns each); the workgroups of a tile walked in one part exit at once.
+template <int DV>
+__global__ __launch_bounds__(256)
+void fwd_split_combine_kernel(const AttnParams p) {
+  constexpr int kTpr = DV / 4, kRpp = 256 / kTpr, kChunks = kBM / kRpp;
+  const int chunk = blockIdx.x % kChunks;
+  const int bt = blockIdx.x / kChunks;
+  const int bh = bt / p.n_tiles;
+  const int qt = bt - bh * p.n_tiles;
+  const int q0 = qt * kBM;
+  int tlo, count;
+  band_tile_range(p.mask, q0, kBM, p.Nq, p.Nk, kBN, &tlo, &count);
+  const int pieces = key_pieces(count, p.kv_splits, p.split_tiles);
+  if (pieces <= 1) return;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int c = threadIdx.x % kTpr;
+  const int r = chunk * kRpp + threadIdx.x / kTpr;
+  const int64_t slot0 = ((int64_t)bh * p.n_tiles + qt) * p.kv_splits;
+  __bf16* Og = (__bf16*)p.o + b * p.os_b + h * p.os_h;
+  float* Lg = p.lse + ((int64_t)b * p.H + h) * p.Nq;
+  if (q0 + r < p.Nq) {
+    float ls[kMaxKeyParts];
+    float mx = kNegInf;
+#pragma unroll
+    for (int s = 0; s < kMaxKeyParts; ++s) {
+      ls[s] = s < pieces ? p.split_lse[(slot0 + s) * kBM + r] : kNegInf;
+      mx = fmaxf(mx, ls[s]);
+    }
+    const bool empty = mx == kNegInf;
+    const float mu = empty ? 0.0f : mx;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float tot = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxKeyParts; ++s) {
+      if (s < pieces) {
+        const float wgt = exp2f((ls[s] - mu) * kLog2e);
+        tot += wgt;
+        acc += wgt * *(const f32x4*)(p.split_o + ((slot0 + s) * kBM + r) * DV + 4 * c);
+      }
+    }
+    const float inv = empty ? 0.0f : 1.0f / tot;
+    u32x2 v;
+    v[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    v[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *(u32x2*)(Og + (int64_t)(q0 + r) * p.os_s + 4 * c) = v;
+    if (c == 0) Lg[q0 + r] = empty ? kNegInf : mu + logf(tot);
+  }
+}
+
+FwdKeySplit fwd_bf16_key_split(int B, int H, int Nq, int Nk, const MaskParams& m, int dqk, int dv, bool lists) {
+  // A query tile is one workgroup's walk over its visible key tiles, and a launch that does
+  // not fill the CUs lasts as long as its longest walk. When the grid is short of the 256
+  // CUs, the longest tiles can be walked in parts of T key tiles, one workgroup each. Every
+  // candidate part count s (T = ceil(longest / s), at least kMinPartTiles) whose parts all
+  // start at once on the CUs (a second round would cost more than the balance gains) is
+  // priced with a cost model measured on MI355X: a 64-key tile of the walk takes about
+  // 1.5 us at Dv = 128 and 1.0 us at Dv = 64 with the GPU busy, and a split costs about
+  // 5 us plus 0.9 us per MiB of fp32 partial O (written by the parts, read by the
+  // combine). The count with the largest predicted saving is used, none if no saving.
+  const FwdKeySplit none{1, 0};
+  if (lists || dqk != dv || (dv != 64 && dv != 128) || B <= 0 || H <= 0 || Nq <= 0) return none;
+  const int n_tiles = (Nq + kBM - 1) / kBM;
+  const int64_t heads = (int64_t)B * H;
+  if (heads * n_tiles >= kCUs) return none;   // the grid fills the CUs already
+  int counts[kCUs];
+  int longest = 0;
+  for (int qt = 0; qt < n_tiles; ++qt) {
+    int tlo;
+    band_tile_range(m, qt * kBM, kBM, Nq, Nk, kBN, &tlo, &counts[qt]);
+    longest = max(longest, counts[qt]);
+  }
+  const double tile_us = dv == 128 ? 1.5 : 1.0;
+  FwdKeySplit best = none;
+  double best_saving = 0.0;
+  for (int s = 2; s <= kMaxKeyParts; ++s) {
+    const int tiles = (longest + s - 1) / s;
+    if (tiles < kMinPartTiles) break;
+    int64_t workgroups = 0, part_rows = 0;
+    int piece = 0;
+    for (int qt = 0; qt < n_tiles; ++qt) {
+      const int n = key_pieces(counts[qt], kMaxKeyParts, tiles);
+      workgroups += n;
+      if (n > 1) part_rows += (int64_t)n * kBM;
+      piece = max(piece, (counts[qt] + n - 1) / n);
+    }
+    if (workgroups * heads > kCUs) continue;
+    const double part_mib = (double)(part_rows * heads) * dv * sizeof(float) / (1 << 20);
+    const double saving = (longest - piece) * tile_us - (kSplitFixedUs + kSplitUsPerMiB * part_mib);
+    if (saving > best_saving) {
+      best_saving = saving;
+      best = FwdKeySplit{(longest + tiles - 1) / tiles, tiles};
+    }
+  }
+  return best;
+}
+
+size_t fwd_bf16_split_workspace_bytes(int B, int H, int Nq, int dv, int splits) {
+  const size_t rows = (size_t)B * H * ((Nq + kBM - 1) / kBM) * splits * kBM;
+  return ((rows * dv * sizeof(float) + 255) / 256) * 256 + rows * sizeof(float);
+}
+
+hipError_t launch_fwd_split_combine(AttnParams p, int dv, hipStream_t st) {
+  p.n_tiles = (p.Nq + kBM - 1) / kBM;
+  const unsigned grid = (unsigned)(p.B * p.H * p.n_tiles) * (unsigned)(kBM * dv / 1024);
+  if (dv == 128) hipLaunchKernelGGL(fwd_split_combine_kernel<128>, dim3(grid), dim3(256), 0, st, p);
+  else if (dv == 64) hipLaunchKernelGGL(fwd_split_combine_kernel<64>, dim3(grid), dim3(256), 0, st, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(AttnParams p, int dqk, int dv, hipStream_t st) {

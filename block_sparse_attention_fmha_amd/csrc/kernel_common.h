@@ -60,6 +60,36 @@ struct MaskParams {
   const int* doc_k;  // [B, Nk]
 };
 
+// Key tiles [*t_lo, *t_lo + *count) of width `tile` that a band mask leaves visible to the
+// query rows [q0, q0 + rows): causal and sliding-window rows i see keys up to
+// i + Nk - Nq (bottom-right aligned), a sliding window from i + Nk - Nq - window, prefix-LM
+// rows also every key below the prefix; no mask and the block-diagonal mask walk every
+// tile. Host and device, so that the host plans the forward's key split from the same
+// counts the kernels walk.
+__host__ __device__ inline void band_tile_range(const MaskParams& m, int q0, int rows, int Nq, int Nk,
+                                                int tile, int* t_lo, int* count) {
+  const int delta = Nk - Nq;
+  int lo = 0, hi = Nk;
+  if (m.kind == kMaskCausal || m.kind == kMaskWindow) hi = q0 + rows + delta < Nk ? q0 + rows + delta : Nk;
+  if (m.kind == kMaskPrefix) {
+    const int reach = m.prefix > q0 + rows + delta ? m.prefix : q0 + rows + delta;
+    hi = reach < Nk ? reach : Nk;
+  }
+  if (m.kind == kMaskWindow) lo = q0 + delta - m.window > 0 ? q0 + delta - m.window : 0;
+  if (hi < 0) hi = 0;
+  const int tlo = lo / tile, thi = (hi + tile - 1) / tile;
+  *t_lo = tlo;
+  *count = thi > tlo ? thi - tlo : 0;
+}
+
+// Number of contiguous key parts a query tile of `count` key tiles is walked in under a
+// key split of at most `splits` parts of about `tiles` tiles each (1: not split).
+__host__ __device__ inline int key_pieces(int count, int splits, int tiles) {
+  if (splits <= 1) return 1;
+  const int n = (count + tiles - 1) / tiles;
+  return n < 1 ? 1 : (n > splits ? splits : n);
+}
+
 constexpr int kMaxLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 
 struct ListParams {  // block-sparse index lists, forward or transposed orientation
@@ -89,10 +119,13 @@ struct AttnParams {
   float cap_u;        // softcap: softcap * log2(e) (the capped score's log2-unit limit)
   int cap_fixed;      // softcap without bias and 2 cap_u <= 100: the forward may use cap_u as
                       // a fixed softmax maximum (every exp2(u - cap_u) lies in [2^-100, 1])
-  // key split of the bf16 forward (1 = off): workgroup (tile, s) walks the s-th of
-  // kv_splits contiguous parts of its tile range and writes its normalised fp32 partial O
-  // [B*H, S, Nq, Dv] and natural-log partial LSE [B*H, S, Nq] for the split-KV combine
+  // key split of the bf16 forward (kv_splits 1 = off): a query tile whose visible range
+  // holds `count` key tiles is walked in key_pieces(count, kv_splits, split_tiles)
+  // contiguous parts, workgroup (tile, s) taking part s; a tile walked in more than one
+  // part writes normalised fp32 partial O [B*H, n_tiles, kv_splits, tile rows, Dv] and
+  // natural-log partial LSE [B*H, n_tiles, kv_splits, tile rows] for the combine
   int kv_splits;
+  int split_tiles;
   float* split_o;
   float* split_lse;
   float bias_log2;    // relative-bias slope * log2(e)

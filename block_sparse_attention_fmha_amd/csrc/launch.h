@@ -15,7 +15,15 @@ int fwd_bf16_list_rows();    // block-sparse tile_m must be a multiple (each hal
 int fwd_bf16_tile_keys();    // keys per tile (block-sparse tile_n must be a multiple)
 // Whether the merged tile sequence of a list row fits the forward kernel's LDS.
 bool fwd_bf16_lists_fit(int dqk, int dv, int n_cols, int tile_cols);
-int fwd_bf16_key_splits(int B, int H, int Nq, int Nk, int dqk, int dv, bool lists);
+// Key split of the bf16 forward for one launch: at most `splits` parts per query tile, of
+// about `tiles` key tiles each (splits 1: none). Only without block-sparse lists and with
+// Dqk == Dv in {64, 128}.
+struct FwdKeySplit { int splits, tiles; };
+FwdKeySplit fwd_bf16_key_split(int B, int H, int Nq, int Nk, const MaskParams& m, int dqk, int dv, bool lists);
+size_t fwd_bf16_split_workspace_bytes(int B, int H, int Nq, int dv, int splits);
+// Merges the partials of the split query tiles (p as given to launch_fwd_bf16, with
+// kv_splits, split_tiles, split_o, split_lse set).
+hipError_t launch_fwd_split_combine(AttnParams p, int dv, hipStream_t st);
 
 // fp32 forward, D-split across wavefronts: D in {64, 128, 1024}, Dqk == Dv, analytic masks.
 hipError_t launch_fwd_f32(AttnParams p, int d, hipStream_t st);
@@ -25,7 +33,6 @@ size_t splitkv_workspace_bytes(int B, int H, int Nq, int Dv, int splits);
 int splitkv_tile_keys();
 // `group` query heads share each K/V head (1 = multi-head).
 hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* ws, hipStream_t st);
-hipError_t launch_splitkv_combine(const AttnParams& p, int d, int splits, void* ws, hipStream_t st);
 
 // bf16 backward: preprocess, dK/dV pass, dQ pass.
 hipError_t launch_bwd_bf16(BwdParams p, int dqk, int dv, hipStream_t st);

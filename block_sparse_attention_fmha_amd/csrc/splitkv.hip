@@ -527,22 +527,6 @@ size_t splitkv_workspace_bytes(int B, int H, int Nq, int Dv, int splits) {
   return ((o_bytes + 255) / 256) * 256 + rows * sizeof(float);
 }
 
-hipError_t launch_splitkv_combine(const AttnParams& p, int d, int splits, void* ws, hipStream_t st) {
-  SplitParams sp;
-  sp.a = p;
-  sp.splits = splits;
-  sp.group = 1;
-  sp.per_split = 0;
-  const size_t rows = (size_t)p.B * p.H * splits * p.Nq;
-  sp.part_o = (float*)ws;
-  sp.part_lse = (float*)((char*)ws + ((rows * d * sizeof(float) + 255) / 256) * 256);
-  const unsigned nrow = (unsigned)(p.B * p.H * p.Nq);
-  if (d == 128) hipLaunchKernelGGL(splitkv_combine_kernel<128>, dim3(nrow), dim3(128), 0, st, sp);
-  else if (d == 64) hipLaunchKernelGGL(splitkv_combine_kernel<64>, dim3(nrow), dim3(64), 0, st, sp);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
 hipError_t launch_fwd_splitkv(AttnParams p, int d, int splits, int group, void* ws, hipStream_t st) {
   SplitParams sp;
   sp.a = p;

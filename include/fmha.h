@@ -180,15 +180,18 @@ typedef struct {
  * the band edge or is listed as partial. */
 int fmha_fwd(const fmha_fwd_args* args, void* stream);
 
-/* Forward with an optional workspace, for short query sides against long key ranges
- * (chunked prefill). When the bf16 forward (no block-sparse lists, Dqk == Dv in {64, 128})
- * would launch fewer workgroups than the GPU has CUs (B * H * ceil(Nq / 256) < 256), it
- * splits each workgroup's key range into S contiguous parts (S = min(ceil(256 /
- * workgroups), ceil(Nk / 64) / 32, 16), used when at least 2: every part keeps about 2048
- * keys or more), computes every part's normalised partial O and LSE in the workspace, and
- * merges them with the LSE-weighted combine of fmha_fwd_splitkv (the two-chunk online-
- * softmax merge of the POPCORNBENCH transcript "Kimi-K2.6 l1 p97"). The result is the
- * same attention as fmha_fwd within the bf16 tolerance, not bit-identical to it.
+/* Forward with an optional workspace, for launches that leave CUs idle: a short query side
+ * against a long key range (chunked prefill), or few heads with a causal mask, whose
+ * longest 256-row query tile walks many more key tiles than the others. When the bf16
+ * forward (no block-sparse lists, Dqk == Dv in {64, 128}) would launch fewer workgroups
+ * than the GPU has CUs (B * H * ceil(Nq / 256) < 256), the long query tiles' key ranges
+ * are walked in contiguous parts of T key tiles (64 keys each), one workgroup per part;
+ * each part writes its normalised partial O and LSE to the workspace, and a combine merges
+ * the parts of each tile with the LSE-weighted rule of fmha_fwd_splitkv (the two-chunk
+ * online-softmax merge of the POPCORNBENCH transcript "Kimi-K2.6 l1 p97"). The library
+ * picks the number of parts (2-16, all running at once on the CUs) from a measured cost
+ * model, or none when a split would not pay. The result is the same attention as
+ * fmha_fwd within the bf16 tolerance, not bit-identical to it, and deterministic.
  * fmha_fwd_workspace_size returns the bytes this needs for `args` (0 when no split
  * applies, or for invalid args); with a NULL workspace, or one smaller than that, the call
  * is exactly fmha_fwd. The workspace is owned by the caller, device memory, 256-byte

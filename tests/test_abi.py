@@ -127,28 +127,83 @@ def _align256(x):
     return (x + 255) // 256 * 256
 
 
+MASK_CAUSAL, MASK_WINDOW, MASK_PREFIX = (fa.MASK_KINDS[k] for k in ("causal", "sliding_window", "prefix_lm"))
+
+
+def _key_tiles(kind, window, prefix, q0, Nq, Nk, rows=256, tile=64):
+    """Key tiles a 256-row query tile of the bf16 forward walks under a band mask."""
+    delta = Nk - Nq
+    lo, hi = 0, Nk
+    if kind in (MASK_CAUSAL, MASK_WINDOW):
+        hi = min(Nk, q0 + rows + delta)
+    if kind == MASK_PREFIX:
+        hi = min(Nk, max(prefix, q0 + rows + delta))
+    if kind == MASK_WINDOW:
+        lo = max(0, q0 + delta - window)
+    hi = max(hi, 0)
+    return max(0, -(-hi // tile) - lo // tile)
+
+
+def _key_split(B, H, Nq, Nk, kind=0, window=0, prefix=0, Dv=128):
+    """(parts, tiles) of the forward's key split: for grids short of the 256 CUs, the part
+    count whose parts fit the CUs in one round with the largest predicted saving (tiles of
+    1.5 us at Dv 128, 1.0 us at Dv 64; a split costs 5 us + 0.9 us per MiB of fp32 partial O)."""
+    n_tiles = -(-Nq // 256)
+    heads = B * H
+    if heads * n_tiles >= 256:
+        return 1, 0
+    counts = [_key_tiles(kind, window, prefix, 256 * t, Nq, Nk) for t in range(n_tiles)]
+    longest = max(counts)
+    tile_us = 1.5 if Dv == 128 else 1.0
+    best, best_saving = (1, 0), 0.0
+    for s in range(2, 17):
+        tiles = -(-longest // s)
+        if tiles < 4:
+            break
+        ns = [min(16, max(1, -(-c // tiles))) for c in counts]
+        if sum(ns) * heads > 256:
+            continue
+        piece = max(-(-c // n) for c, n in zip(counts, ns))
+        part_rows = sum(n * 256 for n in ns if n > 1)
+        part_mib = float(part_rows * heads) * Dv * 4 / (1 << 20)
+        saving = (longest - piece) * tile_us - (5.0 + 0.9 * part_mib)
+        if saving > best_saving:
+            best, best_saving = (-(-longest // tiles), tiles), saving
+    return best
+
+
 @pytest.mark.parametrize("kw,splits", [
-    ({"H": 16, "Nq": 1024, "Nk": 8192}, 4),      # 64 workgroups, 128 key tiles: 4 splits of 32
+    ({"H": 16, "Nq": 1024, "Nk": 8192}, 4),      # 64 tiles of 128 key tiles: 4 parts of 32 fill 256 CUs
     ({"H": 16, "Nq": 256, "Nk": 32768}, 16),     # short query side, long keys: capped at 16
-    ({"H": 2, "Nq": 129, "Nk": 8000}, 3),        # 125 key tiles: 3 splits
-    ({"H": 16, "Nq": 1024, "Nk": 1024}, 1),      # 16 key tiles: a split would cost more than it saves
+    ({"H": 2, "Nq": 129, "Nk": 8000}, 16),       # 2 tiles of 125 key tiles: parts of 8
+    ({"H": 16, "Nq": 1024, "Nk": 1024}, 1),      # 16 key tiles: the partials cost more than they save
+    ({"H": 16, "Nq": 1024, "Nk": 1024, "mask": MASK_CAUSAL}, 1),
     ({"H": 16, "Nq": 2048, "Nk": 2048}, 1),
-    ({"H": 16, "Nq": 4096, "Nk": 32768}, 1),     # 256 workgroups fill the GPU: no split
+    ({"H": 16, "Nq": 2048, "Nk": 2048, "mask": MASK_CAUSAL}, 2),   # the 4 longest tiles in 2 parts
+    ({"H": 16, "Nq": 4096, "Nk": 4096, "mask": MASK_CAUSAL}, 1),   # 256 tiles fill the CUs
+    ({"H": 2, "Nq": 4096, "Nk": 4096, "mask": MASK_CAUSAL}, 8),    # 32 tiles, longest 64
+    ({"H": 16, "Nq": 4096, "Nk": 4096, "mask": MASK_WINDOW, "window": 1024}, 1),
+    ({"H": 16, "Nq": 16384, "Nk": 16384, "mask": MASK_CAUSAL}, 1),
     ({"H": 16, "Nq": 1024, "Nk": 8192, "Dqk": 64, "Dv": 64}, 4),
     ({"H": 16, "Nq": 1024, "Nk": 8192, "Dqk": 192, "Dv": 128}, 1),
     ({"H": 16, "Nq": 1024, "Nk": 8192, "dtype": fa.FMHA_FP32}, 1),
     ({"H": 16, "Nq": 1024, "Nk": 8192, "lse": None}, 0),   # invalid: no workspace
 ])
 def test_fwd_workspace_size(lib, kw, splits):
+    kw = dict(kw)
+    kind, window = kw.pop("mask", 0), kw.pop("window", 0)
     a = _args(**kw)
+    a.mask.kind, a.mask.window = kind, window
     for s in (a.q_stride, a.k_stride, a.v_stride, a.o_stride):
         s[0], s[1] = a.Nq * a.H * 128 * 2 if s is a.q_stride else max(a.Nq, a.Nk) * a.H * 128 * 2, a.H * 128 * 2
     got = lib.fmha_fwd_workspace_size(ctypes.byref(a))
     if splits <= 1:
         assert got == 0
-    else:
-        rows = a.B * a.H * splits * a.Nq
-        assert got == _align256(_align256(rows * a.Dv * 4) + rows * 4)
+        return
+    if a.dtype == fa.FMHA_BF16 and a.Dqk == a.Dv:
+        assert _key_split(a.B, a.H, a.Nq, a.Nk, kind, window, Dv=a.Dv)[0] == splits
+    rows = a.B * a.H * -(-a.Nq // 256) * splits * 256   # 256-row slots per query tile and part
+    assert got == _align256(_align256(rows * a.Dv * 4) + rows * 4)
 
 
 def test_fwd_rejects_sequence_stride_beyond_32bit_tile_offsets(lib):

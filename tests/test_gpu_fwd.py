@@ -179,12 +179,18 @@ KEY_SPLIT = [
     # long key ranges, so that the forward splits the keys
     (1, 256, 8192, 16, 16, 128, "none", 0, 0, 0.0, 0.0),
     (1, 256, 8192, 16, 16, 128, "causal", 0, 0, 0.0, 0.0),
-    (1, 256, 8192, 16, 16, 128, "sliding_window", 300, 0, 0.0, 0.0),
+    (1, 256, 8192, 16, 16, 128, "sliding_window", 3000, 0, 0.0, 0.0),   # 51 tiles in 7 parts
     (1, 256, 8192, 16, 16, 128, "prefix_lm", 0, 200, 30.0, 0.0),
     (1, 256, 8192, 16, 16, 64, "causal", 0, 0, 0.0, -0.01),
     (1, 256, 8192, 16, 4, 128, "causal", 0, 0, 0.0, 0.0),       # grouped K/V heads
     (2, 300, 5000, 3, 3, 128, "none", 0, 0, 0.0, 0.0),          # ragged rows and keys
-    (1, 129, 8000, 2, 2, 64, "causal", 0, 0, 0.0, 0.0),         # 3 splits of a ragged range
+    (1, 129, 8000, 2, 2, 64, "causal", 0, 0, 0.0, 0.0),         # 16 parts of a ragged range
+    # causal imbalance and small grids: split and unsplit query tiles in one launch
+    (1, 2048, 2048, 16, 16, 128, "causal", 0, 0, 0.0, 0.0),     # 1-3 parts of up to 12 tiles
+    (1, 4096, 4096, 2, 2, 128, "causal", 0, 0, 0.0, 0.0),       # up to 8 parts of 8 tiles
+    (1, 2000, 2000, 4, 4, 64, "prefix_lm", 0, 300, 0.0, 0.0),   # ragged last query tile
+    (1, 700, 3000, 4, 4, 128, "causal", 0, 0, 30.0, -0.02),     # Nq < Nk: 5-6 parts, softcap + bias
+    (1, 512, 4096, 4, 4, 128, "sliding_window", 1500, 0, 0.0, 0.0),  # window: 4 parts of 7
 ]
 
 
