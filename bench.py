@@ -20,7 +20,9 @@ Prints ONE JSON line on stdout:
                to TFLOP/s of useful work
 --all-configs additionally prints per-workload timings of the other configurations to
 stderr (not part of the JSON line), with the CPU oracle's time on each configuration
-(sampled (b, h) pairs, extrapolated; skipped with --no-cpu-baseline).
+(sampled (b, h) pairs, extrapolated; skipped with --no-cpu-baseline). Forward and decode
+rows are GPU time per call from HIP graph replay (`timing: "graph replay"`), which leaves
+out the host-side cost of each call; the others are HIP events around single calls.
 """
 from __future__ import annotations
 
@@ -307,6 +309,33 @@ def all_configs_report(oracle_too: bool = True):
             ts.append(a.elapsed_time(b))
         return float(np.median(ts))
 
+    def gpu_time(fn, reps=20, warm=3):
+        """GPU time per call in ms: `reps` calls captured in one HIP graph, the median of 7
+        replays. Unlike events around single calls this excludes the host-side cost of a
+        call (argument marshalling, launch), which is several microseconds and dominates
+        kernels of a few tens of microseconds."""
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for _ in range(reps):
+                    fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(7):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(); g.replay(); b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / reps)
+        del g
+        return float(np.median(ts))
+
     def log(**kw):
         sys.stderr.write(json.dumps(kw) + "\n")
         sys.stderr.flush()
@@ -321,7 +350,7 @@ def all_configs_report(oracle_too: bool = True):
             for kind in ("none", "causal", "sliding_window"):
                 for cap in (0.0, 30.0):
                     m = fa.Mask(kind, window=1024)
-                    ms = timeit(lambda: fa.fmha_fwd(q, k, v, mask=m, softcap=cap))
+                    ms = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m, softcap=cap))
                     if kind == "none":
                         a = n * n
                     elif kind == "causal":
@@ -330,16 +359,33 @@ def all_configs_report(oracle_too: bool = True):
                         a = sum(min(i, 1024) + 1 for i in range(n))
                     f = 2.0 * 16 * 2 * d * a
                     log(workload="fwd_bf16", N=n, D=d, mask=kind, softcap=cap, ms=round(ms, 4),
-                        tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+                        tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                        timing="graph replay")
+    # key-split forward (grids short of the CUs), against the same call without the split
+    for hh, nq, nk, d, kind in ((16, 256, 32768, 128, "none"), (16, 1024, 8192, 128, "none"),
+                                (16, 1024, 8192, 64, "causal"), (2, 4096, 4096, 128, "causal"),
+                                (16, 2048, 2048, 128, "causal")):
+        q = torch.randn(1, nq, hh, d, device=dev).bfloat16()
+        k, v = (torch.randn(1, nk, hh, d, device=dev).bfloat16() for _ in range(2))
+        m = fa.Mask(kind)
+        ms = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m))
+        ms_off = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m, key_split=False))
+        a = nq * nk if kind == "none" else sum(min(nk, i + 1 + nk - nq) for i in range(nq))
+        f = 2.0 * hh * 2 * d * a
+        log(workload="fwd_bf16_key_split", H=hh, Nq=nq, Nk=nk, D=d, mask=kind, ms=round(ms, 4),
+            ms_unsplit=round(ms_off, 4), tflops=round(f / ms / 1e9, 1),
+            frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4), workspace_bytes=fa.fwd_workspace_size(q, k, v, mask=m),
+            timing="graph replay")
+    del q, k, v
     # split-KV decode
     q = torch.randn(8, 1, 32, 128, device=dev).bfloat16()
     k = torch.randn(8, 32768, 32, 128, device=dev).bfloat16()
     v = torch.randn(8, 32768, 32, 128, device=dev).bfloat16()
     for s in (1, 2, 4, 8, 16):
-        ms = timeit(lambda: fa.fmha_fwd_splitkv(q, k, v, s))
+        ms = gpu_time(lambda: fa.fmha_fwd_splitkv(q, k, v, s))
         byts = 2 * k.numel() * 2
         log(workload="splitkv", splits=s, ms=round(ms, 4), GBs=round(byts / ms / 1e6, 1),
-            frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+            frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), timing="graph replay")
     del k, v
     # grouped-query and multi-query decode: H=32 query heads over 8 or 1 K/V heads; the
     # algorithmic bytes are the K/V of the K/V heads
@@ -347,25 +393,26 @@ def all_configs_report(oracle_too: bool = True):
         k = torch.randn(8, 32768, hkv, 128, device=dev).bfloat16()
         v = torch.randn(8, 32768, hkv, 128, device=dev).bfloat16()
         for s in (4, 16, 64):
-            ms = timeit(lambda: fa.fmha_fwd_splitkv(q, k, v, s))
+            ms = gpu_time(lambda: fa.fmha_fwd_splitkv(q, k, v, s))
             byts = 2 * k.numel() * 2
             log(workload="splitkv_grouped", H=32, Hkv=hkv, splits=s, ms=round(ms, 4),
-                GBs=round(byts / ms / 1e6, 1), frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4))
+                GBs=round(byts / ms / 1e6, 1), frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4),
+                timing="graph replay")
         del k, v
     # fp32 wide head
     q, k, v = (torch.randn(4, 512, 8, 1024, device=dev) for _ in range(3))
-    ms = timeit(lambda: fa.fmha_fwd(q, k, v))
+    ms = gpu_time(lambda: fa.fmha_fwd(q, k, v))
     f = 2.0 * 4 * 8 * 2048 * 512 * 512
     log(workload="fwd_fp32_d1024", ms=round(ms, 4), tflops=round(f / ms / 1e9, 2),
-        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 4))
+        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 4), timing="graph replay")
     del q, k, v
     # fp32 parity workload (latency-bound: one 32-row workgroup)
     q, k, v = (torch.randn(1, 128, 1, 64, device=dev) for _ in range(3))
     m = fa.Mask("causal")
-    ms = timeit(lambda: fa.fmha_fwd(q, k, v, mask=m))
+    ms = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m))
     f = 2.0 * 2 * 64 * causal_pairs(128)
     log(workload="fwd_fp32_n128_d64_causal", ms=round(ms, 4), tflops=round(f / ms / 1e9, 4),
-        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 6))
+        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 6), timing="graph replay")
     # block-sparse forward: B=2 H=8 N=8192 D=128, 128 x 128 sparse tiles from the element
     # mask, relative bias -0.01 |i - j|; useful FLOPs on the visible pairs only
     n, bsz, hh = 8192, 2, 8
