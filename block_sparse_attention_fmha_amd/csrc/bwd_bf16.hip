@@ -299,20 +299,21 @@ void bwd_dkdv_kernel(const BwdParams bp) {
               const int ee = 2 * e + z, r = 8 * hh + ee;
               const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
               const int qidx = qb + ee;
-              float dcap = 1.0f, u;
+              // x = u - lse2 (one fma without a score transform); rows past Nq carry
+              // lse2 = +inf, so their P is 0 whatever the test says
+              float dcap = 1.0f, x;
               if constexpr (BIAS && !SOFTCAP)
-                u = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee));
-              else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap);
-              else u = s[kb][r] * p.scale_log2;
-              // rows past Nq carry lse2 = +inf, so their P is 0 whatever the test says
+                x = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee)) - lse2;
+              else if constexpr (SOFTCAP || BIAS) x = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap) - lse2;
+              else x = __builtin_fmaf(s[kb][r], p.scale_log2, -lse2);
               if constexpr (TEST == kTestBand) {
-                if ((uint32_t)qidx - (uint32_t)qlo > qspan) u = kNegInf;
+                if ((uint32_t)qidx - (uint32_t)qlo > qspan) x = kNegInf;
               } else if constexpr (TEST == kTestDoc) {
                 // unconditional (clamped) load, so the loads of a chunk issue back to back
                 const int dq = p.mask.doc_q[(int64_t)b * Nq + min(qidx, Nq - 1)];
-                if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) u = kNegInf;
+                if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) x = kNegInf;
               }
-              pv[z] = fast_exp2(u - lse2);
+              pv[z] = fast_exp2(x);
               pd[z] = pv[z] * dcap;
             }
             pk[e] = pack_bf16x2(pv[0], pv[1]);
@@ -672,19 +673,20 @@ void bwd_dkdv_split_kernel(const BwdParams bp) {
             const float lse2 = ee < 4 ? la[ee] : lb[ee - 4];
             const float dd = ee < 4 ? da[ee] : db4[ee - 4];
             const int qidx = qb + ee;
-            float dcap = 1.0f, u;
+            // x = u - lse2 (one fma without a score transform); rows past Nq carry
+            // lse2 = +inf, so their P is 0 whatever the test says
+            float dcap = 1.0f, x;
             if constexpr (BIAS && !SOFTCAP)
-              u = __builtin_fmaf(s[r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee));
-            else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(s[r], p, qidx, key, dcap);
-            else u = s[r] * p.scale_log2;
-            // rows past Nq carry lse2 = +inf, so their P is 0 whatever the test says
+              x = __builtin_fmaf(s[r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee)) - lse2;
+            else if constexpr (SOFTCAP || BIAS) x = score_log2_d<SOFTCAP, BIAS>(s[r], p, qidx, key, dcap) - lse2;
+            else x = __builtin_fmaf(s[r], p.scale_log2, -lse2);
             if constexpr (TEST == kTestBand) {
-              if ((uint32_t)qidx - (uint32_t)qlo > qspan) u = kNegInf;
+              if ((uint32_t)qidx - (uint32_t)qlo > qspan) x = kNegInf;
             } else if constexpr (TEST == kTestDoc) {
               const int dq = p.mask.doc_q[(int64_t)b * Nq + min(qidx, Nq - 1)];
-              if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) u = kNegInf;
+              if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) x = kNegInf;
             }
-            pv[z] = fast_exp2(u - lse2);
+            pv[z] = fast_exp2(x);
             dsv[z] = pv[z] * dcap * (dp[r] - dd);
           }
           pk[e] = pack_bf16x2(pv[0], pv[1]);

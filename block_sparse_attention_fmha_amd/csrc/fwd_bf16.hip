@@ -249,13 +249,14 @@ void fwd_bf16_kernel(const AttnParams p) {
           s[kb][r] = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(t));
         }
     } else if constexpr (FIXED) {
-      // u - cap_u = -2 cap_u r, r = 1 / (exp(2 y) + 1)
-      const float k2 = -2.0f * p.cap_u;
+      // u - cap_u = -2 cap_u / (exp(2 y) + 1): one fma scales the denominator by
+      // -1 / (2 cap_u), so its reciprocal is the exponent itself
+      const float ik = -0.5f / p.cap_u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          s[kb][r] = fast_rcp(fast_exp2(s[kb][r] * p.cap_k1) + 1.0f) * k2;
+          s[kb][r] = fast_rcp(__builtin_fmaf(fast_exp2(s[kb][r] * p.cap_k1), ik, ik));
     } else if constexpr (SOFTCAP || BIAS) {
       const int jb = opaque_int(n0 + 8 * g);
 #pragma unroll
