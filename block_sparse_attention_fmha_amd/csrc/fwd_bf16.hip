@@ -237,17 +237,10 @@ void fwd_bf16_kernel(const AttnParams p) {
     }
     // score transform (softcap / bias) and mask; reg r of block kb holds key
     // n0 + 32 kb + 16 (r / 8) + 8 g + r % 8 of query row qrow.
-    if constexpr (BIAS && !SOFTCAP) {
-      // relative bias alone: i - j = (qrow - n0 - 8 g) - (register offset), exact in fp32,
-      // so each score costs a subtraction with a literal, a multiply with |.| and an fma
-      const float dq = __int_as_float(opaque_int(__float_as_int((float)(qrow - n0 - 8 * g))));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float t = dq - (float)(32 * kb + 16 * (r >> 3) + (r & 7));
-          s[kb][r] = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(t));
-        }
+    // relative bias alone (BIAS_ONLY): the scores stay raw through the mask and the row
+    // max; the bias enters with the exponent (below)
+    constexpr bool BIAS_ONLY = BIAS && !SOFTCAP;
+    if constexpr (BIAS_ONLY) {
     } else if constexpr (FIXED) {
       // u - cap_u = -2 cap_u / (exp(2 y) + 1): one fma scales the denominator by
       // -1 / (2 cap_u), so its reciprocal is the exponent itself
@@ -277,9 +270,22 @@ void fwd_bf16_kernel(const AttnParams p) {
     // wave raised its running max. O already holds every P V up to tile ts - 1.
     // row max as a shallow tree (short dependency chains: this phase has one wave per
     // SIMD, so latency, not issue rate, bounds it)
+    // BIAS_ONLY: i - j = dq - off_r with dq = qrow - n0 - 8 g and off_r in [0, 55] the
+    // register's key offset, exact in fp32. The largest bias term of the lane's row is at
+    // an end of that range, or 0 where the row's |i - j| reaches 0 (the row inside the
+    // tile's keys), so max(raw) scale + that term bounds the row max from above (the
+    // lazy rescale below only needs an upper bound)
+    const float dq = BIAS_ONLY ? __int_as_float(opaque_int(__float_as_int((float)(qrow - n0 - 8 * g)))) : 0.0f;
+    const bool one_side = qw >= n0 + kBN - 1 || qw + 31 < n0;   // the tile's keys on one side of every row
     if constexpr (!FIXED) {
       float mt = tree_max32(s);
-      mt = pair_max(mt) * c_eff;
+      if constexpr (BIAS_ONLY) {
+        float bm = fmaxf(p.bias_log2 * __builtin_fabsf(dq), p.bias_log2 * __builtin_fabsf(dq - 55.0f));
+        if (!one_side) bm = fmaxf(bm, 0.0f);
+        mt = pair_max(__builtin_fmaf(mt, p.scale_log2, bm));
+      } else {
+        mt = pair_max(mt) * c_eff;
+      }
       // lazy rescale: keep a stale running max until some row's max exceeds it by more
       // than kRescaleLog2, so p = exp2(s - m) <= 2^kRescaleLog2 and the rescale runs only
       // on large jumps (usually just the first tile); O and l always share the same m
@@ -295,6 +301,30 @@ void fwd_bf16_kernel(const AttnParams p) {
       }
     }
     const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+    if constexpr (BIAS_ONLY) {
+      // exponent u - m = raw scale + bias |i - j| - m, in place
+      if (one_side) {
+        // |i - j| = sign (dq - off_r): with sb = sign bias, one fma with the literal off_r
+        // (sb (dq - off_r) - m) and one fma per score
+        const float sb = qw >= n0 + kBN - 1 ? p.bias_log2 : -p.bias_log2;
+        const float am = __builtin_fmaf(sb, dq, -m_use);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[kb][r] = __builtin_fmaf(s[kb][r], p.scale_log2,
+                                      __builtin_fmaf(sb, -(float)(32 * kb + 16 * (r >> 3) + (r & 7)), am));
+      } else {
+        // both sides: a subtraction with a literal, an fma with |.| and an fma per score
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float t = dq - (float)(32 * kb + 16 * (r >> 3) + (r & 7));
+            s[kb][r] = __builtin_fmaf(s[kb][r], p.scale_log2, __builtin_fmaf(p.bias_log2, __builtin_fabsf(t), -m_use));
+          }
+      }
+    }
     // four independent partial row sums of the fp32 probabilities (plain adds: the packed
     // bf16 dot product would stall the partner wave's MFMAs, as it shares their pipe)
     float ls[4];
@@ -305,10 +335,10 @@ void fwd_bf16_kernel(const AttnParams p) {
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = FIXED ? fast_exp2(s[kb][8 * hh + 2 * e])
-                                 : fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
-          const float p1 = FIXED ? fast_exp2(s[kb][8 * hh + 2 * e + 1])
-                                 : fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
+          const float p0 = (FIXED || BIAS_ONLY) ? fast_exp2(s[kb][8 * hh + 2 * e])
+                                                : fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e], c_eff, -m_use));
+          const float p1 = (FIXED || BIAS_ONLY) ? fast_exp2(s[kb][8 * hh + 2 * e + 1])
+                                                : fast_exp2(__builtin_fmaf(s[kb][8 * hh + 2 * e + 1], c_eff, -m_use));
           pk[e] = pack_bf16x2(p0, p1);
           ls[e] = (kb == 0 && hh == 0) ? p0 + p1 : ls[e] + (p0 + p1);   // no 0 + x: it does not fold
         }
