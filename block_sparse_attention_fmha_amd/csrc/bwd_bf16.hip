@@ -303,7 +303,7 @@ void bwd_dkdv_kernel(const BwdParams bp) {
               // lse2 = +inf, so their P is 0 whatever the test says
               float dcap = 1.0f, x;
               if constexpr (BIAS && !SOFTCAP)
-                x = __builtin_fmaf(s[kb][r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee)) - lse2;
+                x = __builtin_fmaf(s[kb][r], p.scale_log2, __builtin_fmaf(p.bias_log2, __builtin_fabsf(dij + (float)ee), -lse2));
               else if constexpr (SOFTCAP || BIAS) x = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qidx, key, dcap) - lse2;
               else x = __builtin_fmaf(s[kb][r], p.scale_log2, -lse2);
               if constexpr (TEST == kTestBand) {
@@ -677,7 +677,7 @@ void bwd_dkdv_split_kernel(const BwdParams bp) {
             // lse2 = +inf, so their P is 0 whatever the test says
             float dcap = 1.0f, x;
             if constexpr (BIAS && !SOFTCAP)
-              x = __builtin_fmaf(s[r], p.scale_log2, p.bias_log2 * __builtin_fabsf(dij + (float)ee)) - lse2;
+              x = __builtin_fmaf(s[r], p.scale_log2, __builtin_fmaf(p.bias_log2, __builtin_fabsf(dij + (float)ee), -lse2));
             else if constexpr (SOFTCAP || BIAS) x = score_log2_d<SOFTCAP, BIAS>(s[r], p, qidx, key, dcap) - lse2;
             else x = __builtin_fmaf(s[r], p.scale_log2, -lse2);
             if constexpr (TEST == kTestBand) {
@@ -962,16 +962,19 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
             for (int z = 0; z < 2; ++z) {
               const int r = 8 * hh + 2 * e + z;
               const int j = jb + 2 * e + z;
-              float dcap = 1.0f, u = s[kb][r];
+              // x = u - lse2, the relative bias folded with -lse2 into one fma
+              float dcap = 1.0f, x;
               if constexpr (BIAS && !SOFTCAP)
-                u = __builtin_fmaf(u, p.scale_log2, p.bias_log2 * __builtin_fabsf(dij - (float)(2 * e + z)));
-              else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
+                x = __builtin_fmaf(s[kb][r], p.scale_log2,
+                                   __builtin_fmaf(p.bias_log2, __builtin_fabsf(dij - (float)(2 * e + z)), -rowv));
+              else if constexpr (SOFTCAP || BIAS) x = score_log2_d<SOFTCAP, BIAS>(s[kb][r], p, qrow, j, dcap) - rowv;
+              else x = __builtin_fmaf(s[kb][r], c_eff, -rowv);
               if constexpr (TEST != kTestNone) {
                 bool vis = (unsigned)(j - lo) < span;
                 if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
-                if (!vis) u = kNegInf;
+                if (!vis) x = kNegInf;
               }
-              pv[z] = fast_exp2(__builtin_fmaf(u, c_eff, -rowv));
+              pv[z] = fast_exp2(x);
               if constexpr (SOFTCAP) pv[z] *= dcap;
             }
             pk[e] = pack_bf16x2(pv[0], pv[1]);
@@ -1275,16 +1278,19 @@ void bwd_dq_kernel(const BwdParams bp) {
           for (int z = 0; z < 2; ++z) {
             const int r = 8 * hh + 2 * e + z;
             const int j = jb + 2 * e + z;
-            float dcap = 1.0f, u = s[r];
+            // x = u - lse2, the relative bias folded with -lse2 into one fma
+            float dcap = 1.0f, x;
             if constexpr (BIAS && !SOFTCAP)
-              u = __builtin_fmaf(u, p.scale_log2, p.bias_log2 * __builtin_fabsf(dij - (float)(2 * e + z)));
-            else if constexpr (SOFTCAP || BIAS) u = score_log2_d<SOFTCAP, BIAS>(u, p, qrow, j, dcap);
+              x = __builtin_fmaf(s[r], p.scale_log2,
+                                 __builtin_fmaf(p.bias_log2, __builtin_fabsf(dij - (float)(2 * e + z)), -lse2));
+            else if constexpr (SOFTCAP || BIAS) x = score_log2_d<SOFTCAP, BIAS>(s[r], p, qrow, j, dcap) - lse2;
+            else x = __builtin_fmaf(s[r], c_eff, -lse2);
             if constexpr (TEST != kTestNone) {
               bool vis = (unsigned)(j - lo) < span;
               if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
-              if (!vis) u = kNegInf;
+              if (!vis) x = kNegInf;
             }
-            float pv = fast_exp2(__builtin_fmaf(u, c_eff, -lse2));
+            float pv = fast_exp2(x);
             if constexpr (SOFTCAP) pv *= dcap;
             dv[z] = pv * (dp[r] - dsum);
           }
