@@ -206,6 +206,38 @@ def test_fwd_workspace_size(lib, kw, splits):
     assert got == _align256(_align256(rows * a.Dv * 4) + rows * 4)
 
 
+def test_fwd_key_split_planner_random_sweep(lib):
+    """The library's key-split plan (seen through the workspace size) equals the host model
+    above on 600 random shapes and masks: B, H, Nq, Nk, Dv, mask kind, window and prefix."""
+    import random
+    rnd = random.Random(20261203)
+    kinds = [0, MASK_CAUSAL, MASK_WINDOW, MASK_PREFIX, fa.MASK_KINDS["block_diagonal"]]
+    split_seen = 0
+    for _ in range(600):
+        B, H = rnd.choice([1, 1, 2, 4]), rnd.choice([1, 2, 3, 8, 16, 32])
+        Nq = rnd.choice([1, 7, 64, 129, 256, 300, 512, 1000, 1024, 2048, 4096])
+        Nk = rnd.choice([1, 63, 64, 500, 1024, 2048, 4097, 8192, 16384, 65536])
+        D = rnd.choice([64, 128])
+        kind = rnd.choice(kinds)
+        window = rnd.choice([0, 100, 1024, 3000]) if kind == MASK_WINDOW else 0
+        prefix = rnd.choice([0, 200, 5000]) if kind == MASK_PREFIX else 0
+        a = _args(B=B, H=H, Nq=Nq, Nk=Nk, Dqk=D, Dv=D)
+        a.mask.kind, a.mask.window, a.mask.prefix = kind, window, prefix
+        if kind == fa.MASK_KINDS["block_diagonal"]:
+            a.mask.doc_q = a.mask.doc_k = 0x100000   # never dereferenced by the size query
+        for st, rows in ((a.q_stride, Nq), (a.o_stride, Nq), (a.k_stride, Nk), (a.v_stride, Nk)):
+            st[0], st[1], st[2] = rows * H * D, H * D, D
+        got = lib.fmha_fwd_workspace_size(ctypes.byref(a))
+        parts, _ = _key_split(B, H, Nq, Nk, kind, window, prefix, Dv=D)
+        if parts <= 1:
+            assert got == 0, (B, H, Nq, Nk, D, kind, window, prefix)
+        else:
+            split_seen += 1
+            rows_ = B * H * -(-Nq // 256) * parts * 256
+            assert got == _align256(_align256(rows_ * D * 4) + rows_ * 4), (B, H, Nq, Nk, D, kind, window, prefix)
+    assert split_seen > 50   # the sweep exercises the split path, not only the unsplit one
+
+
 def test_fwd_rejects_sequence_stride_beyond_32bit_tile_offsets(lib):
     a = _args()
     a.k_stride[1] = (1 << 31) // (2 * 64)          # 64 rows of bf16 reach 2^31 bytes

@@ -3,6 +3,8 @@
 Small cases compare every output element; the full-size workloads compare sampled
 heads / rows that the oracle computes one by one (the oracle is exact per row, so a
 sampled row is as strict as a full comparison of that row)."""
+import functools
+
 import numpy as np
 import pytest
 
@@ -214,3 +216,49 @@ def test_fwd_bf16_key_split(case):
         torch.cuda.synchronize()
         check_bf16(f"O split={split}", host(out)[:, :, hsel], o_ref[:, :, hsel])
         check_bf16(f"LSE split={split}", host(lse)[:, hsel], l_ref[:, hsel])
+
+
+@functools.lru_cache(maxsize=1)
+def _key_split_fuzz_cases(n=16, seed=4242):
+    """Seeded random forwards that take the key-split path: (B, Nq, Nk, H, Hkv, D, kind,
+    window, prefix, softcap, slope), drawn until n of them split (checked with the
+    library's own workspace query on empty tensors of those shapes)."""
+    import random
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    rnd = random.Random(seed)
+    out = []
+    while len(out) < n:
+        B, H = rnd.choice([1, 2]), rnd.choice([1, 2, 4, 8, 12])
+        Hkv = rnd.choice([h for h in (1, 2, 4, H) if H % h == 0])
+        Nq, Nk = rnd.randint(1, 600), rnd.randint(1500, 6000)
+        D = rnd.choice([64, 128])
+        kind = rnd.choice(["none", "causal", "sliding_window", "prefix_lm"])
+        window = rnd.randint(200, 4000) if kind == "sliding_window" else 0
+        prefix = rnd.randint(0, 3000) if kind == "prefix_lm" else 0
+        cap = rnd.choice([0.0, 0.0, 20.0, 50.0])
+        slope = rnd.choice([0.0, 0.0, -0.005, 0.003])
+        q = torch.empty(B, Nq, H, D, device=device(), dtype=torch.bfloat16)
+        k = torch.empty(B, Nk, Hkv, D, device=device(), dtype=torch.bfloat16)
+        if fa.fwd_workspace_size(q, k, k, mask=fa.Mask(kind, window=window, prefix=prefix)) > 0:
+            out.append((B, Nq, Nk, H, Hkv, D, kind, window, prefix, cap, slope))
+    return out
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_fwd_bf16_key_split_fuzz(case):
+    import block_sparse_attention_fmha_amd as fa
+    B, Nq, Nk, H, Hkv, D, kind, W, P, cap, slope = _key_split_fuzz_cases()[case]
+    seed = synth.case_seed(9, 500 + case)
+    q, k, v = synth.normal_tensors(seed, [(B, Nq, H, D), (B, Nk, Hkv, D), (B, Nk, Hkv, D)], "bf16")
+    om, gm = mask_pair(kind, B, Nq, Nk, W, P)
+    heads = None if H <= 2 else [0, H - 1]
+    o_ref, l_ref = oracle.forward(q.values, k.values, v.values, softcap=cap, bias_slope=slope, mask=om, heads=heads)
+    hsel = slice(None) if heads is None else np.asarray(heads)
+    announce(f"fwd bf16 key-split fuzz {case}: B={B} Nq={Nq} Nk={Nk} H={H} Hkv={Hkv} D={D} mask={kind} "
+             f"window={W} prefix={P} softcap={cap} bias={slope}")
+    out, lse = fa.fmha_fwd(to_dev(q), to_dev(k), to_dev(v), mask=gm, softcap=cap, bias_slope=slope)
+    import torch
+    torch.cuda.synchronize()
+    check_bf16("O", host(out)[:, :, hsel], o_ref[:, :, hsel])
+    check_bf16("LSE", host(lse)[:, hsel], l_ref[:, hsel])
