@@ -8,8 +8,10 @@
 // wavefronts of a workgroup its own D slice of width DW for everything:
 //   * S^T partial = K[:, slice] Q[:, slice]^T with v_mfma_f32_32x32x2_f32 (true fp32,
 //     not a reduced-precision tensor format), Q slice resident in VGPRs;
-//   * the NW partial S^T tiles are summed through LDS in a fixed wave order (same result
-//     in every wave, deterministic), every wave then runs the identical online softmax;
+//   * the NW partial S^T tiles are summed through LDS in a fixed wave order (a
+//     reduce-scatter: wave w sums the w-th part of the tile over all partials, every wave
+//     then reads the whole sum; deterministic), every wave then runs the identical online
+//     softmax;
 //   * O^T[slice] += V[:, slice]^T P^T with the same MFMA, so the O accumulator of a wave
 //     is only its slice (32 queries x DW).
 // Each K and V slice is used by exactly one wave, so nothing is shared through LDS but
@@ -185,34 +187,40 @@ void fwd_f32_kernel(const AttnParams p) {
       for (int j = 0; j < KPRE; ++j) kr[j] = *(const f32x4*)(kp + 8 * j);
     }
 
-    // every wave needs the full sum: exchange the partials (previous readers are past
-    // the barrier below, so the buffer is free)
+    // every wave needs the full sum: a reduce-scatter through LDS. Each wave writes its
+    // partial; wave w sums the w-th of NW equal parts of the tile over all partials (in
+    // wave order) and writes it over that part of wave 0's partial, which only wave w
+    // reads; then every wave reads the summed tile. (The previous tile's readers are past
+    // the first barrier, so the buffer is free.)
     if (it > 0) lds_barrier();
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq)
       red_w[rq * 64] = float4{acc[4 * rq], acc[4 * rq + 1], acc[4 * rq + 2], acc[4 * rq + 3]};
     lds_barrier();
-    // one register quad at a time: each quad's read address depends on the previous
-    // quad's sum (an empty asm), so the compiler cannot hoist all NW * 4 reads (16 NW
-    // registers) to the barrier
+    {
+      constexpr int PER = 256 * 4 / NW;                 // floats of the tile per wave (128 at NW = 8)
+      static_assert(PER % 64 == 0, "whole floats per lane");
+      constexpr int FPL = PER / 64;                     // floats per lane
+      float* part = (float*)(smem + NW * SM::VSLICE);   // wave 0's partial; wave ww's at + ww * 1024
+      const int f0 = PER * w + FPL * l;
+      float x[FPL];
+#pragma unroll
+      for (int e = 0; e < FPL; ++e) x[e] = part[f0 + e];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww)
+#pragma unroll
+        for (int e = 0; e < FPL; ++e) x[e] += part[ww * 1024 + f0 + e];
+#pragma unroll
+      for (int e = 0; e < FPL; ++e) part[f0 + e] = x[e];
+    }
+    lds_barrier();
     float sc[16];
     {
-      int roff = NW * SM::VSLICE + 16 * l;   // this lane's first partial quad (bytes)
+      const float4* q4 = (const float4*)(smem + NW * SM::VSLICE) + l;
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const float4* q4 = (const float4*)(smem + roff) + rq * 64;
-        float4 y[NW];
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) y[ww] = q4[ww * 4 * 64];
-        float4 x = y[0];
-#pragma unroll
-        for (int ww = 1; ww < NW; ++ww) {
-          x.x += y[ww].x; x.y += y[ww].y; x.z += y[ww].z; x.w += y[ww].w;
-        }
+        const float4 x = q4[rq * 64];
         sc[4 * rq] = x.x; sc[4 * rq + 1] = x.y; sc[4 * rq + 2] = x.z; sc[4 * rq + 3] = x.w;
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(roff) : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
-#endif
       }
     }
 
