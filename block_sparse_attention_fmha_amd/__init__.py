@@ -244,23 +244,30 @@ class BlockSparse:
 
 
 def _fwd_args(q, k, v, out, lse, scale, softcap, bias_slope, mask, block_sparse):
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse")):
+    """Argument block of a forward call. out / lse None (size queries only): q's address and
+    the contiguous [B, Nq, H, Dv] strides stand in for them; nothing is read or written."""
+    size_query = out is None
+    for t, n in ((q, "q"), (k, "k"), (v, "v")) + (() if size_query else ((out, "out"), (lse, "lse"))):
         _need_device(t, n)
-    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+    if not (q.dtype == k.dtype == v.dtype and (size_query or out.dtype == q.dtype)):
         raise ValueError("q, k, v and out must share one dtype")
     B, Nq, H, Dqk = q.shape
     Nk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
-    if k.shape != (B, Nk, Hkv, Dqk) or v.shape != (B, Nk, Hkv, Dv) or out.shape != (B, Nq, H, Dv):
+    if k.shape != (B, Nk, Hkv, Dqk) or v.shape != (B, Nk, Hkv, Dv) or (
+            not size_query and out.shape != (B, Nq, H, Dv)):
         raise ValueError("inconsistent q / k / v / out shapes")
-    if tuple(lse.shape) != (B, H, Nq) or str(lse.dtype) != "torch.float32" or not lse.is_contiguous():
+    if not size_query and (tuple(lse.shape) != (B, H, Nq) or str(lse.dtype) != "torch.float32"
+                           or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     a = CFwdArgs()
     a.B, a.H, a.Nq, a.Nk, a.Dqk, a.Dv = B, H, Nq, Nk, Dqk, Dv
     a.dtype = _dtype_code(q)
     a.kv_heads = 0 if Hkv == H else Hkv   # grouped K/V heads: the library decides support
     a.reserved2 = 0
-    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
-    a.q_stride, a.k_stride, a.v_stride, a.o_stride = _strides(q), _strides(k), _strides(v), _strides(out)
+    o_ptr, lse_ptr = (q.data_ptr(), q.data_ptr()) if size_query else (out.data_ptr(), lse.data_ptr())
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), o_ptr, lse_ptr
+    o_stride = Strides3(Nq * H * Dv, H * Dv, Dv) if size_query else _strides(out)
+    a.q_stride, a.k_stride, a.v_stride, a.o_stride = _strides(q), _strides(k), _strides(v), o_stride
     a.scale = float(1.0 / math.sqrt(Dqk) if scale is None else scale)
     a.softcap = float(softcap or 0.0)
     a.bias_slope = float(bias_slope or 0.0)
@@ -305,11 +312,7 @@ def fmha_fwd(q, k, v, *, scale=None, softcap=0.0, bias_slope=0.0, mask: Mask | N
 
 def fwd_workspace_size(q, k, v, *, mask: Mask | None = None, block_sparse: BlockSparse | None = None) -> int:
     """Bytes of workspace the key-split forward uses for these shapes (0: no split)."""
-    import torch
-    B, Nq, H, _ = q.shape
-    out = torch.empty((B, Nq, H, v.shape[3]), dtype=q.dtype, device=q.device)
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    a, _keep = _fwd_args(q, k, v, out, lse, None, 0.0, 0.0, mask, block_sparse)
+    a, _keep = _fwd_args(q, k, v, None, None, None, 0.0, 0.0, mask, block_sparse)
     return int(load_library().fmha_fwd_workspace_size(ctypes.byref(a)))
 
 
