@@ -482,20 +482,20 @@ def all_configs_report(oracle_too: bool = True):
 # (and DIR/bench_all.log, the `--all-configs` line of the same box, if present).
 
 PROFILE_CMDS = {
-    "trace": "timeout -k 10 240 rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/trace -o run -- "
+    "trace": "timeout -k 10 240 rocprofv3 --kernel-trace --stats -d $OUT/trace -o run -- "
              "python3 $R/bench.py --profile --steps 5 --warmup 2",
-    "fetch": "timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o run -- "
+    "fetch": "timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE -d $OUT/fetch -o run -- "
              "python3 $R/bench.py --profile --steps 2 --warmup 1",
-    "write": "timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o run -- "
+    "write": "timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE -d $OUT/write -o run -- "
              "python3 $R/bench.py --profile --steps 2 --warmup 1",
     "sq1": "timeout -s KILL 180 rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
            "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
-           "GRBM_GUI_ACTIVE -d $R/gpurun_out/prof/sq1 -o run -- python3 $R/bench.py --profile --steps 1 --warmup 1",
+           "GRBM_GUI_ACTIVE -d $OUT/sq1 -o run -- python3 $R/bench.py --profile --steps 1 --warmup 1",
     "sq2": "timeout -s KILL 180 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 "
            "SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_LDS_DATA_FIFO_FULL GRBM_GUI_ACTIVE "
-           "-d $R/gpurun_out/prof/sq2 -o run -- python3 $R/bench.py --profile --steps 1 --warmup 1",
+           "-d $OUT/sq2 -o run -- python3 $R/bench.py --profile --steps 1 --warmup 1",
 }
-PROFILE_PRE = "R=$PWD; cd /tmp; export TMPDIR=/tmp"
+PROFILE_PRE = "R=$PWD; OUT=<results directory>; cd /tmp; export TMPDIR=/tmp"
 PROFILE_COPY = "__amd_rocclr_copyBuffer"
 PROFILE_HEAD = ["fwd_bf16_kernel<128, 128, false, false, false>", "bwd_preprocess_kernel<128>",
                 "bwd_dkdv_kernel<128, 128, false, false, false>", "bwd_dq_kernel<128, 128, false, false, false>"]
@@ -630,7 +630,7 @@ def summarize_profiles(src: str, out_dir: str):
         fh.write("\n".join([
             "# Kernel trace: causal bf16 fwd+bwd, B=1 H=16 Nq=Nk=16384 D=128", "",
             f"Command (on the MI355X box, from the repository root, `{PROFILE_PRE}`); summary written by "
-            f"`python3 bench.py --summarize-profiles gpurun_out/prof`:", "", *cmd("trace"), "",
+            f"`python3 bench.py --summarize-profiles $OUT`:", "", *cmd("trace"), "",
             f"{note} {hashline}", "", bench_note, "", *TRH, *head_t, ""]))
     with open(os.path.join(out_dir, "fwd_bwd_causal_b1h16n16384d128_hbm_counters.md"), "w") as fh:
         fh.write("\n".join([
@@ -677,7 +677,7 @@ def summarize_profiles(src: str, out_dir: str):
             "N=8192 D=128, causal element mask on 128x128 sparse tiles, relative bias -0.01|i-j|, with "
             "`build_block_mask` (`classify_kernel<false>` forward lists, `<true>` transposed lists).", "",
             f"Same runs as the fwd+bwd profiles (`{PROFILE_PRE}`), summarised by "
-            f"`python3 bench.py --summarize-profiles gpurun_out/prof`, which stops with an error when a kernel "
+            f"`python3 bench.py --summarize-profiles $OUT`, which stops with an error when a kernel "
             f"listed here has no row:", "", *cmd("trace", "fetch", "write", "sq1", "sq2"), "",
             note, "", hashline, "", calib, "", "## Kernel trace", "", *TRH, *other_t, "", *lines, "",
             "## HBM traffic", "", *HBH, *other_h, "", "## SQ counters", "",
