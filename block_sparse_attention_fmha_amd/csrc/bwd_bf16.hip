@@ -276,6 +276,9 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     const int tq = head_step(ts, gi);
     const int i0 = seq.start(tq, LISTS);
     const float* LD = (const float*)(smem + (ts % SM::NST) * SM::STAGE + SM::QB + SM::OB);
+    // the batch's query document ids; vector loads need them 16-byte aligned
+    const int* dqrow = p.mask.doc_q + (int64_t)b * Nq;
+    const bool dq_al = (reinterpret_cast<uintptr_t>(dqrow) & 15) == 0;
     bool need;
     if constexpr (LISTS) need = seq.cls(tq, 0, true) != 2u;
     else need = i0 < need_below || i0 > need_above;
@@ -290,6 +293,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
           const int qb = (TEST != kTestNone || BIAS) ? opaque_int(i0 + qi) : 0;
           // relative bias alone: i - j = (i0 + qi - key) + ee, exact in fp32 (as in the forward)
           const float dij = (BIAS && !SOFTCAP) ? __int_as_float(opaque_int(__float_as_int((float)(i0 + qi - key)))) : 0.0f;
+          int dqv[8];   // documents of queries qb .. qb + 7
+          if constexpr (TEST >= kTestDoc) doc_ids8<TEST == kTestDocVec>(dqrow, qb, Nq, dqv);
           u32x4 pk, pc;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -308,10 +313,8 @@ void bwd_dkdv_kernel(const BwdParams bp) {
               else x = __builtin_fmaf(s[kb][r], p.scale_log2, -lse2);
               if constexpr (TEST == kTestBand) {
                 if ((uint32_t)qidx - (uint32_t)qlo > qspan) x = kNegInf;
-              } else if constexpr (TEST == kTestDoc) {
-                // unconditional (clamped) load, so the loads of a chunk issue back to back
-                const int dq = p.mask.doc_q[(int64_t)b * Nq + min(qidx, Nq - 1)];
-                if ((qidx < Nq) & (key < Nk) & (dq != kdoc)) x = kNegInf;
+              } else if constexpr (TEST >= kTestDoc) {
+                if ((qidx < Nq) & (key < Nk) & (dqv[ee] != kdoc)) x = kNegInf;
               }
               pv[z] = fast_exp2(x);
               pd[z] = pv[z] * dcap;
@@ -325,6 +328,7 @@ void bwd_dkdv_kernel(const BwdParams bp) {
     };
     if (!need) body(IntC<kTestNone>{});
     else if (mk != kMaskBlockDiag) body(IntC<kTestBand>{});
+    else if (dq_al && i0 + 64 <= Nq) body(IntC<kTestDocVec>{});   // the step's 64 queries in bounds
     else body(IntC<kTestDoc>{});
   };
 
@@ -698,7 +702,7 @@ void bwd_dkdv_split_kernel(const BwdParams bp) {
     };
     if (!need) body(IntC<kTestNone>{});
     else if (mk != kMaskBlockDiag) body(IntC<kTestBand>{});
-    else body(IntC<kTestDoc>{});
+    else body(IntC<kTestDoc>{});   // (a vector-load body measured no gain here)
   };
 
   // Step t refills the stage of step t - 2 (read up to step t - 1) with step t + NST - 2,
@@ -941,6 +945,8 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
     // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents);
     // rows past Nq carry rowv = +inf, so their P is 0 whatever the test says
     const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
+    // a 64-key tile in bounds with an aligned row: the documents come in vector loads
+    const bool dk_wide = n0 + 64 <= Nk && (reinterpret_cast<uintptr_t>(dkd) & 15) == 0;
     const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;   // wave-uniform
     const bool band = elem && mk != kMaskBlockDiag;
     const int lo = band ? band_lo : 0, hi = hide ? 0 : band ? band_hi : Nk;
@@ -954,6 +960,8 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
           const int jb = (TEST != kTestNone || BIAS) ? opaque_int(n0 + 32 * kb + 16 * hh + 8 * g) : 0;
           // relative bias alone: i - j = (qrow - jb) - (2 e + z), exact in fp32 (as in the forward)
           const float dij = (BIAS && !SOFTCAP) ? __int_as_float(opaque_int(__float_as_int((float)(qrow - jb)))) : 0.0f;
+          int dkv[8];   // documents of keys jb .. jb + 7
+          if constexpr (TEST >= kTestDoc) doc_ids8<TEST == kTestDocVec>(dkd, jb, Nk, dkv);
           u32x4 pk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -971,7 +979,7 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
               else x = __builtin_fmaf(s[kb][r], c_eff, -rowv);
               if constexpr (TEST != kTestNone) {
                 bool vis = (unsigned)(j - lo) < span;
-                if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
+                if constexpr (TEST >= kTestDoc) vis = vis & (dkv[2 * e + z] == dqd);
                 if (!vis) x = kNegInf;
               }
               pv[z] = fast_exp2(x);
@@ -984,6 +992,7 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
     };
     if (!need) body(IntC<kTestNone>{});
     else if (!bdw) body(IntC<kTestBand>{});
+    else if (dk_wide) body(IntC<kTestDocVec>{});
     else body(IntC<kTestDoc>{});
   };
 
@@ -1259,6 +1268,8 @@ void bwd_dq_kernel(const BwdParams bp) {
     }
     // visible keys of the lane's row in this tile: lo <= j < hi (and equal documents)
     const int* dkd = p.mask.doc_k + (int64_t)b * Nk;
+    // a 64-key tile in bounds with an aligned row: the documents come in vector loads
+    const bool dk_wide = n0 + 64 <= Nk && (reinterpret_cast<uintptr_t>(dkd) & 15) == 0;
     const bool bdw = need && !hide && elem && mk == kMaskBlockDiag;   // wave-uniform
     const bool band = elem && mk != kMaskBlockDiag;
     const int lo = band ? band_lo : 0, hi = hide ? 0 : band ? band_hi : Nk;
@@ -1270,6 +1281,8 @@ void bwd_dq_kernel(const BwdParams bp) {
         const int jb = (TEST != kTestNone || BIAS) ? opaque_int(n0 + 32 * half + 16 * hh + 8 * g) : 0;
         // relative bias alone: i - j = (qrow - jb) - (2 e + z), exact in fp32 (as in the forward)
         const float dij = (BIAS && !SOFTCAP) ? __int_as_float(opaque_int(__float_as_int((float)(qrow - jb)))) : 0.0f;
+        int dkv[8];   // documents of keys jb .. jb + 7
+        if constexpr (TEST >= kTestDoc) doc_ids8<TEST == kTestDocVec>(dkd, jb, Nk, dkv);
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1287,7 +1300,7 @@ void bwd_dq_kernel(const BwdParams bp) {
             else x = __builtin_fmaf(s[r], c_eff, -lse2);
             if constexpr (TEST != kTestNone) {
               bool vis = (unsigned)(j - lo) < span;
-              if constexpr (TEST == kTestDoc) vis = vis & (dkd[min(j, Nk - 1)] == dqd);   // unconditional load
+              if constexpr (TEST >= kTestDoc) vis = vis & (dkv[2 * e + z] == dqd);
               if (!vis) x = kNegInf;
             }
             float pv = fast_exp2(x);
@@ -1301,6 +1314,7 @@ void bwd_dq_kernel(const BwdParams bp) {
     };
     if (!need) body(IntC<kTestNone>{});
     else if (!bdw) body(IntC<kTestBand>{});
+    else if (dk_wide) body(IntC<kTestDocVec>{});
     else body(IntC<kTestDoc>{});
   };
 

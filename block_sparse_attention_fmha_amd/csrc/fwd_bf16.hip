@@ -262,7 +262,8 @@ void fwd_bf16_kernel(const AttnParams p) {
       // rows past Nq are never stored, so their mask does not matter
       const int kbase = opaque_int(n0 + 8 * g);
       if (hide) mask_tile_band(s, kbase, 0, 0);
-      else if (elem && mk == kMaskBlockDiag) mask_tile_doc(s, p.mask.doc_k + (int64_t)b * Nk, row_doc, kbase, Nk);
+      else if (elem && mk == kMaskBlockDiag)   // lists with softcap alone sit at the register limit
+        mask_tile_doc<!(LISTS && SOFTCAP && !BIAS)>(s, p.mask.doc_k + (int64_t)b * Nk, row_doc, kbase, Nk);
       else mask_tile_band(s, kbase, elem ? band_lo : 0, elem ? band_hi : Nk);
     }
 

@@ -38,7 +38,9 @@ enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskBlockDiag 
 
 // Per-tile element-mask test, chosen once per tile so the unrolled element loops carry no
 // run-time case: none, a visible interval per row or column, or the document comparison.
-enum MaskTest { kTestNone = 0, kTestBand = 1, kTestDoc = 2 };
+// kTestDocVec is the document comparison on a tile whose document ids are all in bounds
+// and 16-byte aligned, so they are read with vector loads.
+enum MaskTest { kTestNone = 0, kTestBand = 1, kTestDoc = 2, kTestDocVec = 3 };
 template <int V> struct IntC { static constexpr int value = V; };
 
 // A value the optimiser may not look through. Used on per-step row or column bases so the
@@ -574,7 +576,26 @@ __device__ __forceinline__ void mask_tile_band(f32x16 (&s)[2], int kbase, int lo
 }
 
 // Document (block-diagonal) variant: key j visible iff j < nk and its document is dq.
+// The lane's keys are four runs of 8: kbase + 32 kb + 16 h + e. With VEC, when every
+// lane's runs are in bounds and 16-byte aligned (one ballot keeps the branch wave-uniform),
+// their document ids come in 8 vector loads instead of 32 scalar ones; the 32 ids then in
+// flight cost registers, so a kernel at its register limit passes VEC = false.
+template <bool VEC>
 __device__ __forceinline__ void mask_tile_doc(f32x16 (&s)[2], const int* doc_k, int dq, int kbase, int nk) {
+  const bool wide = VEC && kbase + 56 <= nk && ((reinterpret_cast<uintptr_t>(doc_k + kbase) & 15) == 0);
+  if (VEC && __builtin_amdgcn_ballot_w64(!wide) == 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int4 a = *(const int4*)(doc_k + kbase + 32 * kb + 16 * h);
+        const int4 c = *(const int4*)(doc_k + kbase + 32 * kb + 16 * h + 4);
+        const int d[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[kb][8 * h + e] = d[e] == dq ? s[kb][8 * h + e] : kNegInf;
+      }
+    return;
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -583,6 +604,21 @@ __device__ __forceinline__ void mask_tile_doc(f32x16 (&s)[2], const int* doc_k, 
       const bool vis = (j < nk) & (doc_k[min(j, nk - 1)] == dq);   // unconditional (clamped) load
       s[kb][r] = vis ? s[kb][r] : kNegInf;
     }
+}
+
+// Document ids of the 8 consecutive positions j0 .. j0 + 7 of a row of n ids. WIDE
+// promises j0 + 8 <= n and doc + j0 16-byte aligned: two vector loads; otherwise eight
+// scalar loads clamped to the row (the caller masks j >= n itself).
+template <bool WIDE>
+__device__ __forceinline__ void doc_ids8(const int* doc, int j0, int n, int (&d)[8]) {
+  if constexpr (WIDE) {
+    const int4 a = *(const int4*)(doc + j0), c = *(const int4*)(doc + j0 + 4);
+    d[0] = a.x, d[1] = a.y, d[2] = a.z, d[3] = a.w;
+    d[4] = c.x, d[5] = c.y, d[6] = c.z, d[7] = c.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = doc[min(j0 + e, n - 1)];
+  }
 }
 
 // Tiles of a row band that need the element mask: with tile start n0 (a multiple of

@@ -50,6 +50,9 @@ SMALL = [
     (1, 512, 512, 2, 64, 64, "sliding_window", 100, 0, 30.0, 0.0),
     (2, 384, 384, 2, 128, 128, "prefix_lm", 0, 100, 0.0, -0.01),
     (2, 512, 512, 1, 128, 128, "block_diagonal", 0, 0, 0.0, -0.01),
+    # odd lengths: row 1's document ids unaligned, ragged last tiles (vector and scalar loads)
+    (2, 515, 517, 2, 128, 128, "block_diagonal", 0, 0, 0.0, 0.0),
+    (2, 517, 515, 2, 64, 64, "block_diagonal", 0, 0, 0.0, 0.0),
     (1, 200, 200, 2, 128, 128, "none", 0, 0, 5.0, -0.05),
 ]
 

@@ -56,6 +56,10 @@ SMALL = [
     (1, 640, 640, 2, 64, 64, "sliding_window", 100, 0, 30.0, 0.0),
     (2, 384, 384, 2, 64, 64, "prefix_lm", 0, 100, 0.0, -0.01),
     (2, 512, 512, 2, 128, 128, "block_diagonal", 0, 0, 0.0, -0.01),
+    # odd lengths: batch row 1's document ids are not 16-byte aligned and the last key tile
+    # is ragged, so both the vector and the scalar document loads run
+    (2, 515, 517, 2, 128, 128, "block_diagonal", 0, 0, 0.0, 0.0),
+    (2, 517, 515, 2, 64, 64, "block_diagonal", 0, 0, 0.0, 0.0),
     (1, 255, 385, 2, 192, 128, "causal", 0, 0, 0.0, 0.0),      # MLA-shaped heads
     (1, 200, 200, 2, 128, 128, "none", 0, 0, 5.0, -0.05),
     (1, 300, 300, 2, 128, 128, "causal", 0, 0, 30.0, 0.0),     # softcap, fixed softmax maximum
