@@ -133,12 +133,17 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   const int G = p.group > 1 ? p.group : 1;
   const int Hkv = p.H / G;
   const int bhk = bid / bp.n_kv_tiles;
-  const int kt = bid - bhk * bp.n_kv_tiles;   // ascending: under causal masks the first key
+  int kt = bid - bhk * bp.n_kv_tiles;   // ascending: under causal masks the first key
   const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;   // tiles see the most queries
   const int h0 = hk * G;
+  const int tid = threadIdx.x;
+  // under lists without a band order (causal and prefix-LM walks already shrink with the
+  // tile index) the transposed list lengths set the order (fixed lengths under lists)
+  if (LISTS && !p.longest_first)
+    kt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h0)) * p.lists.n_rows,
+                               bp.n_kv_tiles, kKB, 0, p.Nk, kt, (int*)smem, tid);
   const int k0 = kt * kKB;
 
-  const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 5, lq = l & 31;
   const int role = w >> 2;     // 0: P wave (K; S, P, dV), 1: dS wave (V; dP, dS, dK)
@@ -529,12 +534,17 @@ void bwd_dkdv_split_kernel(const BwdParams bp) {
   const int G = p.group > 1 ? p.group : 1;
   const int Hkv = p.H / G;
   const int bhk = bid / bp.n_kv_tiles;
-  const int kt = bid - bhk * bp.n_kv_tiles;
+  int kt = bid - bhk * bp.n_kv_tiles;
   const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;
   const int h0 = hk * G;
+  const int tid = threadIdx.x;
+  // under lists without a band order (causal and prefix-LM walks already shrink with the
+  // tile index) the transposed list lengths set the order (fixed lengths under lists)
+  if (LISTS && !p.longest_first)
+    kt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h0)) * p.lists.n_rows,
+                               bp.n_kv_tiles, kKB, 0, p.Nk, kt, (int*)smem, tid);
   const int k0 = kt * kKB;
 
-  const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 5, lq = l & 31;
   const int half = w >> 2;     // queries 32 half .. 32 half + 31 of every step
@@ -822,11 +832,16 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
   if (bid >= p.total_work) return;
   const int bh = bid / p.n_tiles;
   const int t = bid - bh * p.n_tiles;
-  const int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int tid = threadIdx.x;
+  int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
+  // under lists without a band order (causal and prefix-LM walks already shrink from the
+  // last tile) the list lengths set the order (fixed lengths under lists)
+  if (LISTS && !p.longest_first)
+    qt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
+                               p.n_tiles, kQM, 0, p.Nq, t, (int*)smem, tid);
   const int q0 = qt * kQM;
 
-  const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 5, lq = l & 31;
   const int role = w >> 2;     // 0: S wave (Q; S^T, P), 1: dQ wave (dO; dP^T, dS, dQ^T)
@@ -1149,11 +1164,16 @@ void bwd_dq_kernel(const BwdParams bp) {
   if (bid >= p.total_work) return;
   const int bh = bid / p.n_tiles;
   const int t = bid - bh * p.n_tiles;
-  const int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int tid = threadIdx.x;
+  int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
+  // under lists without a band order (causal and prefix-LM walks already shrink from the
+  // last tile) the list lengths set the order (fixed lengths under lists)
+  if (LISTS && !p.longest_first)
+    qt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
+                               p.n_tiles, kQM, 0, p.Nq, t, (int*)smem, tid);
   const int q0 = qt * kQM;
 
-  const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 5, lq = l & 31;
   const int half = w >> 2;     // keys 32 half .. 32 half + 31 of every tile

@@ -711,6 +711,46 @@ __device__ int build_tile_sequence(const ListParams& L, int64_t row0, int64_t ro
   return *total;
 }
 
+// Longest walks first under block-sparse lists. The n resident tiles of one (batch, mask
+// head) are ranked by how many sparse tiles their list rows name (descending, ties by
+// index), and workgroup t of them takes the tile of rank t, so the longest walks start in
+// the first dispatch round and the short ones fill in behind them. Tile j covers elements
+// [j span, (j + 1) span) of the list side: its row holds element j span and, with
+// half > 0, also element j span + half when that lies in bounds and in another list row
+// (the forward's two 128-row halves). The rank is a heuristic of the dispatch order
+// only; results do not depend on it. `lds` holds n + 1 ints (n <= kMaxRankedTiles, else
+// the natural order j = t is kept). Contains barriers: every thread of the workgroup calls it.
+constexpr int kMaxRankedTiles = 4096;
+template <int NTHREADS>
+__device__ int ranked_tile(const ListParams& L, int64_t rbase, int n, int span, int half, int n_elems, int t,
+                           int* lds, int tid) {
+  if (n > kMaxRankedTiles) return t;
+  for (int j = tid; j < n; j += NTHREADS) {
+    const int e0 = j * span;
+    const int64_t r0 = rbase + e0 / L.tile_rows;
+    int c = clamp_count(L.pcnt[r0], L.n_cols) + clamp_count(L.fcnt[r0], L.n_cols);
+    if (half > 0 && e0 + half < n_elems && (e0 + half) / L.tile_rows != e0 / L.tile_rows) {
+      const int64_t r1 = rbase + (e0 + half) / L.tile_rows;
+      c += clamp_count(L.pcnt[r1], L.n_cols) + clamp_count(L.fcnt[r1], L.n_cols);
+    }
+    lds[j] = c;
+  }
+  __syncthreads();
+  for (int j = tid; j < n; j += NTHREADS) {
+    const int cj = lds[j];
+    int rank = 0;
+    for (int k = 0; k < n; ++k) {
+      const int ck = lds[k];
+      rank += (ck > cj) | ((ck == cj) & (k < j));
+    }
+    if (rank == t) lds[n] = j;   // exactly one j has rank t (ranks are a permutation)
+  }
+  __syncthreads();
+  const int r = lds[n];
+  __syncthreads();   // every thread has read the result: the caller may reuse `lds`
+  return r;
+}
+
 // Key / query tile walk of one workgroup: an analytic run of tiles, or a merged sequence.
 template <int UNIT>
 struct TileSeq {

@@ -95,13 +95,15 @@ def test_block_sparse_forward_full_size(kind, W, P):
     check_bf16("LSE", l[:, heads][:, :, rows], l_ref[:, heads][:, :, rows])
 
 
-@pytest.mark.parametrize("N,TM,TN,heads", [(512, 128, 128, 1), (700, 128, 192, 2), (1100, 384, 64, 2),
-                                          (300, 256, 128, 1)])
-def test_block_sparse_custom_lists_small(N, TM, TN, heads):
+@pytest.mark.parametrize("N,TM,TN,heads,kind", [(512, 128, 128, 1, "causal"), (700, 128, 192, 2, "causal"),
+                                               (1100, 384, 64, 2, "causal"), (300, 256, 128, 1, "causal"),
+                                               (1100, 128, 128, 2, "none"), (2000, 256, 64, 2, "none")])
+def test_block_sparse_custom_lists_small(N, TM, TN, heads, kind):
     # arbitrary lists (not derived from the mask): full tiles ignore the element mask,
     # partial tiles apply it, unlisted tiles are skipped. Entries are unsorted, some are
     # repeated, some columns sit in both lists of a row (full wins), and one row is empty
-    # (its queries see nothing: O = 0, LSE = -inf).
+    # (its queries see nothing: O = 0, LSE = -inf). Without a band mask ("none") the
+    # workgroups take their query tiles in order of list length, per head.
     import torch
     import block_sparse_attention_fmha_amd as fa
     B, H, D = 1, 2, 128
@@ -125,8 +127,8 @@ def test_block_sparse_custom_lists_small(N, TM, TN, heads):
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(a).to(dev)
     bs = fa.BlockSparse(TM, TN, nqt, nkt, heads, t(pc), t(pi), t(fc), t(fi), None, None, None, None)
-    om, gm = mask_pair("causal", B, N, N)
-    announce(f"block-sparse fwd with custom lists N={N} tiles={TM}x{TN} heads={heads}")
+    om, gm = mask_pair(kind, B, N, N)
+    announce(f"block-sparse fwd with custom lists N={N} tiles={TM}x{TN} heads={heads} mask={kind}")
     out, lse = fa.fmha_fwd(to_dev(q), to_dev(k), to_dev(v), mask=gm, block_sparse=bs)
     torch.cuda.synchronize()
     ref_lists = oracle.BlockLists(TM, TN, pc, pi, fc, fi, None, None, None, None)
