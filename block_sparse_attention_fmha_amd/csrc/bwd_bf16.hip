@@ -132,16 +132,18 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   // sums stay deterministic)
   const int G = p.group > 1 ? p.group : 1;
   const int Hkv = p.H / G;
-  const int bhk = bid / bp.n_kv_tiles;
-  int kt = bid - bhk * bp.n_kv_tiles;   // ascending: under causal masks the first key
-  const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;   // tiles see the most queries
+  const int kt0 = bid - (bid / bp.n_kv_tiles) * bp.n_kv_tiles;   // ascending: under causal masks
+  const int bhk = work_bh<!LISTS>(p, bid / bp.n_kv_tiles, Hkv);    // the first key tiles see the most queries
+  const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;
   const int h0 = hk * G;
   const int tid = threadIdx.x;
   // under lists without a band order (causal and prefix-LM walks already shrink with the
   // tile index) the transposed list lengths set the order (fixed lengths under lists)
-  if (LISTS && !p.longest_first)
-    kt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h0)) * p.lists.n_rows,
-                               bp.n_kv_tiles, kKB, 0, p.Nk, kt, (int*)smem, tid);
+  const int kt = (LISTS && !p.longest_first)
+                     ? ranked_tile<kThreads>(p.lists,
+                                             ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h0)) * p.lists.n_rows,
+                                             bp.n_kv_tiles, kKB, 0, p.Nk, kt0, (int*)smem, tid)
+                     : kt0;
   const int k0 = kt * kKB;
 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -533,16 +535,18 @@ void bwd_dkdv_split_kernel(const BwdParams bp) {
   // work item: (batch b, K/V head hk, key tile kt); grouped query heads walked in order
   const int G = p.group > 1 ? p.group : 1;
   const int Hkv = p.H / G;
-  const int bhk = bid / bp.n_kv_tiles;
-  int kt = bid - bhk * bp.n_kv_tiles;
+  const int kt0 = bid - (bid / bp.n_kv_tiles) * bp.n_kv_tiles;
+  const int bhk = work_bh<!LISTS>(p, bid / bp.n_kv_tiles, Hkv);
   const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;
   const int h0 = hk * G;
   const int tid = threadIdx.x;
   // under lists without a band order (causal and prefix-LM walks already shrink with the
   // tile index) the transposed list lengths set the order (fixed lengths under lists)
-  if (LISTS && !p.longest_first)
-    kt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h0)) * p.lists.n_rows,
-                               bp.n_kv_tiles, kKB, 0, p.Nk, kt, (int*)smem, tid);
+  const int kt = (LISTS && !p.longest_first)
+                     ? ranked_tile<kThreads>(p.lists,
+                                             ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h0)) * p.lists.n_rows,
+                                             bp.n_kv_tiles, kKB, 0, p.Nk, kt0, (int*)smem, tid)
+                     : kt0;
   const int k0 = kt * kKB;
 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -830,16 +834,17 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
 
   const int bid = xcd_remap(blockIdx.x, p.grid_padded);
   if (bid >= p.total_work) return;
-  const int bh = bid / p.n_tiles;
-  const int t = bid - bh * p.n_tiles;
+  const int t = bid - (bid / p.n_tiles) * p.n_tiles;
+  const int bh = work_bh<!LISTS>(p, bid / p.n_tiles, p.H);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int tid = threadIdx.x;
-  int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
   // under lists without a band order (causal and prefix-LM walks already shrink from the
   // last tile) the list lengths set the order (fixed lengths under lists)
-  if (LISTS && !p.longest_first)
-    qt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
-                               p.n_tiles, kQM, 0, p.Nq, t, (int*)smem, tid);
+  const int qt = (LISTS && !p.longest_first)
+                     ? ranked_tile<kThreads>(p.lists,
+                                             ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
+                                             p.n_tiles, kQM, 0, p.Nq, t, (int*)smem, tid)
+                     : (p.longest_first ? (p.n_tiles - 1 - t) : t);
   const int q0 = qt * kQM;
 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1162,16 +1167,17 @@ void bwd_dq_kernel(const BwdParams bp) {
 
   const int bid = xcd_remap(blockIdx.x, p.grid_padded);
   if (bid >= p.total_work) return;
-  const int bh = bid / p.n_tiles;
-  const int t = bid - bh * p.n_tiles;
+  const int t = bid - (bid / p.n_tiles) * p.n_tiles;
+  const int bh = work_bh<!LISTS>(p, bid / p.n_tiles, p.H);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int tid = threadIdx.x;
-  int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
   // under lists without a band order (causal and prefix-LM walks already shrink from the
   // last tile) the list lengths set the order (fixed lengths under lists)
-  if (LISTS && !p.longest_first)
-    qt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
-                               p.n_tiles, kQM, 0, p.Nq, t, (int*)smem, tid);
+  const int qt = (LISTS && !p.longest_first)
+                     ? ranked_tile<kThreads>(p.lists,
+                                             ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
+                                             p.n_tiles, kQM, 0, p.Nq, t, (int*)smem, tid)
+                     : (p.longest_first ? (p.n_tiles - 1 - t) : t);
   const int q0 = qt * kQM;
 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -99,16 +99,17 @@ void fwd_bf16_kernel(const AttnParams p) {
   if (bid0 >= p.total_work) return;
   const int ks = p.kv_splits > 1 ? bid0 % p.kv_splits : 0;   // this workgroup's key part
   const int bid = p.kv_splits > 1 ? bid0 / p.kv_splits : bid0;
-  const int bh = bid / p.n_tiles;
-  const int t = bid - bh * p.n_tiles;
+  const int t = bid - (bid / p.n_tiles) * p.n_tiles;
+  const int bh = work_bh<!LISTS>(p, bid / p.n_tiles, p.H);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int tid = threadIdx.x;
-  int qt = p.longest_first ? (p.n_tiles - 1 - t) : t;
   // under lists without a band order (causal and prefix-LM walks already shrink from the
   // last tile) the list lengths set the order (fixed lengths: no packed sequences here)
-  if (LISTS && !p.longest_first)
-    qt = ranked_tile<kThreads>(p.lists, ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
-                               p.n_tiles, kBM, kBM / 2, p.Nq, t, (int*)smem, tid);
+  const int qt = (LISTS && !p.longest_first)
+                     ? ranked_tile<kThreads>(p.lists,
+                                             ((int64_t)b * p.lists.heads + (p.lists.heads == 1 ? 0 : h)) * p.lists.n_rows,
+                                             p.n_tiles, kBM, kBM / 2, p.Nq, t, (int*)smem, tid)
+                     : (p.longest_first ? (p.n_tiles - 1 - t) : t);
   const int q0 = qt * kBM;
 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so per-wave tests branch on scalars

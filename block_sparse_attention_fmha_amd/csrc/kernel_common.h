@@ -198,6 +198,17 @@ __device__ __forceinline__ int64_t lse_base(const AttnParams& p, const SeqInfo& 
   return s.packed ? (int64_t)h * p.lse_total + s.qs : ((int64_t)b * p.H + h) * p.Nq;
 }
 
+// Work index of (batch, head) pair x < B * nh, decoded as b = bh / nh, h = bh % nh.
+// Packed variable-length sequences take x head-major (bh = (x % B) nh + x / B): the XCD
+// remap hands every XCD a contiguous run of x, which then spans all sequences of one head
+// instead of a few sequences of unequal length. Fixed lengths keep x (every (b, h) costs
+// the same). PACKED = false for kernels that never see packed sequences (the block-sparse
+// list variants).
+template <bool PACKED>
+__device__ __forceinline__ int work_bh(const AttnParams& p, int x, int nh) {
+  return (PACKED && p.cu_q != nullptr) ? (x - (x / p.B) * p.B) * nh + x / p.B : x;
+}
+
 // ---------------------------------------------------------------------------------------
 // Small device helpers.
 
