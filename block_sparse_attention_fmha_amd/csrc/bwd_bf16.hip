@@ -133,7 +133,7 @@ void bwd_dkdv_kernel(const BwdParams bp) {
   const int G = p.group > 1 ? p.group : 1;
   const int Hkv = p.H / G;
   const int kt0 = bid - (bid / bp.n_kv_tiles) * bp.n_kv_tiles;   // ascending: under causal masks
-  const int bhk = work_bh<!LISTS>(p, bid / bp.n_kv_tiles, Hkv);    // the first key tiles see the most queries
+  const int bhk = work_bh<LISTS>(p, bid / bp.n_kv_tiles, Hkv);    // the first key tiles see the most queries
   const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;
   const int h0 = hk * G;
   const int tid = threadIdx.x;
@@ -536,7 +536,7 @@ void bwd_dkdv_split_kernel(const BwdParams bp) {
   const int G = p.group > 1 ? p.group : 1;
   const int Hkv = p.H / G;
   const int kt0 = bid - (bid / bp.n_kv_tiles) * bp.n_kv_tiles;
-  const int bhk = work_bh<!LISTS>(p, bid / bp.n_kv_tiles, Hkv);
+  const int bhk = work_bh<LISTS>(p, bid / bp.n_kv_tiles, Hkv);
   const int b = bhk / Hkv, hk = bhk - (bhk / Hkv) * Hkv;
   const int h0 = hk * G;
   const int tid = threadIdx.x;
@@ -835,7 +835,7 @@ void bwd_dq_roles_kernel(const BwdParams bp) {
   const int bid = xcd_remap(blockIdx.x, p.grid_padded);
   if (bid >= p.total_work) return;
   const int t = bid - (bid / p.n_tiles) * p.n_tiles;
-  const int bh = work_bh<!LISTS>(p, bid / p.n_tiles, p.H);
+  const int bh = work_bh<LISTS>(p, bid / p.n_tiles, p.H);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int tid = threadIdx.x;
   // under lists without a band order (causal and prefix-LM walks already shrink from the
@@ -1168,7 +1168,7 @@ void bwd_dq_kernel(const BwdParams bp) {
   const int bid = xcd_remap(blockIdx.x, p.grid_padded);
   if (bid >= p.total_work) return;
   const int t = bid - (bid / p.n_tiles) * p.n_tiles;
-  const int bh = work_bh<!LISTS>(p, bid / p.n_tiles, p.H);
+  const int bh = work_bh<LISTS>(p, bid / p.n_tiles, p.H);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int tid = threadIdx.x;
   // under lists without a band order (causal and prefix-LM walks already shrink from the

@@ -100,7 +100,7 @@ void fwd_bf16_kernel(const AttnParams p) {
   const int ks = p.kv_splits > 1 ? bid0 % p.kv_splits : 0;   // this workgroup's key part
   const int bid = p.kv_splits > 1 ? bid0 / p.kv_splits : bid0;
   const int t = bid - (bid / p.n_tiles) * p.n_tiles;
-  const int bh = work_bh<!LISTS>(p, bid / p.n_tiles, p.H);
+  const int bh = work_bh<LISTS>(p, bid / p.n_tiles, p.H);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int tid = threadIdx.x;
   // under lists without a band order (causal and prefix-LM walks already shrink from the

@@ -199,14 +199,14 @@ __device__ __forceinline__ int64_t lse_base(const AttnParams& p, const SeqInfo& 
 }
 
 // Work index of (batch, head) pair x < B * nh, decoded as b = bh / nh, h = bh % nh.
-// Packed variable-length sequences take x head-major (bh = (x % B) nh + x / B): the XCD
-// remap hands every XCD a contiguous run of x, which then spans all sequences of one head
-// instead of a few sequences of unequal length. Fixed lengths keep x (every (b, h) costs
-// the same). PACKED = false for kernels that never see packed sequences (the block-sparse
-// list variants).
-template <bool PACKED>
+// The XCD remap hands every XCD a contiguous run of x. Where batch rows differ in cost,
+// x is taken head-major (bh = (x % B) nh + x / B) so that a run spans every batch row of
+// one head instead of a few rows of unequal cost: packed variable-length sequences, and
+// block-sparse lists (LISTS), whose rows list different numbers of tiles. Other
+// fixed-length grids keep x (every (b, h) costs the same).
+template <bool LISTS>
 __device__ __forceinline__ int work_bh(const AttnParams& p, int x, int nh) {
-  return (PACKED && p.cu_q != nullptr) ? (x - (x / p.B) * p.B) * nh + x / p.B : x;
+  return (LISTS || p.cu_q != nullptr) ? (x - (x / p.B) * p.B) * nh + x / p.B : x;
 }
 
 // ---------------------------------------------------------------------------------------
