@@ -10,17 +10,22 @@ from tests.gpu_util import announce, check_bf16, check_grad, host
 pytestmark = pytest.mark.gpu
 
 
-def _run(seed, lq, lk, H, dqk, dv, kind, window=0, prefix=0, softcap=0.0, slope=0.0, backward=False):
+def _run(seed, lq, lk, H, dqk, dv, kind, window=0, prefix=0, softcap=0.0, slope=0.0, backward=False, hkv=None):
     import torch
     import block_sparse_attention_fmha_amd as fa
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
     # packed rows from the shared seeded generator: [1, total, H, D] -> [total, H, D]
-    q = synth.attention_inputs(seed, 1, int(cu_q[-1]), int(cu_k[-1]), H, dqk, dv, "bf16", with_dout=True)
+    tq_, tk_ = int(cu_q[-1]), int(cu_k[-1])
+    if hkv is None or hkv == H:
+        q = synth.attention_inputs(seed, 1, tq_, tk_, H, dqk, dv, "bf16", with_dout=True)
+    else:   # grouped K/V heads: K / V carry hkv heads
+        q = synth.normal_tensors(seed, [(1, tq_, H, dqk), (1, tk_, hkv, dqk), (1, tk_, hkv, dv), (1, tq_, H, dv)],
+                                 "bf16")
     qv, kv, vv, dov = (x.values[0] for x in q)
     dev = torch.device("cuda:0")
     tq, tk, tv, tdo = (x.to_torch(dev)[0] for x in q)
-    announce(f"varlen fwd seed={seed} seqs={len(lq)} total_q={cu_q[-1]} total_k={cu_k[-1]} H={H} "
+    announce(f"varlen fwd seed={seed} seqs={len(lq)} total_q={cu_q[-1]} total_k={cu_k[-1]} H={H} Hkv={hkv or H} "
              f"D={dqk}/{dv} mask={kind} W={window} P={prefix} softcap={softcap} bias={slope}")
     out, lse = fa.fmha_fwd_varlen(tq, tk, tv, torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev),
                                   max(lq), max(lk), mask=fa.Mask(kind, window=window, prefix=prefix),
@@ -66,6 +71,21 @@ def test_varlen_documents_of_the_block_sparse_workload():
     docs = synth.document_ids(synth.case_seed(3, 2), 2, 8192)
     lens = [int(c) for b in range(2) for c in np.bincount(docs[b])]
     _run(synth.case_seed(9, 850), lens, lens, 2, 128, 128, "none", slope=-0.01)
+
+
+GQA_CASES = [
+    # (query lengths, key lengths, H, Hkv, D, mask, window, slope): grouped K/V heads, where
+    # the work order runs over query heads (forward, dQ) and K/V heads (dK / dV)
+    ([300, 1, 700, 129], [300, 1, 700, 129], 4, 2, 128, "causal", 0, 0.0),
+    ([513, 40, 1000], [769, 200, 1000], 4, 1, 128, "none", 0, -0.01),
+    ([640, 333, 77], [640, 333, 77], 4, 2, 64, "sliding_window", 100, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GQA_CASES)))
+def test_varlen_grouped_heads(case):
+    lq, lk, H, hkv, d, kind, w, slope = GQA_CASES[case]
+    _run(synth.case_seed(9, 870 + case), lq, lk, H, d, d, kind, w, 0, 0.0, slope, backward=True, hkv=hkv)
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
