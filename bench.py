@@ -289,7 +289,8 @@ def oracle_config_timings(log):
 
 
 def all_configs_report(oracle_too: bool = True):
-    """Extra timings of the other workloads, to stderr (median of events), and the CPU
+    """Extra timings of the other workloads, to stderr (median, with min and 90th
+    percentile, of events around single calls or of HIP graph replays), and the CPU
     oracle's time on each configuration (sampled; see oracle_config_timings)."""
     import numpy as np
     import torch
@@ -297,7 +298,11 @@ def all_configs_report(oracle_too: bool = True):
     from block_sparse_attention_fmha_amd import synth  # document ids (data only)
     dev = torch.device("cuda:0")
 
-    def timeit(fn, reps=20, warm=3):
+    # spread of the last measurement (min and 90th percentile, ms), added to the next log line
+    spread = {}
+
+    def timeit(fn, reps=50, warm=10):
+        """Median ms of `reps` calls, each between two events (after `warm` untimed calls)."""
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
@@ -307,13 +312,14 @@ def all_configs_report(oracle_too: bool = True):
             a.record(); fn(); b.record()
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b))
+        spread.update(ms_min=round(float(np.min(ts)), 4), ms_p90=round(float(np.percentile(ts, 90)), 4))
         return float(np.median(ts))
 
-    def gpu_time(fn, reps=20, warm=3):
-        """GPU time per call in ms: `reps` calls captured in one HIP graph, the median of 7
-        replays. Unlike events around single calls this excludes the host-side cost of a
-        call (argument marshalling, launch), which is several microseconds and dominates
-        kernels of a few tens of microseconds."""
+    def gpu_time(fn, reps=20, warm=10, replays=15):
+        """GPU time per call in ms: `reps` calls captured in one HIP graph, the median over
+        `replays` replays (300 timed calls). Unlike events around single calls this excludes
+        the host-side cost of a call (argument marshalling, launch), which is several
+        microseconds and dominates kernels of a few tens of microseconds."""
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
@@ -328,15 +334,19 @@ def all_configs_report(oracle_too: bool = True):
         g.replay()
         torch.cuda.synchronize()
         ts = []
-        for _ in range(7):
+        for _ in range(replays):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(); g.replay(); b.record()
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b) / reps)
         del g
+        spread.update(ms_min=round(float(np.min(ts)), 4), ms_p90=round(float(np.percentile(ts, 90)), 4))
         return float(np.median(ts))
 
     def log(**kw):
+        if "ms" in kw and spread:   # the spread of the timing `ms` reports (measured last)
+            kw.update(spread)
+            spread.clear()
         sys.stderr.write(json.dumps(kw) + "\n")
         sys.stderr.flush()
 
@@ -368,8 +378,8 @@ def all_configs_report(oracle_too: bool = True):
         q = torch.randn(1, nq, hh, d, device=dev).bfloat16()
         k, v = (torch.randn(1, nk, hh, d, device=dev).bfloat16() for _ in range(2))
         m = fa.Mask(kind)
-        ms = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m))
         ms_off = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m, key_split=False))
+        ms = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m))   # timed last: its spread is logged
         a = nq * nk if kind == "none" else sum(min(nk, i + 1 + nk - nq) for i in range(nq))
         f = 2.0 * hh * 2 * d * a
         log(workload="fwd_bf16_key_split", H=hh, Nq=nq, Nk=nk, D=d, mask=kind, ms=round(ms, 4),
