@@ -243,7 +243,8 @@ def oracle_config_timings(log):
     """The CPU oracle beside the other configurations: each timed on a stated sample of
     (batch, head) pairs and extrapolated linearly to the whole configuration (every pair of
     a configuration costs the same: the oracle materialises each (b, h) score matrix).
-    About half a minute of CPU work in all."""
+    About half a minute of CPU work in all. Returns the extrapolated seconds per
+    configuration key ("1", "3", "4/4096", "4/8192", "5a", "5b")."""
     import numpy as np
     import oracle
     from block_sparse_attention_fmha_amd import synth
@@ -253,7 +254,10 @@ def oracle_config_timings(log):
         fn()
         return time.perf_counter() - t0
 
-    def report(config, workload, secs, done, total, unit_desc):
+    whole = {}
+
+    def report(config, workload, secs, done, total, unit_desc, key=None):
+        whole[key or config] = secs * total / done
         log(oracle=config, workload=workload, sample=f"{done} of {total} {unit_desc}",
             sample_s=round(secs, 3), extrapolated_s=round(secs * total / done, 2), threads=oracle_threads())
 
@@ -276,7 +280,7 @@ def oracle_config_timings(log):
         secs = timed(lambda: oracle.backward_bh(q.values[0, :, 0], k.values[0, :, 0], v.values[0, :, 0],
                                                 do.values[0, :, 0], 0, 0, scale=1.0 / math.sqrt(dqk),
                                                 mask=oracle.MaskSpec("causal")))
-        report("4", f"bwd bf16 B=1 H=16 N={n} Dqk={dqk} Dv={dv} causal", secs, 1, 16, "(b, h)")
+        report("4", f"bwd bf16 B=1 H=16 N={n} Dqk={dqk} Dv={dv} causal", secs, 1, 16, "(b, h)", key=f"4/{n}")
     # 5a: split-KV decode B=8 H=32 Nq=1 Nk=32768 D=128, 16 splits + combine (8 (b, h) pairs)
     nk = 32768
     q, k, v = synth.attention_inputs(synth.case_seed(5, 0), 1, 1, nk, 8, 128, 128, "bf16")
@@ -286,6 +290,7 @@ def oracle_config_timings(log):
     q, k, v = synth.attention_inputs(synth.case_seed(5, 1), 1, 512, 512, 1, 1024, 1024, "fp32")
     secs = timed(lambda: oracle.forward(q.values, k.values, v.values))
     report("5b", "fwd fp32 B=4 H=8 N=512 D=1024", secs, 1, 32, "(b, h)")
+    return whole
 
 
 def all_configs_report(oracle_too: bool = True):
@@ -350,8 +355,11 @@ def all_configs_report(oracle_too: bool = True):
         sys.stderr.write(json.dumps(kw) + "\n")
         sys.stderr.flush()
 
-    if oracle_too:
-        oracle_config_timings(log)
+    ora = oracle_config_timings(log) if oracle_too else {}
+
+    def vs_oracle(key, ms):
+        """The configuration's CPU oracle time over this GPU time (both whole-configuration)."""
+        return {"x_vs_oracle": round(ora[key] * 1e3 / ms)} if key in ora else {}
 
     # forward grid: N x D x mask x softcap (B=1 H=16)
     for n in (1024, 4096, 16384):
@@ -395,7 +403,8 @@ def all_configs_report(oracle_too: bool = True):
         ms = gpu_time(lambda: fa.fmha_fwd_splitkv(q, k, v, s))
         byts = 2 * k.numel() * 2
         log(workload="splitkv", splits=s, ms=round(ms, 4), GBs=round(byts / ms / 1e6, 1),
-            frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), timing="graph replay")
+            frac=round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), timing="graph replay",
+            **(vs_oracle("5a", ms) if s == 16 else {}))
     del k, v
     # grouped-query and multi-query decode: H=32 query heads over 8 or 1 K/V heads; the
     # algorithmic bytes are the K/V of the K/V heads
@@ -414,7 +423,7 @@ def all_configs_report(oracle_too: bool = True):
     ms = gpu_time(lambda: fa.fmha_fwd(q, k, v))
     f = 2.0 * 4 * 8 * 2048 * 512 * 512
     log(workload="fwd_fp32_d1024", ms=round(ms, 4), tflops=round(f / ms / 1e9, 2),
-        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 4), timing="graph replay")
+        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 4), timing="graph replay", **vs_oracle("5b", ms))
     del q, k, v
     # fp32 parity workload (latency-bound: one 32-row workgroup)
     q, k, v = (torch.randn(1, 128, 1, 64, device=dev) for _ in range(3))
@@ -422,7 +431,7 @@ def all_configs_report(oracle_too: bool = True):
     ms = gpu_time(lambda: fa.fmha_fwd(q, k, v, mask=m))
     f = 2.0 * 2 * 64 * causal_pairs(128)
     log(workload="fwd_fp32_n128_d64_causal", ms=round(ms, 4), tflops=round(f / ms / 1e9, 4),
-        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 6), timing="graph replay")
+        frac=round(f / ms / 1e9 / PEAK_FP32_TFLOPS, 6), timing="graph replay", **vs_oracle("1", ms))
     # block-sparse forward: B=2 H=8 N=8192 D=128, 128 x 128 sparse tiles from the element
     # mask, relative bias -0.01 |i - j|; useful FLOPs on the visible pairs only
     n, bsz, hh = 8192, 2, 8
@@ -441,7 +450,8 @@ def all_configs_report(oracle_too: bool = True):
         tiles = int(bs.partial_cnt.sum().item() + bs.full_cnt.sum().item())
         log(workload="fwd_bf16_block_sparse", N=n, B=bsz, H=hh, D=128, mask=kind, ms=round(ms, 4),
             tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-            visited_tiles=tiles, of_tiles=bsz * (n // 128) ** 2, build_block_mask_ms=round(ms_bm, 4))
+            visited_tiles=tiles, of_tiles=bsz * (n // 128) ** 2, build_block_mask_ms=round(ms_bm, 4),
+            **(vs_oracle("3", ms) if kind == "causal" else {}))
         # the backward through the transposed lists (dQ, dK, dV), same mask and bias
         do = torch.randn_like(q)
         out, lse = fa.fmha_fwd(q, k, v, mask=m, bias_slope=-0.01, block_sparse=bs)
@@ -482,7 +492,8 @@ def all_configs_report(oracle_too: bool = True):
         ms = timeit(lambda: fa.fmha_bwd(q, k, v, out, lse, do, mask=m, dq=dq, dk=dk, dv=dv_, workspace=ws))
         f = useful_flops(1, 16, causal_pairs(n), dqk, dv)[1]
         log(workload="bwd_bf16", N=n, Dqk=dqk, Dv=dv, mask="causal", ms=round(ms, 4),
-            tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+            tflops=round(f / ms / 1e9, 1), frac=round(f / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            **(vs_oracle(f"4/{n}", ms) if (n, dqk) in ((4096, 128), (8192, 192)) else {}))
         del q, k, v, do, out, lse, dq, dk, dv_, ws
 
 
