@@ -165,3 +165,34 @@ def test_varlen_seqused(case):
     check_grad("dV", gv[used_k], g_ref[2][used_k])
     assert np.all(np.isnan(gq[~used_q])), "dQ rows past seqused_q were written"
     assert np.all(np.isnan(gk[~used_k])) and np.all(np.isnan(gv[~used_k])), "dK / dV rows past seqused_k were written"
+
+
+def _varlen_fuzz_cases(n=24, seed=5150):
+    """Seeded random packed batches: 1-12 sequences of 0-700 rows (query and key lengths
+    drawn apart), grouped K/V heads, every mask kind without documents, softcap or bias.
+    (lq, lk, H, Hkv, D, mask, window, prefix, softcap, slope) per case."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        nseq = int(rng.integers(1, 13))
+        lq = [int(x) for x in rng.integers(0, 701, nseq)]
+        lk = [int(x) if rng.random() < 0.5 else lq[i] for i, x in enumerate(rng.integers(0, 701, nseq))]
+        if sum(lq) == 0:
+            lq[0] = 1
+        H = int(rng.choice([1, 2, 4]))
+        hkv = int(rng.choice([h for h in (1, 2, 4) if H % h == 0]))
+        d = int(rng.choice([64, 128]))
+        kind = str(rng.choice(["none", "causal", "sliding_window", "prefix_lm"]))
+        window = int(rng.integers(1, 400)) if kind == "sliding_window" else 0
+        prefix = int(rng.integers(0, 400)) if kind == "prefix_lm" else 0
+        mod = rng.integers(0, 3)
+        cap = 20.0 if mod == 1 else 0.0
+        slope = -0.02 if mod == 2 else 0.0
+        cases.append((lq, lk, H, hkv, d, kind, window, prefix, cap, slope))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_varlen_fuzz(case):
+    lq, lk, H, hkv, d, kind, w, p, cap, slope = _varlen_fuzz_cases()[case]
+    _run(synth.case_seed(9, 1000 + case), lq, lk, H, d, d, kind, w, p, cap, slope, backward=True, hkv=hkv)
