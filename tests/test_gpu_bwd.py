@@ -130,3 +130,72 @@ CONFIG4 = [(4096, 64, 64), (4096, 128, 128), (16384, 64, 64), (16384, 128, 128),
 def test_bwd_full_size(case):
     N, Dqk, Dv = CONFIG4[case]
     _case(synth.case_seed(4, case), 1, N, N, 16, Dqk, Dv, "causal", heads=[case % 16])
+
+
+def _random_list_cases(n=10, seed=2718):
+    """Seeded block-sparse problems with arbitrary tile classes (not derived from a mask):
+    (B, Nq, Nk, H, Hm, D, tile_m, tile_n, mask, class seed) per case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 4))
+        H = int(rng.choice([2, 4]))
+        Hm = int(rng.choice([1, H]))
+        d = int(rng.choice([64, 128]))
+        tm, tn = (int(x) for x in rng.choice([128, 256], 2))
+        out.append((B, int(rng.integers(257, 1400)), int(rng.integers(257, 1400)), H, Hm, d, tm, tn,
+                    str(rng.choice(["none", "causal"])), int(rng.integers(1 << 30))))
+    return out
+
+
+def _lists_from_classes(cls):
+    """Forward and transposed lists of a class map cls [B, Hm, nQt, nKt] (0 skip, 1 partial,
+    2 full), ascending and -1 padded, as numpy int32 arrays in BlockLists field order."""
+    B, Hm, nqt, nkt = cls.shape
+
+    def rows(c, n_rows, n_cols, val):
+        cnt = np.zeros((B, Hm, n_rows), np.int32)
+        idx = np.full((B, Hm, n_rows, n_cols), -1, np.int32)
+        for b in range(B):
+            for h in range(Hm):
+                for r in range(n_rows):
+                    sel = np.nonzero(c[b, h, r] == val)[0]
+                    cnt[b, h, r] = len(sel)
+                    idx[b, h, r, :len(sel)] = sel
+        return cnt, idx
+
+    pc, pi = rows(cls, nqt, nkt, 1)
+    fc, fi = rows(cls, nqt, nkt, 2)
+    t = np.ascontiguousarray(cls.transpose(0, 1, 3, 2))
+    tpc, tpi = rows(t, nkt, nqt, 1)
+    tfc, tfi = rows(t, nkt, nqt, 2)
+    return pc, pi, fc, fi, tpc, tpi, tfc, tfi
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_bwd_random_lists(case):
+    # arbitrary per-head lists over several batch rows: the workgroups take their tiles in
+    # order of list length (per batch row and mask head), rows and key tiles without any
+    # listed tile give O = 0 / LSE = -inf / dQ = 0 and dK = dV = 0
+    import torch
+    import block_sparse_attention_fmha_amd as fa
+    B, Nq, Nk, H, Hm, d, tm, tn, kind, cseed = _random_list_cases()[case]
+    nqt, nkt = -(-Nq // tm), -(-Nk // tn)
+    rng = np.random.default_rng(cseed)
+    cls = rng.integers(0, 3, size=(B, Hm, nqt, nkt))
+    cls[0, 0, nqt - 1] = 0          # an empty query-tile row
+    cls[B - 1, Hm - 1, :, 0] = 0     # an empty key-tile column
+    arrays = _lists_from_classes(cls)
+    seed = synth.case_seed(9, 700 + case)
+    q, k, v, do = synth.attention_inputs(seed, B, Nq, Nk, H, d, d, "bf16", with_dout=True)
+    om, gm = mask_pair(kind, B, Nq, Nk)
+    announce(f"bwd random lists case={case} B={B} Nq={Nq} Nk={Nk} H={H} Hm={Hm} D={d} tiles={tm}x{tn} mask={kind}")
+    dev = torch.device("cuda:0")
+    bs = fa.BlockSparse(tm, tn, nqt, nkt, Hm, *(torch.from_numpy(a).to(dev) for a in arrays))
+    out, lse, dq, dk, dv = run_fwd_bwd(to_dev(q), to_dev(k), to_dev(v), to_dev(do), gm, block_sparse=bs)
+    lists = oracle.BlockLists(tm, tn, *arrays)
+    ref = oracle.backward(q.values, k.values, v.values, do.values, mask=om, lists=lists)
+    for name, got, want in (("dQ", dq, ref[0]), ("dK", dk, ref[1]), ("dV", dv, ref[2])):
+        check_grad(name, host(got), want)
+    check_bf16("O", host(out), ref[3])
+    check_bf16("LSE", host(lse), ref[4])
