@@ -729,9 +729,11 @@ __device__ int build_tile_sequence(const ListParams& L, int64_t row0, int64_t ro
 // [j span, (j + 1) span) of the list side: its row holds element j span and, with
 // half > 0, also element j span + half when that lies in bounds and in another list row
 // (the forward's two 128-row halves). The rank is a heuristic of the dispatch order
-// only; results do not depend on it. `lds` holds n + 1 ints (n <= kMaxRankedTiles, else
-// the natural order j = t is kept). Contains barriers: every thread of the workgroup calls it.
-constexpr int kMaxRankedTiles = 4096;
+// only; results do not depend on it. `lds` holds n + 1 ints. The ranking costs
+// O(n^2 / NTHREADS) LDS compares per workgroup (about 1-2 us at n = 512), so above
+// kMaxRankedTiles the natural order j = t is kept: there a workgroup's share of a short
+// walk would go to ranking. Contains barriers: every thread of the workgroup calls it.
+constexpr int kMaxRankedTiles = 512;
 template <int NTHREADS>
 __device__ int ranked_tile(const ListParams& L, int64_t rbase, int n, int span, int half, int n_elems, int t,
                            int* lds, int tid) {
