@@ -528,8 +528,7 @@ PROFILE_OTHER = [
     ("split-KV combine (all three)", "splitkv_combine_kernel<128>", (0, 1)),
     ("fp32 wide-head forward", "fwd_f32_kernel<1024, 128>", (0, 1)),
     ("block-sparse forward", "fwd_bf16_kernel<128, 128, true, false, true>", (0, 1)),
-    ("block-mask build, forward lists", "classify_kernel<false>", (0, 1)),
-    ("block-mask build, transposed lists", "classify_kernel<true>", (0, 1)),
+    ("block-mask build, both orientations", "classify_kernel", (0, 1)),
 ]
 
 
@@ -696,7 +695,7 @@ def summarize_profiles(src: str, out_dir: str):
             "(multi-query); the grouped launches run `splitkv_mfma_kernel<128>` and are split here by launch order "
             "(8-head launches first); fp32 forward B=4 H=8 N=512 D=1024, no mask; block-sparse bf16 forward B=2 H=8 "
             "N=8192 D=128, causal element mask on 128x128 sparse tiles, relative bias -0.01|i-j|, with "
-            "`build_block_mask` (`classify_kernel<false>` forward lists, `<true>` transposed lists).", "",
+            "`build_block_mask` (`classify_kernel`: forward and transposed lists in one launch).", "",
             f"Same runs as the fwd+bwd profiles (`{PROFILE_PRE}`), summarised by "
             f"`python3 bench.py --summarize-profiles $OUT`, which stops with an error when a kernel "
             f"listed here has no row:", "", *cmd("trace", "fetch", "write", "sq1", "sq2"), "",

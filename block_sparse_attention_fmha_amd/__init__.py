@@ -514,12 +514,16 @@ def build_block_mask(mask: Mask, B: int, Nq: int, Nk: int, tile_m: int, tile_n: 
     the forward and transposed index lists."""
     import torch
     nqt, nkt = -(-Nq // tile_m), -(-Nk // tile_n)
-    i32 = dict(dtype=torch.int32, device=device)
-    bs = BlockSparse(tile_m, tile_n, nqt, nkt, heads,
-                     torch.empty((B, heads, nqt), **i32), torch.empty((B, heads, nqt, nkt), **i32),
-                     torch.empty((B, heads, nqt), **i32), torch.empty((B, heads, nqt, nkt), **i32),
-                     torch.empty((B, heads, nkt), **i32), torch.empty((B, heads, nkt, nqt), **i32),
-                     torch.empty((B, heads, nkt), **i32), torch.empty((B, heads, nkt, nqt), **i32))
+    # the eight arrays are contiguous slices of one allocation (one allocator call per build)
+    shapes = [(B, heads, nqt), (B, heads, nqt, nkt), (B, heads, nqt), (B, heads, nqt, nkt),
+              (B, heads, nkt), (B, heads, nkt, nqt), (B, heads, nkt), (B, heads, nkt, nqt)]
+    sizes = [math.prod(sh) for sh in shapes]
+    flat = torch.empty(sum(sizes), dtype=torch.int32, device=device)
+    parts, o = [], 0
+    for sh, n in zip(shapes, sizes):
+        parts.append(flat[o:o + n].view(sh))
+        o += n
+    bs = BlockSparse(tile_m, tile_n, nqt, nkt, heads, *parts)
     c = bs.to_c()
     cm = mask.to_c()
     _check(load_library().build_block_mask(ctypes.byref(cm), B, heads, Nq, Nk, tile_m, tile_n,

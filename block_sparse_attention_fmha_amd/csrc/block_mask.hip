@@ -58,15 +58,15 @@ __device__ __forceinline__ int64_t row_visible(const MaskParams& m, int i, int k
 // end of the tile starting at t0 with size ts, clipped to n (no int overflow)
 __device__ __forceinline__ int tile_end(int t0, int ts, int n) { return (int)min((int64_t)n, (int64_t)t0 + ts); }
 
-// TRANSPOSED = false: grid rows are query tiles, entries are key tiles.
-// TRANSPOSED = true:  grid rows are key tiles, entries are query tiles.
+// One list row (workgroup `blk` of its orientation).
+// TRANSPOSED = false: rows are query tiles, entries are key tiles.
+// TRANSPOSED = true:  rows are key tiles, entries are query tiles.
 template <bool TRANSPOSED>
-__global__ __launch_bounds__(kThreads)
-void classify_kernel(const MaskParams m, int Hm, int nq, int nk, int tile_m, int tile_n, int n_rows,
-                     int n_cols, int* pcnt, int* pidx, int* fcnt, int* fidx) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char cls[];
-  const int row = blockIdx.x % n_rows;
-  const int bhm = blockIdx.x / n_rows;
+__device__ __forceinline__ void classify_row(const MaskParams& m, int Hm, int nq, int nk, int tile_m, int tile_n,
+                                             int n_rows, int n_cols, int* pcnt, int* pidx, int* fcnt, int* fidx,
+                                             int blk, unsigned char* cls) {
+  const int row = blk % n_rows;
+  const int bhm = blk / n_rows;
   const int b = bhm / Hm;
   if (m.kind == kMaskBlockDiag && (TRANSPOSED ? min(tile_n, nk - row * tile_n) : min(tile_m, nq - row * tile_m)) <= kMaxHistRows) {
     // ---- histogram path
@@ -214,7 +214,7 @@ void classify_kernel(const MaskParams m, int Hm, int nq, int nk, int tile_m, int
       tp += wsum[2 * v];
       tf += wsum[2 * v + 1];
     }
-    const int64_t base = (int64_t)blockIdx.x * n_cols;
+    const int64_t base = (int64_t)blk * n_cols;
     for (int col = c0; col < c1; ++col) {
       const unsigned char c = cls[col];
       if (c == 1) pidx[base + op++] = col;
@@ -223,10 +223,24 @@ void classify_kernel(const MaskParams m, int Hm, int nq, int nk, int tile_m, int
     for (int e = tp + t; e < n_cols; e += kThreads) pidx[base + e] = -1;
     for (int e = tf + t; e < n_cols; e += kThreads) fidx[base + e] = -1;
     if (t == 0) {
-      pcnt[blockIdx.x] = tp;
-      fcnt[blockIdx.x] = tf;
+      pcnt[blk] = tp;
+      fcnt[blk] = tf;
     }
   }
+}
+
+// Both orientations in one launch: the first B Hm n_q_tiles workgroups build the forward
+// lists, the rest the transposed ones.
+__global__ __launch_bounds__(kThreads)
+void classify_kernel(const MaskParams m, int Hm, int nq, int nk, int tile_m, int tile_n, int nqt, int nkt,
+                     int fwd_blocks, const BlockMaskOut out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char cls[];
+  if ((int)blockIdx.x < fwd_blocks)
+    classify_row<false>(m, Hm, nq, nk, tile_m, tile_n, nqt, nkt, out.pcnt, out.pidx, out.fcnt, out.fidx,
+                        blockIdx.x, cls);
+  else
+    classify_row<true>(m, Hm, nq, nk, tile_m, tile_n, nkt, nqt, out.tpcnt, out.tpidx, out.tfcnt, out.tfidx,
+                       blockIdx.x - fwd_blocks, cls);
 }
 
 }  // namespace
@@ -235,18 +249,12 @@ hipError_t launch_build_block_mask(const MaskParams& m, int B, int Hm, int Nq, i
                                    int tile_n, const BlockMaskOut& out, hipStream_t st) {
   const int nqt = (Nq + tile_m - 1) / tile_m;
   const int nkt = (Nk + tile_n - 1) / tile_n;
-  hipError_t e = hipFuncSetAttribute((const void*)classify_kernel<false>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(nkt));
+  const int bytes = lds_bytes(nkt > nqt ? nkt : nqt);   // either orientation's columns
+  hipError_t e = hipFuncSetAttribute((const void*)classify_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)classify_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          lds_bytes(nqt));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(classify_kernel<false>, dim3(B * Hm * nqt), dim3(kThreads), lds_bytes(nkt), st, m, Hm, Nq,
-                     Nk, tile_m, tile_n, nqt, nkt, out.pcnt, out.pidx, out.fcnt, out.fidx);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(classify_kernel<true>, dim3(B * Hm * nkt), dim3(kThreads), lds_bytes(nqt), st, m, Hm, Nq,
-                     Nk, tile_m, tile_n, nkt, nqt, out.tpcnt, out.tpidx, out.tfcnt, out.tfidx);
+  const int fwd_blocks = B * Hm * nqt;
+  hipLaunchKernelGGL(classify_kernel, dim3(fwd_blocks + B * Hm * nkt), dim3(kThreads), bytes, st, m, Hm, Nq, Nk,
+                     tile_m, tile_n, nqt, nkt, fwd_blocks, out);
   return hipGetLastError();
 }
 
