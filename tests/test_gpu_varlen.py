@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from block_sparse_attention_fmha_amd import synth
-from tests.gpu_util import announce, check_bf16, check_grad, host
+from tests.gpu_util import announce, check_bf16, check_grad, host, varlen_grad_allowances
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +41,13 @@ def _run(seed, lq, lk, H, dqk, dv, kind, window=0, prefix=0, softcap=0.0, slope=
                                          mask=fa.Mask(kind, window=window, prefix=prefix), softcap=softcap,
                                          bias_slope=slope)
         torch.cuda.synchronize()
-        ref = oracle.backward_varlen(qv, kv, vv, dov, cu_q, cu_k, softcap=softcap, bias_slope=slope,
-                                     mask=oracle.MaskSpec(kind, window=window, prefix=prefix))
-        for name, got, want in (("dQ", dq, ref[0]), ("dK", dk, ref[1]), ("dV", dv_, ref[2])):
-            check_grad(name, host(got), want)
+        om = oracle.MaskSpec(kind, window=window, prefix=prefix)
+        ref = oracle.backward_varlen(qv, kv, vv, dov, cu_q, cu_k, softcap=softcap, bias_slope=slope, mask=om)
+        # dQ and dK also carry the error of the forward output they were handed (through D)
+        dq_a, dk_a = varlen_grad_allowances(qv, kv, dov, host(out), o_ref, cu_q, cu_k, softcap=softcap,
+                                            bias_slope=slope, mask=om)
+        for name, got, want, allow in (("dQ", dq, ref[0], dq_a), ("dK", dk, ref[1], dk_a), ("dV", dv_, ref[2], None)):
+            check_grad(name, host(got), want, row_allowance=allow)
 
 
 CASES = [
@@ -86,6 +89,15 @@ GQA_CASES = [
 def test_varlen_grouped_heads(case):
     lq, lk, H, hkv, d, kind, w, slope = GQA_CASES[case]
     _run(synth.case_seed(9, 870 + case), lq, lk, H, d, d, kind, w, 0, 0.0, slope, backward=True, hkv=hkv)
+
+
+def test_varlen_backward_single_key_sequence():
+    # the batch a seeded 600-case varlen sweep failed on: sequence 3 has 642 queries and one
+    # key, so P = 1 and the exact dQ of its rows is 0 (dP = D); the kernel's dQ there is what
+    # the bf16 forward output leaves of that cancellation, which the per-block check's dQ
+    # allowance accounts for (the whole-tensor bound holds: those rows are 14% of the batch)
+    lq, lk, H, hkv, d, kind, w, p, cap, slope = _varlen_fuzz_cases(n=1, seed=80443)[0]
+    _run(synth.case_seed(11, 80443), lq, lk, H, d, d, kind, w, p, cap, slope, backward=True, hkv=hkv)
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
