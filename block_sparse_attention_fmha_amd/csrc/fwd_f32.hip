@@ -238,9 +238,13 @@ void fwd_f32_kernel(const AttnParams p) {
       if (mk == kMaskBlockDiag) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          // an unconditional (clamped) load and a select, no per-key branch: with a
+          // short-circuit test here the compiler dropped the -inf store of the first
+          // register in the loop body, leaving keys n0 and n0 + 4 of every tile visible
+          // to other documents' rows
           const int key = kb + 8 * (r >> 2) + (r & 3);
-          const bool vis = key < Nk && doc_k[min(key, Nk - 1)] == row_doc;
-          if (!vis) sc[r] = kNegInf;
+          const bool vis = (key < Nk) & (doc_k[min(key, Nk - 1)] == row_doc);
+          sc[r] = vis ? sc[r] : kNegInf;
         }
       } else {
 #pragma unroll

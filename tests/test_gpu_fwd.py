@@ -142,6 +142,20 @@ def test_fwd_fp32_small(case):
     _case(seed, B, Nq, Nk, H, D, D, "fp32", kind, window=50, prefix=prefix)
 
 
+# (case index for the seed, B, N, H, D): seeds whose documents split every batch row
+# (two rows of 637 + 263 and 261 + 500 + 139 tokens; one row of 435 + 335 + 230 and of
+# 435 + 335 + 30), so keys of other documents sit inside every query tile's walk
+FP32_DOCS = [(306, 2, 900, 2, 64), (309, 1, 1000, 2, 128), (309, 1, 800, 1, 1024)]
+
+
+@pytest.mark.parametrize("case", range(len(FP32_DOCS)))
+def test_fwd_fp32_block_diagonal_documents(case):
+    c, B, N, H, D = FP32_DOCS[case]
+    seed = synth.case_seed(9, c)
+    assert all(len(np.unique(row)) >= 2 for row in synth.document_ids(seed, B, N))
+    _case(seed, B, N, N, H, D, D, "fp32", "block_diagonal")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def _rows_sample(n, seed):
